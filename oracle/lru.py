@@ -1,0 +1,142 @@
+"""Per-layer VRAM expert-slot cache with least-recently-used replacement.
+
+[39TOK] section "设计核心": a global LRU cache of experts in VRAM catches the
+routing overlap of adjacent tokens; what misses is filled into the GPU cache.
+[753B] section "按带宽动态分配参数存储": frequently used experts stay resident,
+the rest are fetched on demand.  The pages give no further policy detail; the
+batch-aware rule below is the stated reading (R11, R16):
+
+* One pool of S slots per layer over E experts; it starts cold (all empty).
+* A step presents T*k accesses in pair order q = t*k + j.
+* Hits are judged against the state at the start of the step.
+* Each distinct missed expert (in order of first appearance) takes one victim
+  slot.  Victims come only from slots whose expert is not requested in this
+  step: first the empty slots in ascending index, then occupied slots in
+  ascending last-use stamp.  Too few candidates -> capacity error, state kept.
+* Every access, in pair order, advances the clock by one and stamps its slot.
+* Hit rate = (accesses - distinct misses) / accesses: a repeated access to an
+  expert filled earlier in the same step counts as a hit.
+
+``StampLRU`` is the form the GPU kernel implements (four arrays).  ``ListLRU``
+is an independent move-to-MRU list simulation of the same policy; the tests
+require both to give identical slot tables at every step.
+"""
+
+import numpy as np
+
+OK = 0
+E_CAPACITY = -3
+
+
+def _unique_in_order(seq):
+    seen, out = set(), []
+    for e in seq:
+        if e not in seen:
+            seen.add(e)
+            out.append(e)
+    return out
+
+
+class StampLRU:
+    def __init__(self, E: int, S: int):
+        self.E, self.S = E, S
+        self.slot_expert = np.full(S, -1, dtype=np.int32)
+        self.expert_slot = np.full(E, -1, dtype=np.int32)
+        self.slot_stamp = np.zeros(S, dtype=np.int64)
+        self.clock = 0
+
+    def state(self):
+        return (self.slot_expert.copy(), self.expert_slot.copy(),
+                self.slot_stamp.copy(), int(self.clock))
+
+    def step(self, pair_experts):
+        pair_experts = [int(e) for e in np.asarray(pair_experts).ravel()]
+        n = len(pair_experts)
+        requested = set(pair_experts)
+        uniq = _unique_in_order(pair_experts)
+        resident_at_start = {e for e in uniq if self.expert_slot[e] >= 0}
+        misses = [e for e in uniq if e not in resident_at_start]
+        cand = [s for s in range(self.S)
+                if self.slot_expert[s] < 0 or int(self.slot_expert[s]) not in requested]
+        cand.sort(key=lambda s: (0 if self.slot_expert[s] < 0 else 1,
+                                 int(self.slot_stamp[s]), s))
+        if len(cand) < len(misses):
+            return dict(status=E_CAPACITY, n_miss=len(misses))
+        victims = cand[:len(misses)]
+        for e, s in zip(misses, victims):
+            old = int(self.slot_expert[s])
+            if old >= 0:
+                self.expert_slot[old] = -1
+            self.slot_expert[s] = e
+            self.expert_slot[e] = s
+        for e in pair_experts:
+            self.clock += 1
+            self.slot_stamp[self.expert_slot[e]] = self.clock
+        pair_slot = np.array([self.expert_slot[e] for e in pair_experts], dtype=np.int32)
+        hit_pairs = [q for q, e in enumerate(pair_experts) if e in resident_at_start]
+        miss_pairs = [q for q, e in enumerate(pair_experts) if e not in resident_at_start]
+        return dict(status=OK, pair_slot=pair_slot,
+                    pair_order=np.array(hit_pairs + miss_pairs, dtype=np.int32),
+                    n_hit_pairs=len(hit_pairs), n_miss=len(misses),
+                    miss_expert=np.array(misses, dtype=np.int32),
+                    miss_slot=np.array(victims, dtype=np.int32),
+                    n_hits=n - len(misses), n_access=n)
+
+
+class ListLRU:
+    """Move-to-MRU list form of the same policy (independent formulation)."""
+
+    def __init__(self, E: int, S: int):
+        self.E, self.S = E, S
+        self.recency = []            # resident experts, least recent first
+        self.slot_of = {}            # expert -> slot
+
+    def slot_table(self):
+        se = np.full(self.S, -1, dtype=np.int32)
+        for e, s in self.slot_of.items():
+            se[s] = e
+        return se
+
+    def step(self, pair_experts):
+        pair_experts = [int(e) for e in np.asarray(pair_experts).ravel()]
+        requested = set(pair_experts)
+        uniq = _unique_in_order(pair_experts)
+        misses = [e for e in uniq if e not in self.slot_of]
+        used = set(self.slot_of.values())
+        victims = [s for s in range(self.S) if s not in used][:len(misses)]
+        evict = []
+        if len(victims) < len(misses):
+            for e in self.recency:               # from the least-recent end
+                if len(victims) + len(evict) == len(misses):
+                    break
+                if e not in requested:
+                    evict.append(e)
+            if len(victims) + len(evict) < len(misses):
+                return dict(status=E_CAPACITY)
+        for e in evict:
+            victims.append(self.slot_of.pop(e))
+            self.recency.remove(e)
+        for e, s in zip(misses, victims):
+            self.slot_of[e] = s
+        for e in pair_experts:                   # each access moves to MRU
+            if e in self.recency:
+                self.recency.remove(e)
+            self.recency.append(e)
+        return dict(status=OK,
+                    pair_slot=np.array([self.slot_of[e] for e in pair_experts], dtype=np.int32),
+                    n_miss=len(misses), miss_expert=np.array(misses, dtype=np.int32),
+                    miss_slot=np.array(victims, dtype=np.int32))
+
+
+def simulate_hit_rate(steps, E: int, S: int, skip: int = 0):
+    """Hit rate of a sequence of per-step access lists (steps >= skip counted)."""
+    lru = StampLRU(E, S)
+    hits = acc = 0
+    for i, s in enumerate(steps):
+        r = lru.step(s)
+        if r["status"] != OK:
+            raise RuntimeError("capacity")
+        if i >= skip:
+            hits += r["n_hits"]
+            acc += r["n_access"]
+    return hits / max(acc, 1)
