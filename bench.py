@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark: routed block-scaled MoE layer stack, batch-1 decode, one MI355X.
+
+Workload (default): the 35B-A3B-like decode stack - 40 MoE layers, hidden 2048,
+256 experts, top-8, expert width 512, NVFP4 weights drawn from N(0, 0.02),
+fp32 router N(0, 0.05), batch 1, AR(1) bf16 hidden states
+h_t = 0.9 h_{t-1} + 0.44 eps_t.  Every layer of a step receives the same h_t.
+A step is one token through the whole stack: per layer one moe_layer_forward
+call (router GEMV, softmax + top-8, gate/up + SwiGLU, down, gate-weighted
+combine) through the C ABI, layers in order, the step captured in one HIP graph.  All
+weights are resident in HBM before timing starts.
+
+Prints one JSON line (rank 0): tok/s, ms/step, the dominant kernel's roofline
+(HIP-event timed inside the timed region), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MoE-layer decode tok/s + weight-stream HBM GB/s; prefill MFMA util (1 GPU)"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode35b", choices=["decode35b", "decode753b"])
+    p.add_argument("--fmt", type=int, default=0, help="override weight format (1 NVFP4, 2 MXFP4, 3 FP8)")
+    p.add_argument("--layers", type=int, default=0, help="override the layer count (testing only)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-steps", type=int, default=2)
+    p.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
+    return p.parse_args()
+
+
+def build_stack(wl, fmt, n_layers, threads):
+    """Generate, quantize, pack and upload every layer; returns device pools and routers."""
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_gemv_amd import binding as B
+    from block_scaled_fp4_gemv_amd import synth as sy
+
+    sy.set_threads(threads)
+    stride = B.blob_stride(fmt, wl.H, wl.F)
+    pools, routers = [], []
+    host = np.empty(wl.E * stride, np.uint8)
+    t0 = time.time()
+    for l in range(n_layers):
+        batch = sy.experts(fmt, 0, wl.cfg_id, l, 0, wl.E, wl.H, wl.F, wl.w_std)
+        B.pack_layer(fmt, wl.H, wl.F, batch, host, stride)
+        del batch
+        pools.append(torch.from_numpy(host).cuda())
+        routers.append(torch.from_numpy(sy.router(0, wl.cfg_id, l, wl.E, wl.H)).cuda())
+        if l % 4 == 3 or l == n_layers - 1:
+            log(f"layer {l + 1}/{n_layers} generated ({time.time() - t0:.0f} s)")
+    torch.cuda.synchronize()
+    return pools, routers, stride
+
+
+def algorithmic_bytes(wl, fmt):
+    """Bytes one decode token must move, per layer: weights of the k routed experts
+    (codes + block scales + tensor scales), the fp32 router, and the activations."""
+    from block_scaled_fp4_gemv_amd import binding as B
+    eb = B.moe_expert_bytes(fmt, wl.H, wl.F) - 256 + (12 if fmt == 1 else 0)
+    router = wl.E * wl.H * 4
+    act_route = wl.H * 2 + wl.k * 8
+    act_ffn = wl.H * 2 + wl.k * wl.F * 2 * 2 + wl.H * 2 + wl.k * 8
+    return dict(expert=wl.k * eb, router=router, ffn_total=wl.k * eb + act_ffn,
+                route_total=router + act_route, layer_total=wl.k * eb + router + act_route + act_ffn)
+
+
+def cpu_baseline(wl, fmt, xs, n_steps, n_layers):
+    """The oracle as it stands, on the first n_steps tokens of the same stack."""
+    import numpy as np
+
+    from block_scaled_fp4_gemv_amd import synth as sy
+    from oracle import moe
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+
+    class Lazy:
+        def __init__(self, l):
+            self.l, self.c = l, {}
+
+        def __getitem__(self, e):
+            if e not in self.c:
+                b = sy.experts(fmt, 0, wl.cfg_id, self.l, e, 1, wl.H, wl.F, wl.w_std)
+                self.c[e] = sy.expert_view(b, 0)
+            return self.c[e]
+
+    layers = [(sy.router(0, wl.cfg_id, l, wl.E, wl.H), Lazy(l)) for l in range(n_layers)]
+    # weights are generated outside the timed region (the GPU leg also starts resident)
+    for t in range(n_steps):
+        for R, ex in layers:
+            idx, _, _ = moe.route(xs[t:t + 1], R, wl.k)
+            for e in idx.ravel():
+                ex[int(e)]
+    t0 = time.perf_counter()
+    for t in range(n_steps):
+        for R, ex in layers:
+            moe.moe_layer(fmt, xs[t:t + 1], R, ex, wl.k)
+    dt = time.perf_counter() - t0
+    return dict(value=n_steps / dt, unit="tok/s", cores=int(blas_threads), kind="oracle",
+                sample=f"first {n_steps} decode tokens through all {n_layers} layers "
+                       f"(NumPy fp64 oracle incl. dequant; {dt:.1f} s)",
+                host_cpus=os.cpu_count())
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_gemv_amd import binding as B
+    from block_scaled_fp4_gemv_amd import synth as sy
+
+    wl = sy.WORKLOADS[args.workload]
+    fmt = args.fmt or wl.fmt
+    n_layers = args.layers or wl.layers
+    B.lib()
+    torch.cuda.init()
+    log(f"workload {wl.name}: {n_layers} layers H={wl.H} E={wl.E} k={wl.k} F={wl.F} fmt={fmt}")
+    pools, routers, stride = build_stack(wl, fmt, n_layers, args.threads)
+    H, E, F, k = wl.H, wl.E, wl.F, wl.k
+
+    n_states = wl.steps
+    xs = sy.ar1_sequence(0, wl.cfg_id, n_states, H)
+    xs_dev = torch.from_numpy(xs).cuda()
+    x = torch.empty((1, H), dtype=torch.uint16, device="cuda")
+    idx = [torch.empty((1, k), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+    w = [torch.empty((1, k), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    out = [torch.empty((1, H), dtype=torch.uint16, device="cuda") for _ in range(n_layers)]
+    lws = [B.new_layer_workspace(fmt, 1, H, F, k, E) for _ in range(n_layers)]
+
+    def layer(l):
+        B.moe_layer_forward(fmt, pools[l], stride, H, F, E, k, x, routers[l], topk_idx=idx[l],
+                            topk_w=w[l], out=out[l], ws=lws[l])
+
+    def step():
+        for l in range(n_layers):
+            layer(l)
+
+    # eager warm-up, then capture one step in a HIP graph
+    x.copy_(xs_dev[0:1])
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        x.copy_(xs_dev[i % n_states:i % n_states + 1])
+        g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        j = (args.warmup + i) % n_states
+        x.copy_(xs_dev[j:j + 1])
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    tok_s = 1000.0 / ms_step
+    log(f"timed {args.steps} steps: {ms_step * 1000:.1f} us/step, {tok_s:.1f} tok/s")
+
+    # per-layer call durations with HIP events on the stream the kernels run on
+    stream = torch.cuda.current_stream()
+    n_rep = max(1, min(args.steps, 50))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_rep * n_layers)]
+    for r in range(n_rep):
+        j = r % n_states
+        x.copy_(xs_dev[j:j + 1])
+        for l in range(n_layers):
+            e = evs[r * n_layers + l]
+            e[0].record(stream)
+            layer(l)
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    layer_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1000
+
+    nb = algorithmic_bytes(wl, fmt)
+    layer_gbps = nb["layer_total"] / (layer_us * 1e-6) / 1e9
+    stack_bytes = nb["layer_total"] * n_layers
+    stream_gbps = stack_bytes * tok_s / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {1: "nvfp4 weights, bf16 activations, fp32 accumulate",
+                  2: "mxfp4 weights, bf16 activations, fp32 accumulate",
+                  3: "fp8-e4m3 weights, bf16 activations, fp32 accumulate"}[fmt],
+        "data": "synthetic (seeded N(0,0.02) weights quantized to the block format; AR(1) bf16 states)",
+        "config": {"workload": f"{wl.name}: {n_layers} stacked MoE layers, hidden {H}, {E} experts, "
+                               f"top-{k}, expert width {F}, batch 1",
+                   "layers": n_layers, "hidden": H, "experts": E, "top_k": k, "expert_width": F,
+                   "format": {1: "nvfp4", 2: "mxfp4", 3: "fp8"}[fmt], "batch": 1,
+                   "graph": "one HIP graph per step"},
+        "weight_stream_GBps": round(stream_gbps, 1),
+        "weight_stream_frac_of_hbm": round(stream_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": "moe_layer_forward decode layer (router GEMV, gate/up+SwiGLU with "
+                               "in-block top-k, down+combine: 3 kernels)",
+                     "bound": "hbm", "achieved": round(layer_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(layer_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": nb["layer_total"], "avg_launch_us": round(layer_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(wl, fmt, xs, args.cpu_sample_steps, n_layers)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,299 @@
+"""ctypes binding of ``libmoe_fp4.so`` (the C ABI in include/moe_fp4.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Device buffers are torch CUDA tensors (PyTorch supplies device
+memory and streams); host blobs are numpy arrays.  Functions keep the C
+names.  Output tensors that the caller does not pass are allocated here with
+torch (the library itself never allocates).  A missing library raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_fp4.so")
+
+MOE_OK, MOE_E_ARG, MOE_E_FORMAT, MOE_E_CAPACITY, MOE_E_WORKSPACE, MOE_E_HIP = 0, -1, -2, -3, -4, -5
+MOE_FMT_NVFP4, MOE_FMT_MXFP4, MOE_FMT_FP8_E4M3 = 1, 2, 3
+MOE_ROUTE_RENORM = 1
+MOE_FFN_AUTO, MOE_FFN_GEMV, MOE_FFN_GROUPED = 0, 1, 2
+
+_vp, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+
+
+class moe_lru(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("S", ctypes.c_int32), ("slot_expert", _vp),
+                ("expert_slot", _vp), ("slot_stamp", _vp), ("clock", _vp)]
+
+
+SIGNATURES = {
+    "moe_status_str": (ctypes.c_char_p, [_i32]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_abi_version": (_i32, []),
+    "moe_expert_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_pack_expert": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_vp), _vp]),
+    "moe_unpack_expert": (_i32, [_i32, _i32, _i32, _vp, ctypes.POINTER(_vp)]),
+    "moe_route_workspace": (_sz, [_i32, _i32, _i32]),
+    "moe_route": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_lru_reset": (_i32, [ctypes.POINTER(moe_lru), _vp]),
+    "moe_miss_record_words": (_sz, [_i32, _i32, _i32]),
+    "moe_cache_lookup": (_i32, [ctypes.POINTER(moe_lru), _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "moe_cache_fill": (_i32, [_vp, _vp, _vp, _sz, _sz, _vp, _vp, _vp]),
+    "moe_ffn_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "moe_expert_ffn": (_i32, [_i32, _vp, _sz, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp,
+                              _vp, _i32, _vp, _vp, _vp, _u32, _vp, _sz, _vp]),
+    "moe_combine": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "moe_layer_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "moe_layer_forward": (_i32, [_i32, _vp, _sz, _i32, _i32, _i32, _i32, _u32, _vp, _i32, _vp, _vp, _vp,
+                                 _vp, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: the HIP library must be built "
+                               "(__graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        detail = lib().moe_last_error().decode()
+        super().__init__(f"{where}: {lib().moe_status_str(status).decode()} ({status}) {detail}")
+
+
+def _check(st, where):
+    if st != MOE_OK:
+        raise MoeError(st, where)
+
+
+def _ptr(t):
+    """Device/host address of a torch tensor or numpy array (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ blobs
+
+def moe_expert_bytes(fmt, H, F):
+    return int(lib().moe_expert_bytes(fmt, H, F))
+
+
+def blob_stride(fmt, H, F):
+    return (moe_expert_bytes(fmt, H, F) + 255) // 256 * 256
+
+
+def _canon_ptrs(canon, fmt):
+    keys = ("codes_g", "codes_u", "codes_d", "scales_g", "scales_u", "scales_d")
+    arrs = [np.ascontiguousarray(canon[k]) for k in keys]
+    taus = [np.array([canon.get("tau_" + m, 1.0)], dtype=np.float32) for m in "gud"]
+    keep = arrs + taus
+    ptrs = (_vp * 9)(*[a.ctypes.data for a in keep])
+    return ptrs, keep
+
+
+def moe_pack_expert(fmt, H, F, canon, blob=None):
+    """Canonical dict -> packed blob (numpy uint8; written into ``blob`` if given)."""
+    n = moe_expert_bytes(fmt, H, F)
+    if blob is None:
+        blob = np.empty(n, dtype=np.uint8)
+    if blob.nbytes < n or not blob.flags["C_CONTIGUOUS"]:
+        raise ValueError("blob too small or not contiguous")
+    ptrs, keep = _canon_ptrs(canon, fmt)
+    _check(lib().moe_pack_expert(fmt, H, F, ptrs, blob.ctypes.data), "moe_pack_expert")
+    return blob
+
+
+def moe_unpack_expert(fmt, H, F, blob):
+    fp8 = fmt == MOE_FMT_FP8_E4M3
+    cw = (lambda N, K: (N, K)) if fp8 else (lambda N, K: (N, K // 2))
+    if fmt == MOE_FMT_NVFP4:
+        sw, sdt = (lambda N, K: (N, K // 16)), np.uint8
+    elif fmt == MOE_FMT_MXFP4:
+        sw, sdt = (lambda N, K: (N, K // 32)), np.uint8
+    else:
+        sw, sdt = (lambda N, K: (N, K // 128)), np.float32
+    out = dict(codes_g=np.empty(cw(F, H), np.uint8), codes_u=np.empty(cw(F, H), np.uint8),
+               codes_d=np.empty(cw(H, F), np.uint8), scales_g=np.empty(sw(F, H), sdt),
+               scales_u=np.empty(sw(F, H), sdt), scales_d=np.empty(sw(H, F), sdt))
+    taus = [np.zeros(1, np.float32) for _ in range(3)]
+    keys = ("codes_g", "codes_u", "codes_d", "scales_g", "scales_u", "scales_d")
+    ptrs = (_vp * 9)(*([out[k].ctypes.data for k in keys] + [t.ctypes.data for t in taus]))
+    blob = np.ascontiguousarray(blob)
+    _check(lib().moe_unpack_expert(fmt, H, F, blob.ctypes.data, ptrs), "moe_unpack_expert")
+    out["tau_g"], out["tau_u"], out["tau_d"] = (np.float32(t[0]) for t in taus)
+    return out
+
+
+def pack_layer(fmt, H, F, batch, dst, stride):
+    """Pack a synth ``experts`` batch (leading axis = expert) into ``dst`` at ``stride``."""
+    n = batch["codes_g"].shape[0]
+    for i in range(n):
+        canon = {k: batch[k][i] for k in ("codes_g", "codes_u", "codes_d", "scales_g", "scales_u", "scales_d")}
+        canon["tau_g"], canon["tau_u"], canon["tau_d"] = batch["tau"][i]
+        moe_pack_expert(fmt, H, F, canon, dst[i * stride:(i + 1) * stride])
+    return dst
+
+
+# ---------------------------------------------------------------- routing
+
+def moe_route_workspace(T, E, k):
+    return int(lib().moe_route_workspace(T, E, k))
+
+
+def new_route_workspace(T, E, k, device="cuda"):
+    import torch
+    return torch.zeros(moe_route_workspace(T, E, k) + 256, dtype=torch.uint8, device=device)
+
+
+def moe_route(x, router, k, flags=0, topk_idx=None, topk_w=None, pair_perm=None, expert_off=None,
+              ws=None, want_perm=True, stream=None):
+    import torch
+    T, H = x.shape
+    E = router.shape[0]
+    dev = x.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if want_perm and pair_perm is None:
+        pair_perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+        expert_off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = new_route_workspace(T, E, k, dev)
+    st = lib().moe_route(_ptr(x), _ptr(router), T, H, E, k, flags, _ptr(topk_idx), _ptr(topk_w),
+                         _ptr(pair_perm), _ptr(expert_off), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "moe_route")
+    return topk_idx, topk_w, pair_perm, expert_off
+
+
+# ------------------------------------------------------------------ cache
+
+class LRUState:
+    """Per-layer LRU state in device memory (torch tensors) + the C struct view."""
+
+    def __init__(self, E, S, device="cuda"):
+        import torch
+        self.E, self.S = E, S
+        self.slot_expert = torch.full((S,), -1, dtype=torch.int32, device=device)
+        self.expert_slot = torch.full((E,), -1, dtype=torch.int32, device=device)
+        self.slot_stamp = torch.zeros(S, dtype=torch.int64, device=device)
+        self.clock = torch.zeros(1, dtype=torch.int64, device=device)
+
+    def c(self):
+        return moe_lru(self.E, self.S, _ptr(self.slot_expert), _ptr(self.expert_slot),
+                       _ptr(self.slot_stamp), _ptr(self.clock))
+
+
+def moe_lru_reset(state, stream=None):
+    s = state.c()
+    _check(lib().moe_lru_reset(ctypes.byref(s), _stream(stream)), "moe_lru_reset")
+
+
+def moe_miss_record_words(T, k, S):
+    return int(lib().moe_miss_record_words(T, k, S))
+
+
+def moe_cache_lookup(state, topk_idx, pair_slot, pair_order, miss_rec, stream=None):
+    T, k = topk_idx.shape
+    s = state.c()
+    st = lib().moe_cache_lookup(ctypes.byref(s), _ptr(topk_idx), T, k, _ptr(pair_slot),
+                                _ptr(pair_order), _ptr(miss_rec), _stream(stream))
+    _check(st, "moe_cache_lookup")
+
+
+def moe_cache_fill(miss_rec_host, host_pool, slot_pool, expert_bytes, stride, slots_free=None,
+                   copy_stream=None, fill_done=None):
+    ev = lambda e: None if e is None else e.cuda_event  # noqa: E731
+    st = lib().moe_cache_fill(_ptr(miss_rec_host), _ptr(host_pool), _ptr(slot_pool), expert_bytes,
+                              stride, ev(slots_free), _stream(copy_stream), ev(fill_done))
+    _check(st, "moe_cache_fill")
+
+
+# ------------------------------------------------------------ expert FFN
+
+def moe_ffn_workspace(fmt, T, H, F, k, E):
+    return int(lib().moe_ffn_workspace(fmt, T, H, F, k, E))
+
+
+def new_ffn_workspace(fmt, T, H, F, k, E, device="cuda"):
+    import torch
+    return torch.empty(moe_ffn_workspace(fmt, T, H, F, k, E) + 256, dtype=torch.uint8, device=device)
+
+
+def moe_expert_ffn(fmt, slot_pool, stride, H, F, E, x, topk_idx, pair_slot=None, pair_perm=None,
+                   expert_off=None, pair_subset=None, topk_w=None, y=None, out=None, flags=0,
+                   ws=None, stream=None):
+    T, k = topk_idx.shape
+    if ws is None:
+        ws = new_ffn_workspace(fmt, T, H, F, k, E, x.device)
+    n_subset = 0 if pair_subset is None else int(pair_subset.numel())
+    st = lib().moe_expert_ffn(fmt, _ptr(slot_pool), stride, H, F, E, _ptr(x), T, k, _ptr(topk_idx),
+                              _ptr(pair_slot), _ptr(pair_perm), _ptr(expert_off), _ptr(pair_subset),
+                              n_subset, _ptr(topk_w), _ptr(y), _ptr(out), flags, _ptr(ws), ws.numel(),
+                              _stream(stream))
+    _check(st, "moe_expert_ffn")
+    return y, out
+
+
+def moe_combine(y, topk_w, out, stream=None):
+    T, k = topk_w.shape
+    H = y.shape[-1]
+    _check(lib().moe_combine(_ptr(y), _ptr(topk_w), T, H, k, _ptr(out), _stream(stream)), "moe_combine")
+    return out
+
+
+# ------------------------------------------------------------ whole layer
+
+def moe_layer_workspace(fmt, T, H, F, k, E):
+    return int(lib().moe_layer_workspace(fmt, T, H, F, k, E))
+
+
+def new_layer_workspace(fmt, T, H, F, k, E, device="cuda"):
+    import torch
+    return torch.empty(moe_layer_workspace(fmt, T, H, F, k, E) + 256, dtype=torch.uint8, device=device)
+
+
+def moe_layer_forward(fmt, pool, stride, H, F, E, k, x, router, flags=0, topk_idx=None, topk_w=None,
+                      out=None, ws=None, stream=None):
+    import torch
+    T = x.shape[0]
+    dev = x.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.uint16, device=dev)
+    if ws is None:
+        ws = new_layer_workspace(fmt, T, H, F, k, E, dev)
+    st = lib().moe_layer_forward(fmt, _ptr(pool), stride, H, F, E, k, flags, _ptr(x), T, _ptr(router),
+                                 _ptr(topk_idx), _ptr(topk_w), _ptr(out), _ptr(ws), ws.numel(),
+                                 _stream(stream))
+    _check(st, "moe_layer_forward")
+    return topk_idx, topk_w, out

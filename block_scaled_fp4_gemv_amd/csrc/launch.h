@@ -1,0 +1,61 @@
+// Internal launcher interface between the C-ABI host code and the kernels.
+#pragma once
+#include "common.h"
+
+struct FfnArgs {
+  int fmt, H, F, E, T, k;
+  const uint8_t* pool;
+  size_t stride;
+  BlobLayout L;
+  const uint16_t* x;
+  const int32_t* topk_idx;
+  const int32_t* pair_slot;
+  const int32_t* pair_perm;
+  const int32_t* expert_off;
+  const int32_t* pair_subset;
+  int n_pairs;  // pairs to compute (n_subset, or T*k)
+  const float* topk_w;
+  float* y;        // [T*k][H] or NULL
+  uint16_t* out;   // [T][H] or NULL
+  uint16_t* hbuf;  // workspace [T*k][F] bf16
+  float* ybuf;     // workspace [T*k][H] fp32 (grouped path with fused combine)
+};
+
+// GEMV path: gate/up + SwiGLU into hbuf, then down (+ combine when out != NULL).
+hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s);
+// Decode layer: gate/up with the softmax/top-k of `logits` computed inside each
+// workgroup (writes topk_idx/topk_w), then down + combine.  T*k pairs, T <= 4.
+hipError_t launch_decode_layer(const FfnArgs& a, const float* logits, unsigned route_flags,
+                               int32_t* topk_idx, float* topk_w, hipStream_t s);
+// Grouped MFMA path (expert-sorted pairs).
+hipError_t launch_ffn_grouped(const FfnArgs& a, hipStream_t s);
+
+struct RouteArgs {
+  const uint16_t* x;
+  const float* router;
+  int T, H, E, k;
+  unsigned flags;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* pair_perm;
+  int32_t* expert_off;
+  // workspace carve-up
+  float* logits;       // [T][E]
+  int32_t* chunk_cnt;  // [n_chunks][E]
+};
+size_t route_ws_bytes(int T, int E, int k);
+void route_ws_carve(RouteArgs& a, void* ws);
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// Router logits only ([T][E] fp32): GEMV kernel for T <= 4, tiled GEMM otherwise.
+hipError_t launch_router_logits(const uint16_t* x, const float* R, int T, int H, int E, float* logits,
+                                hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, unsigned flags, int32_t* idx,
+                       float* w, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, uint16_t* out,
+                          hipStream_t s);
+
+hipError_t launch_lru_reset(const moe_lru& l, hipStream_t s);
+hipError_t launch_lru_lookup(const moe_lru& l, const int32_t* topk_idx, int n_pairs,
+                             int32_t* pair_slot, int32_t* pair_order, int32_t* miss_rec, int n_max,
+                             hipStream_t s);

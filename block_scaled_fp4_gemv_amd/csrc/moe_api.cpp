@@ -1,0 +1,359 @@
+// C-ABI entry points: argument validation, workspace carving and dispatch.
+// Every check runs on the host before any HIP call; nothing throws across the
+// ABI.  Semantics of each call are documented in include/moe_fp4.h.
+#include <stdio.h>
+#include <string.h>
+
+#include <cstdarg>
+
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool valid_fmt(int fmt) {
+  return fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_MXFP4 || fmt == MOE_FMT_FP8_E4M3;
+}
+
+bool valid_dim(int v) {
+  switch (v) {
+    case 256: case 512: case 1024: case 2048: case 4096: case 6144: case 8192: return true;
+    default: return false;
+  }
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(int fmt, int H, int F) {
+  if (!valid_fmt(fmt)) return fail(MOE_E_FORMAT, "unknown format %d", fmt);
+  if (!valid_dim(H) || !valid_dim(F))
+    return fail(MOE_E_ARG, "H=%d F=%d: each must be one of 256,512,1024,2048,4096,6144,8192", H, F);
+  return MOE_OK;
+}
+
+int check_route_dims(int T, int H, int E, int k) {
+  if (T < 0) return fail(MOE_E_ARG, "T=%d < 0", T);
+  if (!valid_dim(H)) return fail(MOE_E_ARG, "H=%d unsupported", H);
+  if (E < 1 || E > 1024) return fail(MOE_E_ARG, "E=%d outside [1, 1024]", E);
+  if (k < 1 || k > E || k > 64) return fail(MOE_E_ARG, "k=%d outside [1, min(E, 64)]", k);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_E_ARG: return "invalid argument";
+    case MOE_E_FORMAT: return "unknown weight format";
+    case MOE_E_CAPACITY: return "cache capacity exceeded";
+    case MOE_E_WORKSPACE: return "workspace missing or too small";
+    case MOE_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_abi_version(void) { return (1 << 16) | 0; }
+
+// ------------------------------------------------------------------ blobs
+
+size_t moe_expert_bytes(int fmt, int H, int F) {
+  if (!valid_fmt(fmt) || !valid_dim(H) || !valid_dim(F)) return 0;
+  return blob_layout(fmt, H, F).total;
+}
+
+static void copy_sections(int fmt, int H, int F, const BlobLayout& L, uint8_t* blob,
+                          void* const canon[9], bool to_blob) {
+  const size_t off[6] = {L.cg, L.cu, L.cd, L.sg, L.su, L.sd};
+  const size_t len[6] = {code_bytes(fmt, F, H), code_bytes(fmt, F, H), code_bytes(fmt, H, F),
+                         scale_bytes(fmt, F, H), scale_bytes(fmt, F, H), scale_bytes(fmt, H, F)};
+  for (int i = 0; i < 6; ++i) {
+    if (to_blob)
+      memcpy(blob + off[i], canon[i], len[i]);
+    else
+      memcpy(canon[i], blob + off[i], len[i]);
+  }
+  float* tau = reinterpret_cast<float*>(blob + L.tau);
+  for (int i = 0; i < 3; ++i) {
+    if (to_blob) {
+      tau[i] = (fmt == MOE_FMT_NVFP4) ? *static_cast<const float*>(canon[6 + i]) : 1.0f;
+    } else if (canon[6 + i]) {
+      *static_cast<float*>(canon[6 + i]) = tau[i];
+    }
+  }
+}
+
+int moe_pack_expert(int fmt, int H, int F, const void* const canon[9], void* blob) {
+  g_err[0] = 0;
+  int st = check_shape(fmt, H, F);
+  if (st) return st;
+  if (!canon || !blob) return fail(MOE_E_ARG, "NULL canon or blob");
+  const int need = fmt == MOE_FMT_NVFP4 ? 9 : 6;
+  for (int i = 0; i < need; ++i)
+    if (!canon[i]) return fail(MOE_E_ARG, "canon[%d] is NULL", i);
+  const BlobLayout L = blob_layout(fmt, H, F);
+  uint8_t* b = static_cast<uint8_t*>(blob);
+  memset(b, 0, L.total);
+  copy_sections(fmt, H, F, L, b, const_cast<void* const*>(canon), true);
+  return MOE_OK;
+}
+
+int moe_unpack_expert(int fmt, int H, int F, const void* blob, void* const canon[9]) {
+  g_err[0] = 0;
+  int st = check_shape(fmt, H, F);
+  if (st) return st;
+  if (!canon || !blob) return fail(MOE_E_ARG, "NULL canon or blob");
+  for (int i = 0; i < 6; ++i)
+    if (!canon[i]) return fail(MOE_E_ARG, "canon[%d] is NULL", i);
+  copy_sections(fmt, H, F, blob_layout(fmt, H, F),
+                const_cast<uint8_t*>(static_cast<const uint8_t*>(blob)), canon, false);
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- routing
+
+size_t moe_route_workspace(int T, int E, int k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  return route_ws_bytes(T, E, k);
+}
+
+int moe_route(const uint16_t* x, const float* router, int T, int H, int E, int k, unsigned flags,
+              int32_t* topk_idx, float* topk_w, int32_t* pair_perm, int32_t* expert_off, void* ws,
+              size_t ws_bytes, moe_stream_t stream) {
+  g_err[0] = 0;
+  int st = check_route_dims(T, H, E, k);
+  if (st) return st;
+  if (flags & ~MOE_ROUTE_RENORM) return fail(MOE_E_ARG, "unknown route flags 0x%x", flags);
+  if (T > 0 && (pair_perm == nullptr) != (expert_off == nullptr))
+    return fail(MOE_E_ARG, "pair_perm and expert_off must both be given or both be NULL");
+  if (T > 0 && (!x || !router || !topk_idx || !topk_w))
+    return fail(MOE_E_ARG, "NULL x/router/topk_idx/topk_w");
+  if (!aligned(x, 16) || !aligned(router, 16)) return fail(MOE_E_ARG, "x and router must be 16-byte aligned");
+  if (!ws || !aligned(ws, 256) || ws_bytes < route_ws_bytes(T, E, k))
+    return fail(MOE_E_WORKSPACE, "route workspace needs %zu bytes, 256-aligned", route_ws_bytes(T, E, k));
+  RouteArgs a{};
+  a.x = x; a.router = router; a.T = T; a.H = H; a.E = E; a.k = k; a.flags = flags;
+  a.topk_idx = topk_idx; a.topk_w = topk_w; a.pair_perm = pair_perm; a.expert_off = expert_off;
+  route_ws_carve(a, ws);
+  hipError_t e = launch_route(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route");
+}
+
+// ------------------------------------------------------------------ cache
+
+int moe_lru_reset(const moe_lru* lru, moe_stream_t stream) {
+  g_err[0] = 0;
+  if (!lru || !lru->slot_expert || !lru->expert_slot || !lru->slot_stamp || !lru->clock)
+    return fail(MOE_E_ARG, "NULL lru state");
+  if (lru->E < 1 || lru->E > 1024 || lru->S < 1 || lru->S > 1024)
+    return fail(MOE_E_ARG, "E=%d S=%d outside [1, 1024]", lru->E, lru->S);
+  hipError_t e = launch_lru_reset(*lru, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_lru_reset");
+}
+
+size_t moe_miss_record_words(int T, int k, int S) {
+  if (T < 0 || k < 1 || S < 1) return 0;
+  const long long n = (long long)T * k;
+  const long long nmax = n < S ? n : S;
+  return (size_t)(5 + 2 * nmax);
+}
+
+int moe_cache_lookup(const moe_lru* lru, const int32_t* topk_idx, int T, int k, int32_t* pair_slot,
+                     int32_t* pair_order, int32_t* miss_rec, moe_stream_t stream) {
+  g_err[0] = 0;
+  if (!lru || !lru->slot_expert || !lru->expert_slot || !lru->slot_stamp || !lru->clock)
+    return fail(MOE_E_ARG, "NULL lru state");
+  if (lru->E < 1 || lru->E > 1024 || lru->S < 1 || lru->S > 1024)
+    return fail(MOE_E_ARG, "E=%d S=%d outside [1, 1024]", lru->E, lru->S);
+  if (T < 0 || k < 1 || k > lru->E) return fail(MOE_E_ARG, "T=%d k=%d", T, k);
+  if (!miss_rec) return fail(MOE_E_ARG, "NULL miss_rec");
+  const int n = T * k;
+  if (n > 0 && (!topk_idx || !pair_slot || !pair_order)) return fail(MOE_E_ARG, "NULL pair arrays");
+  const int n_max = n < lru->S ? n : lru->S;
+  hipError_t e = launch_lru_lookup(*lru, topk_idx, n, pair_slot, pair_order, miss_rec, n_max,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_cache_lookup");
+}
+
+int moe_cache_fill(const int32_t* rec, const void* host_pool, void* slot_pool, size_t expert_bytes,
+                   size_t stride, moe_event_t slots_free, moe_stream_t copy_stream,
+                   moe_event_t fill_done) {
+  g_err[0] = 0;
+  if (!rec || !host_pool || !slot_pool) return fail(MOE_E_ARG, "NULL record or pool");
+  if (rec[0] != MOE_OK) return fail(MOE_E_CAPACITY, "miss record status %d", rec[0]);
+  if (stride < expert_bytes || stride % 256) return fail(MOE_E_ARG, "bad stride %zu", stride);
+  const int n_miss = rec[1], n_max = rec[4];
+  if (n_miss < 0 || n_miss > n_max) return fail(MOE_E_ARG, "corrupt miss record");
+  hipStream_t cs = static_cast<hipStream_t>(copy_stream);
+  hipError_t e;
+  if (slots_free) {
+    e = hipStreamWaitEvent(cs, static_cast<hipEvent_t>(slots_free), 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  const uint8_t* hp = static_cast<const uint8_t*>(host_pool);
+  uint8_t* sp = static_cast<uint8_t*>(slot_pool);
+  for (int r = 0; r < n_miss; ++r) {
+    const int ex = rec[5 + r], sl = rec[5 + n_max + r];
+    e = hipMemcpyAsync(sp + (size_t)sl * stride, hp + (size_t)ex * stride, expert_bytes,
+                       hipMemcpyHostToDevice, cs);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  }
+  if (fill_done) {
+    e = hipEventRecord(static_cast<hipEvent_t>(fill_done), cs);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- expert FFN
+
+size_t moe_ffn_workspace(int fmt, int T, int H, int F, int k, int E) {
+  if (!valid_fmt(fmt) || T < 0 || k < 1 || E < 1 || !valid_dim(H) || !valid_dim(F)) return 0;
+  const size_t n = (size_t)T * k;
+  return align256(n * F * 2) + align256(n * H * 4) + 256;
+}
+
+int moe_expert_ffn(int fmt, const void* slot_pool, size_t stride, int H, int F, int E,
+                   const uint16_t* x, int T, int k, const int32_t* topk_idx,
+                   const int32_t* pair_slot, const int32_t* pair_perm, const int32_t* expert_off,
+                   const int32_t* pair_subset, int n_subset, const float* topk_w, float* y,
+                   uint16_t* out, unsigned flags, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  g_err[0] = 0;
+  int st = check_shape(fmt, H, F);
+  if (st) return st;
+  if (E < 1 || E > 1024) return fail(MOE_E_ARG, "E=%d outside [1, 1024]", E);
+  if (T < 0 || k < 1 || k > E || k > 64) return fail(MOE_E_ARG, "T=%d k=%d", T, k);
+  if (flags > MOE_FFN_GROUPED) return fail(MOE_E_ARG, "unknown ffn flags 0x%x", flags);
+  if (T == 0) return MOE_OK;
+  if (!y && !out) return fail(MOE_E_ARG, "y and out are both NULL");
+  if (out && !topk_w) return fail(MOE_E_ARG, "out needs topk_w");
+  if (out && pair_subset) return fail(MOE_E_ARG, "the fused combine needs all pairs (pair_subset NULL)");
+  if (pair_subset && (n_subset < 0 || n_subset > T * k)) return fail(MOE_E_ARG, "n_subset=%d", n_subset);
+  const size_t eb = blob_layout(fmt, H, F).total;
+  if (stride < eb || stride % 256) return fail(MOE_E_ARG, "stride %zu < blob %zu or not 256-multiple", stride, eb);
+  if (!slot_pool || !aligned(slot_pool, 256)) return fail(MOE_E_ARG, "slot_pool NULL or not 256-aligned");
+  if (T > 0 && (!x || !topk_idx)) return fail(MOE_E_ARG, "NULL x/topk_idx");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(out, 16))
+    return fail(MOE_E_ARG, "x, y and out must be 16-byte aligned");
+  const size_t need = moe_ffn_workspace(fmt, T, H, F, k, E);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "ffn workspace needs %zu bytes, 256-aligned", need);
+
+  bool grouped = false;
+  const bool have_perm = pair_perm && expert_off;
+  if (flags == MOE_FFN_GROUPED) {
+    if (!have_perm) return fail(MOE_E_ARG, "grouped path needs pair_perm and expert_off");
+    if (pair_subset) return fail(MOE_E_ARG, "grouped path computes all pairs (pair_subset NULL)");
+    grouped = true;
+  } else if (flags == MOE_FFN_AUTO) {
+    grouped = have_perm && !pair_subset && (long long)T * k >= 2LL * E;
+  }
+  if (!grouped && out && k > 16) return fail(MOE_E_ARG, "fused combine on the GEMV path needs k <= 16");
+
+  FfnArgs a{};
+  a.fmt = fmt; a.H = H; a.F = F; a.E = E; a.T = T; a.k = k;
+  a.pool = static_cast<const uint8_t*>(slot_pool); a.stride = stride; a.L = blob_layout(fmt, H, F);
+  a.x = x; a.topk_idx = topk_idx; a.pair_slot = pair_slot; a.pair_perm = pair_perm;
+  a.expert_off = expert_off; a.pair_subset = pair_subset;
+  a.n_pairs = pair_subset ? n_subset : T * k;
+  a.topk_w = topk_w; a.y = y; a.out = out;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  a.hbuf = reinterpret_cast<uint16_t*>(p);
+  a.ybuf = reinterpret_cast<float*>(p + align256((size_t)T * k * F * 2));
+  if (T == 0 || a.n_pairs == 0) return MOE_OK;
+  hipError_t e = grouped ? launch_ffn_grouped(a, static_cast<hipStream_t>(stream))
+                         : launch_ffn_gemv(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, grouped ? "moe_expert_ffn(grouped)" : "moe_expert_ffn(gemv)");
+}
+
+size_t moe_layer_workspace(int fmt, int T, int H, int F, int k, int E) {
+  const size_t ffn = moe_ffn_workspace(fmt, T, H, F, k, E);
+  if (!ffn || E > 1024) return 0;
+  const size_t n = (size_t)T * k;
+  return align256(route_ws_bytes(T, E, k)) + align256(n * 4) + align256((size_t)(E + 1) * 4) + ffn;
+}
+
+int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, int E, int k,
+                      unsigned route_flags, const uint16_t* x, int T, const float* router,
+                      int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                      moe_stream_t stream) {
+  g_err[0] = 0;
+  int st = check_shape(fmt, H, F);
+  if (st) return st;
+  st = check_route_dims(T, H, E, k);
+  if (st) return st;
+  if (route_flags & ~MOE_ROUTE_RENORM) return fail(MOE_E_ARG, "unknown route flags 0x%x", route_flags);
+  if (k > 16) return fail(MOE_E_ARG, "moe_layer_forward needs k <= 16");
+  const size_t eb = blob_layout(fmt, H, F).total;
+  if (stride < eb || stride % 256) return fail(MOE_E_ARG, "stride %zu < blob %zu or not 256-multiple", stride, eb);
+  if (!pool || !aligned(pool, 256)) return fail(MOE_E_ARG, "pool NULL or not 256-aligned");
+  if (T == 0) return MOE_OK;
+  if (!x || !router || !topk_idx || !topk_w || !out) return fail(MOE_E_ARG, "NULL argument");
+  if (!aligned(x, 16) || !aligned(router, 16) || !aligned(out, 16))
+    return fail(MOE_E_ARG, "x, router and out must be 16-byte aligned");
+  const size_t need = moe_layer_workspace(fmt, T, H, F, k, E);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "layer workspace needs %zu bytes, 256-aligned", need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  RouteArgs r{};
+  r.x = x; r.router = router; r.T = T; r.H = H; r.E = E; r.k = k; r.flags = route_flags;
+  r.topk_idx = topk_idx; r.topk_w = topk_w;
+  route_ws_carve(r, p);
+  p += align256(route_ws_bytes(T, E, k));
+  int32_t* perm = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)T * k * 4);
+  int32_t* off = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)(E + 1) * 4);
+  FfnArgs a{};
+  a.fmt = fmt; a.H = H; a.F = F; a.E = E; a.T = T; a.k = k;
+  a.pool = static_cast<const uint8_t*>(pool); a.stride = stride; a.L = blob_layout(fmt, H, F);
+  a.x = x; a.topk_idx = topk_idx; a.topk_w = topk_w; a.out = out; a.n_pairs = T * k;
+  a.hbuf = reinterpret_cast<uint16_t*>(p);
+  a.ybuf = reinterpret_cast<float*>(p + align256((size_t)T * k * F * 2));
+  hipError_t e;
+  if (T <= 4) {
+    e = launch_router_logits(x, router, T, H, E, r.logits, s);
+    if (e == hipSuccess) e = launch_decode_layer(a, r.logits, route_flags, topk_idx, topk_w, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_layer_forward(decode)");
+  }
+  r.pair_perm = perm;
+  r.expert_off = off;
+  e = launch_route(r, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward(route)");
+  a.pair_perm = perm;
+  a.expert_off = off;
+  const bool grouped = (long long)T * k >= 2LL * E;
+  e = grouped ? launch_ffn_grouped(a, s) : launch_ffn_gemv(a, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_layer_forward(ffn)");
+}
+
+int moe_combine(const float* y, const float* topk_w, int T, int H, int k, uint16_t* out,
+                moe_stream_t stream) {
+  g_err[0] = 0;
+  if (T < 0 || k < 1 || !valid_dim(H)) return fail(MOE_E_ARG, "T=%d H=%d k=%d", T, H, k);
+  if (T > 0 && (!y || !topk_w || !out)) return fail(MOE_E_ARG, "NULL y/topk_w/out");
+  if (!aligned(y, 16) || !aligned(out, 16)) return fail(MOE_E_ARG, "y and out must be 16-byte aligned");
+  hipError_t e = launch_combine(y, topk_w, T, H, k, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,253 @@
+/* moe_fp4.h - C ABI of the routed block-scaled MoE layer forward for MI355X (gfx950).
+ *
+ * The calls follow the layer as the FreeToken pages state the problem:
+ *   - the gate is a linear layer followed by a softmax giving a selection
+ *     probability per expert; the top-K experts are evaluated and their
+ *     outputs mixed by a weighted sum; every expert is an independent FFN
+ *     (page "FreeToken：753B大模型塞进单卡的本地部署硬件账该怎么算", section
+ *     "混合专家架构（MoE）的天然稀疏性");
+ *   - low-precision weights are dequantized at compute time (page
+ *     "8GB显存跑35B MoE模型：FreeToken引擎本地部署实战", §2.1) and the formats
+ *     are NVFP4 / MXFP4 / FP8 (page "8GB 笔记本 39.3 tok/s、单卡跑 753B：FreeToken
+ *     把 frontier MoE 拉回本地", section "局限");
+ *   - routed experts are looked up in a global LRU expert cache in VRAM, and
+ *     misses become a GPU cache fill (same page, section "设计核心"), copied
+ *     asynchronously on a stream, overlapped with compute (page "753B...",
+ *     section "按带宽动态分配参数存储").
+ *
+ * Conventions
+ *   - Pointers are DEVICE pointers unless marked [host] (ordinary or pinned
+ *     host memory) or [pinned] (host memory from hipHostMalloc, which the GPU
+ *     can also address).  bf16 values are uint16_t bit patterns.
+ *   - moe_stream_t / moe_event_t are hipStream_t / hipEvent_t handles (NULL =
+ *     the null stream / no event).
+ *   - The caller owns and allocates every buffer (weights, slot pool, host
+ *     pool, LRU state, outputs, workspaces), every stream and every event.
+ *     The library allocates no memory and keeps no mutable global state
+ *     except the per-thread error text; calls are reentrant.
+ *   - Every GPU call is stream-ordered: it validates its arguments on the
+ *     host, enqueues its kernels and returns.  Errors are negative status
+ *     codes; nothing aborts or throws across the ABI.  Shape/argument errors
+ *     are detected before any HIP call.  A failed launch returns MOE_E_HIP
+ *     with detail in moe_last_error().  Faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *
+ * Weight formats (one matrix W[N][K]; blocks run along K, the reduction
+ * dimension of each output row):
+ *   NVFP4: W = e2m1(code) * e4m3(scale[n][k/16]) * tau   (tau: fp32 per matrix)
+ *   MXFP4: W = e2m1(code) * 2^(scale[n][k/32] - 127)     (OCP MX v1.0)
+ *   FP8  : W = e4m3(code) * sigma[n][k/128]              (sigma: fp32)
+ * E2M1: 4-bit S.EE.M, bias 1 (magnitudes 0,0.5,1,1.5,2,3,4,6).  E4M3: OCP
+ * "FN" (bias 7, max 448, S.1111.111 = NaN).  FP4 codes pack two elements per
+ * byte, element 2i in the low nibble.
+ *
+ * Supported shapes: H and F in {256, 512, 1024, 2048, 4096, 6144, 8192};
+ * 1 <= k <= min(E, 64), E <= 1024; T >= 0.  The GEMV path with the combine
+ * fused (out != NULL) needs k <= 16.
+ */
+#ifndef MOE_FP4_H
+#define MOE_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* hipStream_t */
+typedef void* moe_event_t;  /* hipEvent_t  */
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_E_ARG = -1,       /* invalid argument, shape or alignment            */
+  MOE_E_FORMAT = -2,    /* unknown weight format                           */
+  MOE_E_CAPACITY = -3,  /* more distinct misses than evictable slots       */
+  MOE_E_WORKSPACE = -4, /* workspace missing or too small                  */
+  MOE_E_HIP = -5        /* a HIP runtime call failed (see moe_last_error)  */
+};
+
+enum moe_fmt { MOE_FMT_NVFP4 = 1, MOE_FMT_MXFP4 = 2, MOE_FMT_FP8_E4M3 = 3 };
+
+/* moe_route flags */
+#define MOE_ROUTE_RENORM 1u /* w /= sum of the selected probabilities (off by default) */
+
+/* moe_expert_ffn flags */
+#define MOE_FFN_AUTO 0u
+#define MOE_FFN_GEMV 1u    /* per-pair weight-streaming GEMV (batch-1 decode shape)  */
+#define MOE_FFN_GROUPED 2u /* expert-grouped MFMA GEMM (prefill shape); needs pair_perm/expert_off */
+
+/* ------------------------------------------------------------------ misc */
+
+/* Static text for a status code. */
+const char* moe_status_str(int status);
+/* Detail of the last error on the calling thread ("" if none).  Static per-thread storage. */
+const char* moe_last_error(void);
+/* ABI version: (major << 16) | minor. */
+int moe_abi_version(void);
+
+/* --------------------------------------------------------- expert blobs */
+
+/* Bytes of one packed expert blob (gate, up, down with their scales and tensor
+ * scales) for the given format and shape; 0 if the format or shape is invalid.
+ * A blob holds, each section starting on a 256-byte boundary:
+ *   gate codes [F][H*b], up codes [F][H*b], down codes [H][F*b]   (b = 1/2 FP4, 1 FP8)
+ *   gate scales, up scales, down scales in the canonical layout below,
+ *   tau[3] (fp32; 1.0 for MXFP4/FP8).
+ * The slot pool and the host pool hold blobs at a caller-chosen stride that is
+ * >= moe_expert_bytes and a multiple of 256. */
+size_t moe_expert_bytes(int fmt, int H, int F);
+
+/* Canonical arrays of one expert, 9 pointers in this order:
+ *   [0] gate codes  uint8 [F][H/2] (FP4) or [F][H] (FP8)
+ *   [1] up codes    same shape
+ *   [2] down codes  uint8 [H][F/2] or [H][F]
+ *   [3] gate scales NVFP4 uint8 [F][H/16]; MXFP4 uint8 [F][H/32]; FP8 float [F][H/128]
+ *   [4] up scales   same
+ *   [5] down scales NVFP4 [H][F/16]; MXFP4 [H][F/32]; FP8 float [H][F/128]
+ *   [6] gate tau, [7] up tau, [8] down tau: one float each (ignored unless NVFP4;
+ *       may be NULL for MXFP4/FP8).
+ * moe_pack_expert: canonical [host] -> blob [host] (moe_expert_bytes bytes).
+ * moe_unpack_expert: blob [host] -> canonical [host]; the exact inverse.
+ * Both are pure host functions; MOE_E_ARG on NULL pointers or a bad shape. */
+int moe_pack_expert(int fmt, int H, int F, const void* const canon[9], void* blob);
+int moe_unpack_expert(int fmt, int H, int F, const void* blob, void* const canon[9]);
+
+/* ------------------------------------------------------------- routing */
+
+/* Workspace bytes for moe_route (device memory, 256-byte aligned, no
+ * initialisation needed). */
+size_t moe_route_workspace(int T, int E, int k);
+
+/* Router, softmax and top-k for T tokens (page "753B...", section
+ * "混合专家架构（MoE）的天然稀疏性").
+ *   x        bf16  [T][H]   token activations
+ *   router   float [E][H]   gate weights
+ *   topk_idx int32 [T][k]   out: experts by (fp32 logit desc, index asc)
+ *   topk_w   float [T][k]   out: softmax probability (over all E experts) of
+ *                           each selected expert; renormalised over the k
+ *                           selected when flags has MOE_ROUTE_RENORM
+ *   pair_perm  int32 [T*k]  out, optional (NULL): pairs q = t*k+j sorted stably
+ *                           by expert
+ *   expert_off int32 [E+1]  out, optional (NULL together with pair_perm):
+ *                           exclusive prefix sum of the pairs per expert
+ * Logits are fp32 sums of bf16*fp32 products. */
+int moe_route(const uint16_t* x, const float* router, int T, int H, int E, int k, unsigned flags,
+              int32_t* topk_idx, float* topk_w, int32_t* pair_perm, int32_t* expert_off,
+              void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* --------------------------------------------------------------- cache */
+
+/* Per-layer LRU state, caller-owned device memory (page "8GB 笔记本 39.3 tok/s...",
+ * section "设计核心": a global LRU expert cache in VRAM).
+ *   slot_expert int32 [S]  expert held by each slot, -1 = empty
+ *   expert_slot int32 [E]  slot holding each expert, -1 = not resident
+ *   slot_stamp  int64 [S]  clock value of the slot's last access (0 = never)
+ *   clock       int64 [1]  accesses so far */
+typedef struct moe_lru {
+  int32_t E, S;
+  int32_t* slot_expert;
+  int32_t* expert_slot;
+  int64_t* slot_stamp;
+  int64_t* clock;
+} moe_lru;
+
+/* Set the state to a cold cache (all slots empty, clock 0).  Stream-ordered. */
+int moe_lru_reset(const moe_lru* lru, moe_stream_t stream);
+
+/* int32 words of a miss record for T*k accesses to a pool of S slots:
+ *   [0] status (MOE_OK or MOE_E_CAPACITY)   [1] n_miss (distinct missed experts)
+ *   [2] n_hit_pairs (pairs whose expert was resident at the start of the step)
+ *   [3] n_hits (accesses minus n_miss)      [4] n_max = min(T*k, S)
+ *   [5 .. 5+n_max)          missed experts in order of first appearance
+ *   [5+n_max .. 5+2*n_max)  the victim slot assigned to each */
+size_t moe_miss_record_words(int T, int k, int S);
+
+/* One LRU step for the T*k accesses topk_idx (pair order q = t*k+j).
+ * Hits are judged against the state at the start of the step.  Each distinct
+ * missed expert takes a victim slot among slots whose expert is not requested
+ * in this step: empty slots by ascending index first, then occupied slots by
+ * ascending stamp.  Every access, in pair order, advances the clock and stamps
+ * its slot.  With too few candidates the record says MOE_E_CAPACITY and the
+ * state is left unchanged.
+ *   pair_slot  int32 [T*k]  out: slot of each pair after the step
+ *   pair_order int32 [T*k]  out: pairs resident at step start first, then the
+ *                           rest, each in ascending q (for moe_expert_ffn's
+ *                           pair_subset hit/miss split)
+ *   miss_rec   int32 [moe_miss_record_words]  out, device or [pinned] memory;
+ *                           valid on the host only after the caller has
+ *                           synchronised with an event recorded after this call.
+ * Limits: E <= 1024, S <= 1024.  The return value reports only argument and
+ * launch errors; capacity is reported in miss_rec[0]. */
+int moe_cache_lookup(const moe_lru* lru, const int32_t* topk_idx, int T, int k,
+                     int32_t* pair_slot, int32_t* pair_order, int32_t* miss_rec,
+                     moe_stream_t stream);
+
+/* Enqueue the GPU cache fill for a completed miss record (read on the host):
+ * copy_stream first waits on slots_free (if not NULL; record it after the last
+ * kernel that reads the victim slots), then one hipMemcpyAsync host->device of
+ * expert_bytes per miss, from host_pool + expert*stride to slot_pool +
+ * slot*stride, then fill_done is recorded (if not NULL).
+ *   miss_rec   [host] complete record from moe_cache_lookup
+ *   host_pool  [pinned] E blobs at `stride`
+ *   slot_pool  device, S blobs at `stride` */
+int moe_cache_fill(const int32_t* miss_rec, const void* host_pool, void* slot_pool,
+                   size_t expert_bytes, size_t stride, moe_event_t slots_free,
+                   moe_stream_t copy_stream, moe_event_t fill_done);
+
+/* ----------------------------------------------------------- expert FFN */
+
+/* Workspace bytes for moe_expert_ffn. */
+size_t moe_ffn_workspace(int fmt, int T, int H, int F, int k, int E);
+
+/* Expert FFNs of the routed pairs:  for pair q = t*k+j with e = topk_idx[q]
+ * and slot s = pair_slot ? pair_slot[q] : e,
+ *     h = bf16( silu(G_s x_t) * (U_s x_t) ),   y_q = D_s h        (fp32 out)
+ * with the weights of blob s dequantized in registers (never materialised).
+ *   slot_pool   device, blobs at `stride` bytes
+ *   x           bf16 [T][H]
+ *   topk_idx    int32 [T][k] (from moe_route)
+ *   pair_slot   int32 [T*k] or NULL (identity: slot = expert)
+ *   pair_perm, expert_off: from moe_route; required by the grouped path
+ *   pair_subset int32 [n_subset] or NULL (all pairs): compute only these pairs
+ *               (GEMV path; e.g. the hits while the misses are being filled)
+ *   topk_w, out: if out != NULL, also out[t] = bf16(sum_j w[t][j] * y[t][j])
+ *               (the combine fused; requires pair_subset == NULL)
+ *   y           float [T*k][H] pair-major, or NULL when out != NULL
+ *   flags       MOE_FFN_AUTO / MOE_FFN_GEMV / MOE_FFN_GROUPED
+ * AUTO picks the grouped MFMA path when pair_perm/expert_off are given, no
+ * subset is requested and T*k >= 2*E; otherwise the GEMV path. */
+int moe_expert_ffn(int fmt, const void* slot_pool, size_t stride, int H, int F, int E,
+                   const uint16_t* x, int T, int k, const int32_t* topk_idx,
+                   const int32_t* pair_slot, const int32_t* pair_perm, const int32_t* expert_off,
+                   const int32_t* pair_subset, int n_subset, const float* topk_w, float* y,
+                   uint16_t* out, unsigned flags, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Gate-weighted combine (page "753B...", section "混合专家架构（MoE）的天然稀疏性"):
+ *   out[t][n] = bf16( sum_{j=0..k-1} topk_w[t][j] * y[t*k+j][n] ), fp32 sum in j order. */
+int moe_combine(const float* y, const float* topk_w, int T, int H, int k, uint16_t* out,
+                moe_stream_t stream);
+
+/* -------------------------------------------------------- whole layer */
+
+/* Workspace bytes for moe_layer_forward. */
+size_t moe_layer_workspace(int fmt, int T, int H, int F, int k, int E);
+
+/* The whole layer for experts resident in `pool` (blob e at e*stride):
+ * moe_route (router, softmax over all E, top-k), moe_expert_ffn and the
+ * gate-weighted combine, with the same results as calling them in turn.
+ * For T <= 4 (decode) it runs three kernels: the router GEMV, gate/up +
+ * SwiGLU with the softmax/top-k evaluated inside each workgroup, and down +
+ * combine.  Larger T routes with the permutation and uses moe_expert_ffn's
+ * automatic path.
+ *   x bf16 [T][H], router float [E][H]; out bf16 [T][H];
+ *   topk_idx int32 [T][k], topk_w float [T][k] (outputs). */
+int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, int E, int k,
+                      unsigned route_flags, const uint16_t* x, int T, const float* router,
+                      int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                      moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FP4_H */

@@ -1,0 +1,137 @@
+"""The C-ABI library on the host: symbols, blob packing, and argument checks
+that run before any HIP call (no GPU needed)."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_scaled_fp4_gemv_amd import binding as B
+from block_scaled_fp4_gemv_amd import synth as sy
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 15
+    L = ctypes.CDLL(B.LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(B.SIGNATURES) == names
+
+
+def test_status_strings():
+    assert B.lib().moe_status_str(0) == b"ok"
+    assert B.lib().moe_status_str(B.MOE_E_CAPACITY) == b"cache capacity exceeded"
+    assert B.lib().moe_abi_version() == 1 << 16
+
+
+@pytest.mark.parametrize("fmt,H,F,exp", [
+    (1, 2048, 512, 3 * 524288 + 3 * 65536 + 256),
+    (2, 256, 512, 3 * 65536 + 2 * 4096 + 4096 + 256),
+    (3, 6144, 2048, 3 * 12582912 + 3 * 393216 + 256),
+])
+def test_expert_bytes(fmt, H, F, exp):
+    assert B.moe_expert_bytes(fmt, H, F) == exp
+
+
+@pytest.mark.parametrize("bad", [(0, 2048, 512), (4, 2048, 512), (1, 2000, 512), (1, 2048, 96)])
+def test_expert_bytes_invalid(bad):
+    assert B.moe_expert_bytes(*bad) == 0
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_pack_unpack_round_trip(fmt):
+    H, F = 256, 512
+    b = sy.experts(fmt, 0, 5, 0, 0, 1, H, F, 0.02)
+    canon = sy.expert_view(b, 0)
+    blob = B.moe_pack_expert(fmt, H, F, canon)
+    back = B.moe_unpack_expert(fmt, H, F, blob)
+    for key in ("codes_g", "codes_u", "codes_d", "scales_g", "scales_u", "scales_d"):
+        assert np.array_equal(back[key], canon[key]), key
+    if fmt == 1:
+        assert (back["tau_g"], back["tau_u"], back["tau_d"]) == (canon["tau_g"], canon["tau_u"], canon["tau_d"])
+    else:
+        assert back["tau_g"] == 1.0
+    # sections sit where the header says: gate codes first, 256-aligned sections
+    assert np.array_equal(blob[:canon["codes_g"].size], canon["codes_g"].ravel())
+
+
+def test_pack_rejects_null():
+    ptrs = (ctypes.c_void_p * 9)()
+    blob = np.zeros(B.moe_expert_bytes(1, 256, 512), np.uint8)
+    assert B.lib().moe_pack_expert(1, 256, 512, ptrs, blob.ctypes.data) == B.MOE_E_ARG
+    assert B.lib().moe_pack_expert(9, 256, 512, ptrs, blob.ctypes.data) == B.MOE_E_FORMAT
+
+
+def test_route_argument_errors_before_any_hip_call():
+    L = B.lib()
+    ws = np.zeros(1 << 20, np.uint8)
+    fake = 0x1000  # never dereferenced: validation fails first
+    args = lambda T, H, E, k, flags=0, ws_bytes=ws.nbytes, perm=None, off=None: (  # noqa: E731
+        fake, fake, T, H, E, k, flags, fake, fake, perm, off, ws.ctypes.data, ws_bytes, None)
+    assert L.moe_route(*args(1, 2048, 256, 0)) == B.MOE_E_ARG          # k < 1
+    assert L.moe_route(*args(1, 2048, 4, 5)) == B.MOE_E_ARG            # k > E
+    assert L.moe_route(*args(1, 2048, 2048, 8)) == B.MOE_E_ARG         # E > 1024
+    assert L.moe_route(*args(1, 1000, 256, 8)) == B.MOE_E_ARG          # H unsupported
+    assert L.moe_route(*args(-1, 2048, 256, 8)) == B.MOE_E_ARG
+    assert L.moe_route(*args(1, 2048, 256, 8, flags=4)) == B.MOE_E_ARG
+    assert L.moe_route(*args(1, 2048, 256, 8, perm=fake)) == B.MOE_E_ARG   # perm without off
+    assert L.moe_route(*args(64, 2048, 256, 8, ws_bytes=16)) == B.MOE_E_WORKSPACE
+    assert b"workspace" in L.moe_last_error()
+
+
+def test_ffn_argument_errors_before_any_hip_call():
+    L = B.lib()
+    fake = 0x100000
+    eb = B.blob_stride(1, 2048, 512)
+    raw = np.zeros((1 << 22) + 256, np.uint8)
+    ws = raw[(-raw.ctypes.data) % 256:][: 1 << 22]
+    def call(fmt=1, stride=eb, H=2048, F=512, E=256, T=1, k=8, y=fake, out=None, w=None,
+             subset=None, n_sub=0, flags=0, ws_bytes=ws.nbytes, perm=None, off=None):
+        return L.moe_expert_ffn(fmt, fake, stride, H, F, E, fake, T, k, fake, None, perm, off, subset,
+                                n_sub, w, y, out, flags, ws.ctypes.data, ws_bytes, None)
+    assert call(fmt=7) == B.MOE_E_FORMAT
+    assert call(H=3000) == B.MOE_E_ARG
+    assert call(stride=eb - 256) == B.MOE_E_ARG
+    assert call(stride=eb + 1) == B.MOE_E_ARG
+    assert call(y=None, out=None) == B.MOE_E_ARG
+    assert call(out=fake, w=None) == B.MOE_E_ARG
+    assert call(out=fake, w=fake, subset=fake, n_sub=1) == B.MOE_E_ARG
+    assert call(flags=B.MOE_FFN_GROUPED) == B.MOE_E_ARG              # no permutation
+    assert call(k=300) == B.MOE_E_ARG
+    assert call(ws_bytes=8) == B.MOE_E_WORKSPACE
+    assert call(k=32, E=64, out=fake, w=fake, flags=B.MOE_FFN_GEMV) == B.MOE_E_ARG   # fused needs k<=16
+
+
+def test_combine_and_lru_argument_errors():
+    L = B.lib()
+    assert L.moe_combine(0x1000, 0x1000, 1, 100, 8, 0x1000, None) == B.MOE_E_ARG
+    assert L.moe_combine(0x1004, 0x1000, 1, 2048, 8, 0x1000, None) == B.MOE_E_ARG   # misaligned y
+    st = B.moe_lru(256, 64, None, None, None, None)
+    assert L.moe_lru_reset(ctypes.byref(st), None) == B.MOE_E_ARG
+    st2 = B.moe_lru(256, 4096, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert L.moe_cache_lookup(ctypes.byref(st2), 0x1000, 1, 8, 0x1000, 0x1000, 0x1000, None) == B.MOE_E_ARG
+    assert B.moe_miss_record_words(1, 8, 64) == 5 + 16
+    assert B.moe_miss_record_words(16, 8, 64) == 5 + 128
+
+
+def test_cache_fill_refuses_capacity_record():
+    rec = np.array([B.MOE_E_CAPACITY, 3, 0, 0, 2, 0, 0, 0, 0], np.int32)
+    L = B.lib()
+    assert L.moe_cache_fill(rec.ctypes.data, 0x1000, 0x1000, 256, 256, None, None, None) == B.MOE_E_CAPACITY
+    rec_bad = np.array([0, 5, 0, 0, 2, 0, 0, 0, 0], np.int32)   # n_miss > n_max
+    assert L.moe_cache_fill(rec_bad.ctypes.data, 0x1000, 0x1000, 256, 256, None, None, None) == B.MOE_E_ARG
