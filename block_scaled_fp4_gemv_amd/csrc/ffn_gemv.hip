@@ -151,6 +151,7 @@ __global__ __launch_bounds__(WPB * 64) void k_gateup_gemv_topk(
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint16_t* __restrict__ hbuf) {
   using G = Gemv<FMT, C, RB>;
   __shared__ int s_expert;
+  __shared__ uint32_t s_list[32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = blockIdx.y, t = q / k, j = q % k;
   uint32_t xs[G::XS][G::XW];
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(WPB * 64) void k_gateup_gemv_topk(
     wave_load_logits<NV>(logits + (size_t)t * E, E, v);
     int idx;
     float w;
-    wave_topk_regs<NV>(v, E, k, flags, idx, w);
+    wave_topk_regs<NV>(v, E, k, flags, idx, w, s_list);
     if (lane == j) s_expert = idx;
     if (blockIdx.x == 0 && j == 0 && lane < k) {
       topk_idx[(size_t)t * k + lane] = idx;

@@ -19,7 +19,9 @@ struct FfnArgs {
   uint16_t* out;   // [T][H] or NULL
   uint16_t* hbuf;  // workspace [T*k][F] bf16
   float* ybuf;     // workspace [T*k][H] fp32 (grouped path with fused combine)
+  int32_t* tiles;  // workspace: grouped-path tile list (grouped_tiles_bytes)
 };
+size_t grouped_tiles_bytes(int T, int k, int E);
 
 // GEMV path: gate/up + SwiGLU into hbuf, then down (+ combine when out != NULL).
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s);

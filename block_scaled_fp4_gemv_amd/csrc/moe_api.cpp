@@ -49,7 +49,7 @@ int check_route_dims(int T, int H, int E, int k) {
   if (T < 0) return fail(MOE_E_ARG, "T=%d < 0", T);
   if (!valid_dim(H)) return fail(MOE_E_ARG, "H=%d unsupported", H);
   if (E < 1 || E > 1024) return fail(MOE_E_ARG, "E=%d outside [1, 1024]", E);
-  if (k < 1 || k > E || k > 64) return fail(MOE_E_ARG, "k=%d outside [1, min(E, 64)]", k);
+  if (k < 1 || k > E || k > 16) return fail(MOE_E_ARG, "k=%d outside [1, min(E, 16)]", k);
   return MOE_OK;
 }
 
@@ -228,7 +228,7 @@ int moe_cache_fill(const int32_t* rec, const void* host_pool, void* slot_pool, s
 size_t moe_ffn_workspace(int fmt, int T, int H, int F, int k, int E) {
   if (!valid_fmt(fmt) || T < 0 || k < 1 || E < 1 || !valid_dim(H) || !valid_dim(F)) return 0;
   const size_t n = (size_t)T * k;
-  return align256(n * F * 2) + align256(n * H * 4) + 256;
+  return align256(n * F * 2) + align256(n * H * 4) + grouped_tiles_bytes(T, k, E) + 256;
 }
 
 int moe_expert_ffn(int fmt, const void* slot_pool, size_t stride, int H, int F, int E,
@@ -240,7 +240,7 @@ int moe_expert_ffn(int fmt, const void* slot_pool, size_t stride, int H, int F, 
   int st = check_shape(fmt, H, F);
   if (st) return st;
   if (E < 1 || E > 1024) return fail(MOE_E_ARG, "E=%d outside [1, 1024]", E);
-  if (T < 0 || k < 1 || k > E || k > 64) return fail(MOE_E_ARG, "T=%d k=%d", T, k);
+  if (T < 0 || k < 1 || k > E || k > 16) return fail(MOE_E_ARG, "T=%d k=%d", T, k);
   if (flags > MOE_FFN_GROUPED) return fail(MOE_E_ARG, "unknown ffn flags 0x%x", flags);
   if (T == 0) return MOE_OK;
   if (!y && !out) return fail(MOE_E_ARG, "y and out are both NULL");
@@ -278,6 +278,7 @@ int moe_expert_ffn(int fmt, const void* slot_pool, size_t stride, int H, int F, 
   uint8_t* p = static_cast<uint8_t*>(ws);
   a.hbuf = reinterpret_cast<uint16_t*>(p);
   a.ybuf = reinterpret_cast<float*>(p + align256((size_t)T * k * F * 2));
+  a.tiles = reinterpret_cast<int32_t*>(p + align256((size_t)T * k * F * 2) + align256((size_t)T * k * H * 4));
   if (T == 0 || a.n_pairs == 0) return MOE_OK;
   hipError_t e = grouped ? launch_ffn_grouped(a, static_cast<hipStream_t>(stream))
                          : launch_ffn_gemv(a, static_cast<hipStream_t>(stream));
@@ -329,6 +330,7 @@ int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, in
   a.x = x; a.topk_idx = topk_idx; a.topk_w = topk_w; a.out = out; a.n_pairs = T * k;
   a.hbuf = reinterpret_cast<uint16_t*>(p);
   a.ybuf = reinterpret_cast<float*>(p + align256((size_t)T * k * F * 2));
+  a.tiles = reinterpret_cast<int32_t*>(p + align256((size_t)T * k * F * 2) + align256((size_t)T * k * H * 4));
   hipError_t e;
   if (T <= 4) {
     e = launch_router_logits(x, router, T, H, E, r.logits, s);

@@ -46,46 +46,102 @@ __device__ __forceinline__ void wave_argmax(float& z, int& e) {
   e = be;
 }
 
-// Lane l holds logits of experts l, l+64, ..., l+64*(NV-1) (E <= 64*NV, -inf
-// beyond E).  On return, lane r < k holds the rank-r expert and its weight.
+// Order-preserving map of an fp32 logit to uint32 (larger logit -> larger key;
+// -0 and +0 map to one key).  Key 0 is below every finite logit's key.
+__device__ __forceinline__ uint32_t logit_key(float z) {
+  const uint32_t u = __float_as_uint(z + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Lane l holds logits of experts l, l+64, ..., l+64*(NV-1) (E <= 64*NV; values
+// beyond E are ignored).  k <= 16.  `list` is 2*16 words of LDS private to this
+// wave.  On return lane r < k holds the rank-r expert and its weight.
+//
+// Selection is a radix select on the 32-bit keys: 32 ballot/popcount rounds
+// find the k-th largest key T; the experts above T plus the lowest-index ones
+// equal to T form the top-k set, which is compacted into `list` and ordered
+// by (logit desc, index asc) with k*k comparisons.
 template <int NV>
 __device__ __forceinline__ void wave_topk_regs(const float (&v)[NV], int E, int k, unsigned flags,
-                                               int& my_idx, float& my_w) {
+                                               int& my_idx, float& my_w, uint32_t* list) {
   const int lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  uint32_t key[NV];
   float zmax = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) zmax = fmaxf(zmax, v[i]);
+  for (int i = 0; i < NV; ++i) {
+    const bool ok = lane + 64 * i < E;
+    key[i] = ok ? logit_key(v[i]) : 0u;
+    if (ok) zmax = fmaxf(zmax, v[i]);
+  }
   zmax = wave_max(zmax);
   float se = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
-    if (lane + 64 * i < E) se += expf(v[i] - zmax);
+    if (lane + 64 * i < E) se += __expf(v[i] - zmax);
   se = wave_sum(se);
-  uint32_t taken = 0;
-  float selsum = 0.0f;
-  my_idx = 0;
-  my_w = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bz = -INFINITY;
-    int be = 0x7fffffff;
+  // k-th largest key
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = T | (1u << b);
+    int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && better(v[i], e, bz, be)) {
-        bz = v[i];
-        be = e;
-      }
+    for (int i = 0; i < NV; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+    if (cnt >= k) T = cand;
+  }
+  int n_gt = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) n_gt += __popcll(__ballot(key[i] > T));
+  const int need = k - n_gt;  // >= 1 ties at T, taken by ascending expert index
+  int ties_before = 0, sel_before = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint64_t tm = __ballot(key[i] == T && key[i] != 0u);
+    const int tie_rank = ties_before + __popcll(tm & lt_mask);
+    ties_before += __popcll(tm);
+    const bool sel = key[i] > T || (key[i] == T && key[i] != 0u && tie_rank < need);
+    const uint64_t sm = __ballot(sel);
+    if (sel) {
+      const int pos = sel_before + __popcll(sm & lt_mask);
+      list[pos] = __float_as_uint(v[i]);
+      list[16 + pos] = (uint32_t)(lane + 64 * i);
     }
-    wave_argmax(bz, be);
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    const float p = expf(bz - zmax) / se;
-    selsum += p;
-    if (lane == j) {
-      my_idx = be;
-      my_w = p;
+    sel_before += __popcll(sm);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  float z = -INFINITY;
+  int e = 0x7fffffff, rank = 0;
+  if (lane < k) {
+    z = __uint_as_float(list[lane]);
+    e = (int)list[16 + lane];
+    for (int s = 0; s < k; ++s) {
+      const float oz = __uint_as_float(list[s]);
+      const int oe = (int)list[16 + s];
+      rank += better(oz, oe, z, e) ? 1 : 0;
     }
   }
-  if (flags & MOE_ROUTE_RENORM) my_w /= selsum;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // scatter to rank order through the same scratch
+  const float p = lane < k ? __expf(z - zmax) / se : 0.0f;
+  if (lane < k) {
+    list[rank] = __float_as_uint(p);
+    list[16 + rank] = (uint32_t)e;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  my_idx = 0;
+  my_w = 0.0f;
+  if (lane < k) {
+    my_w = __uint_as_float(list[lane]);
+    my_idx = (int)list[16 + lane];
+  }
+  if (flags & MOE_ROUTE_RENORM) {
+    const float tot = wave_sum(lane < k ? my_w : 0.0f);
+    my_w /= tot;
+  }
+  __builtin_amdgcn_wave_barrier();
 }
 
 template <int NV>

@@ -42,8 +42,7 @@
  * byte, element 2i in the low nibble.
  *
  * Supported shapes: H and F in {256, 512, 1024, 2048, 4096, 6144, 8192};
- * 1 <= k <= min(E, 64), E <= 1024; T >= 0.  The GEMV path with the combine
- * fused (out != NULL) needs k <= 16.
+ * 1 <= k <= min(E, 16), E <= 1024; T >= 0.
  */
 #ifndef MOE_FP4_H
 #define MOE_FP4_H

@@ -114,7 +114,7 @@ def test_ffn_argument_errors_before_any_hip_call():
     assert call(flags=B.MOE_FFN_GROUPED) == B.MOE_E_ARG              # no permutation
     assert call(k=300) == B.MOE_E_ARG
     assert call(ws_bytes=8) == B.MOE_E_WORKSPACE
-    assert call(k=32, E=64, out=fake, w=fake, flags=B.MOE_FFN_GEMV) == B.MOE_E_ARG   # fused needs k<=16
+    assert call(k=32, E=64, out=fake, w=fake, flags=B.MOE_FFN_GEMV) == B.MOE_E_ARG   # k <= 16
 
 
 def test_combine_and_lru_argument_errors():

@@ -316,3 +316,52 @@ def test_layer_forward_renorm_and_tiny():
     _check_route(x, L.router, k, idx, w, renorm=True)
     ref = moe.moe_layer(fmt, x, L.router, L.experts, k, renorm=True)
     assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
+
+
+# ------------------------------------------------------- grouped (prefill) path
+
+def _grouped_case(fmt, H, E, F, k, T, cfg, w_std=0.02, sample=None):
+    L = Layer(fmt, H, E, F, cfg=cfg, layer=0, w_std=w_std)
+    x = iid_tokens(0, cfg, T, H, [L.router], k)
+    pool, R = L.device()
+    xd = _x_dev(x)
+    idx, w, perm, off = B.moe_route(xd, R, k)
+    y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.uint16, device="cuda")
+    B.moe_expert_ffn(fmt, pool, L.stride, H, F, E, xd, idx, pair_perm=perm, expert_off=off,
+                     topk_w=w, y=y, out=out, flags=B.MOE_FFN_GROUPED)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if sample is None else np.unique(np.linspace(0, T - 1, sample).astype(int))
+    ref = moe.moe_layer(fmt, x[rows], L.router, L.experts, k)
+    _check_route(x[rows], L.router, k, idx.cpu()[rows], w.cpu()[rows])
+    yg = y.cpu().numpy().reshape(T, k, H)[rows].reshape(-1, H)
+    assert_rows_close(yg, ref["y"].reshape(-1, H), what="y")
+    assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what="out")
+
+
+def test_grouped_tiny_mxfp4():
+    _grouped_case(MX, 256, 8, 512, 2, 16, cfg=0)
+
+
+@pytest.mark.parametrize("fmt,T", [(NV, 512), (MX, 256), (F8, 256)])
+def test_grouped_35b_shape(fmt, T):
+    _grouped_case(fmt, 2048, 256, 512, 8, T, cfg=41 + fmt)
+
+
+def test_grouped_ragged_tiles():
+    """Few tokens over few experts: tiles with 1..63 rows and empty experts."""
+    _grouped_case(NV, 512, 16, 1024, 4, 37, cfg=44)
+
+
+def test_layer_forward_prefill_2048_sampled():
+    """2048-token prefill through one 35B-shape NVFP4 layer (grouped path), 64 sampled tokens."""
+    fmt, H, E, F, k, T = NV, 2048, 256, 512, 8, 2048
+    L = Layer(fmt, H, E, F, cfg=2, layer=0, w_std=0.02)
+    x = iid_tokens(0, 2, T, H, [L.router], k)
+    pool, R = L.device()
+    idx, w, out = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, _x_dev(x), R)
+    torch.cuda.synchronize()
+    rows = np.unique(np.linspace(0, T - 1, 64).astype(int))
+    _check_route(x[rows], L.router, k, idx.cpu()[rows], w.cpu()[rows])
+    ref = moe.moe_layer(fmt, x[rows], L.router, L.experts, k)
+    assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what="out")
