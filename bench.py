@@ -37,11 +37,17 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode35b", choices=["decode35b", "decode753b"])
+    p.add_argument("--prefill", default="prefill35b", choices=["prefill35b", "prefill753b", "none"],
+                   help="prefill workload timed alongside the decode headline")
+    p.add_argument("--prefill-reps", type=int, default=20)
     p.add_argument("--fmt", type=int, default=0, help="override weight format (1 NVFP4, 2 MXFP4, 3 FP8)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (testing only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-steps", type=int, default=2)
+    p.add_argument("--cpu-sample-steps", type=int, default=6)
     p.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
+    p.add_argument("--calib-copy-mib", type=int, default=256,
+                   help="one device-to-device copy of this size before timing: a kernel of known "
+                        "traffic for scaling hardware byte counters (0 = skip)")
     return p.parse_args()
 
 
@@ -80,6 +86,82 @@ def algorithmic_bytes(wl, fmt):
     act_ffn = wl.H * 2 + wl.k * wl.F * 2 * 2 + wl.H * 2 + wl.k * 8
     return dict(expert=wl.k * eb, router=router, ffn_total=wl.k * eb + act_ffn,
                 route_total=router + act_route, layer_total=wl.k * eb + router + act_route + act_ffn)
+
+
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+
+
+def prefill_leg(name, fmt_override, reps, threads):
+    """Time moe_layer_forward over a T-token prefill of one layer (grouped MFMA path)."""
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_gemv_amd import binding as B
+    from block_scaled_fp4_gemv_amd import synth as sy
+
+    wl = sy.WORKLOADS[name]
+    fmt = fmt_override or wl.fmt
+    H, E, F, k, T = wl.H, wl.E, wl.F, wl.k, wl.T
+    sy.set_threads(threads)
+    stride = B.blob_stride(fmt, H, F)
+    host = np.empty(E * stride, np.uint8)
+    B.pack_layer(fmt, H, F, sy.experts(fmt, 0, wl.cfg_id, 0, 0, E, H, F, wl.w_std), host, stride)
+    pool = torch.from_numpy(host).cuda()
+    del host
+    R = torch.from_numpy(sy.router(0, wl.cfg_id, 0, E, H)).cuda()
+    x = torch.from_numpy(sy.token_rows(0, wl.cfg_id, T, H)).cuda()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.uint16, device="cuda")
+    ws = B.new_layer_workspace(fmt, T, H, F, k, E)
+    run = lambda: B.moe_layer_forward(fmt, pool, stride, H, F, E, k, x, R, topk_idx=idx, topk_w=w,  # noqa: E731
+                                      out=out, ws=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1000
+    used = int(torch.unique(idx).numel())
+    eb = B.moe_expert_bytes(fmt, H, F) - 256 + (12 if fmt == 1 else 0)
+    bytes_alg = used * eb + E * H * 4 + T * H * 2 * 2 + T * k * 8
+    flops_mfma = 2.0 * T * k * (2 * F * H + H * F)
+    flops_router = 2.0 * T * E * H
+    t = us * 1e-6
+    hbm_frac = bytes_alg / t / (HBM_PEAK_GBPS * 1e9)
+    mf = flops_mfma / t / 1e12
+    fmt_name = {1: "nvfp4", 2: "mxfp4", 3: "fp8"}[fmt]
+    return {"workload": f"{name}: {T} tokens through one layer, hidden {H}, {E} experts, top-{k}, "
+                        f"width {F}, {fmt_name}",
+            "tokens_per_s": round(T / t, 1), "layer_us": round(us, 2), "experts_used": used,
+            "algorithmic_bytes": bytes_alg, "hbm_GBps": round(bytes_alg / t / 1e9, 1),
+            "hbm_frac": round(hbm_frac, 4), "expert_mfma_tflops": round(mf, 2),
+            "mfma_instruction": "v_mfma_f32_32x32x16_bf16 (weights dequantized in registers)",
+            "mfma_util_vs_bf16_peak": round(mf / MFMA_PEAK_TFLOPS["bf16"], 4),
+            "mfma_util_vs_fp4_peak": round(mf / MFMA_PEAK_TFLOPS["fp4"], 4),
+            "roofline_frac": round(max(hbm_frac, flops_mfma / (MFMA_PEAK_TFLOPS["bf16"] * 1e12) / t), 4),
+            "router_fp32_gflop": round(flops_router / 1e9, 2)}
+
+
+def measured_traffic(n_layers_run, n_layers_default):
+    """HBM bytes per decode layer from the committed FETCH_SIZE/WRITE_SIZE runs, if the
+    kernel sources are unchanged since they were taken (else None)."""
+    import glob
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode35b_traffic.json")
+    if not os.path.exists(path) or n_layers_run != n_layers_default:
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "block_scaled_fp4_gemv_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    if h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return int(rec["decode_layer_read_bytes"] + rec["decode_layer_write_bytes"])
 
 
 def cpu_baseline(wl, fmt, xs, n_steps, n_layers):
@@ -161,6 +243,15 @@ def main():
         for l in range(n_layers):
             layer(l)
 
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # eager warm-up, then capture one step in a HIP graph
     x.copy_(xs_dev[0:1])
     for _ in range(3):
@@ -188,20 +279,9 @@ def main():
     tok_s = 1000.0 / ms_step
     log(f"timed {args.steps} steps: {ms_step * 1000:.1f} us/step, {tok_s:.1f} tok/s")
 
-    # per-layer call durations with HIP events on the stream the kernels run on
-    stream = torch.cuda.current_stream()
-    n_rep = max(1, min(args.steps, 50))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_rep * n_layers)]
-    for r in range(n_rep):
-        j = r % n_states
-        x.copy_(xs_dev[j:j + 1])
-        for l in range(n_layers):
-            e = evs[r * n_layers + l]
-            e[0].record(stream)
-            layer(l)
-            e[1].record(stream)
-    torch.cuda.synchronize()
-    layer_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1000
+    # one layer launch = the layer's kernels inside the timed graph replays: its
+    # mean duration is the timed region (HIP events) divided by steps x layers
+    layer_us = ms_step * 1000.0 / n_layers
 
     nb = algorithmic_bytes(wl, fmt)
     layer_gbps = nb["layer_total"] / (layer_us * 1e-6) / 1e9
@@ -233,9 +313,18 @@ def main():
         "roofline": {"kernel": "moe_layer_forward decode layer (router GEMV, gate/up+SwiGLU with "
                                "in-block top-k, down+combine: 3 kernels)",
                      "bound": "hbm", "achieved": round(layer_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(layer_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "bytes_per_launch": nb["layer_total"], "avg_launch_us": round(layer_us, 3)},
+                     "unit": "GB/s", "frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": (measured_traffic(n_layers, wl.layers)
+                                 if wl.name == "decode35b" and fmt == 1 else None),
+                     "bytes_per_launch": nb["layer_total"], "avg_launch_us": round(layer_us, 3),
+                     "launch_timing": "timed graph replays / (steps x layers), HIP events"},
     }
+    if args.prefill != "none":
+        log(f"prefill leg {args.prefill} ...")
+        del pools
+        torch.cuda.empty_cache()
+        res["prefill"] = prefill_leg(args.prefill, 0, args.prefill_reps, args.threads)
+        log(f"prefill: {res['prefill']['layer_us']} us/layer, {res['prefill']['tokens_per_s']} tok/s")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(wl, fmt, xs, args.cpu_sample_steps, n_layers)

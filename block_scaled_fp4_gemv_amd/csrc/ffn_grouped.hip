@@ -177,18 +177,27 @@ __global__ __launch_bounds__(256) void k_grouped(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[m][s][v] = 0.0f;
 
-  for (int kb = 0; kb < K; kb += BK) {
-    WFrag<FMT> wf[NMAT];
+  // software pipeline: the next step's weights and activations are loaded into
+  // registers while the current step runs its MFMAs
+  WFrag<FMT> wf[NMAT];
+  uint4 av[4];
+  auto gload = [&](int kb) {
     wf[0].load(codes0, scales0, K, n_lane, h, kb);
     if constexpr (NMAT == 2) wf[1].load(blob + L.cu, blob + L.su, K, n_lane, h, kb);
-    uint4 av[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       av[j] = arow ? reinterpret_cast<const uint4*>(arow + kb + ac)[j] : make_uint4(0, 0, 0, 0);
+  };
+  gload(0);
+  for (int kb = 0; kb < K; kb += BK) {
     __syncthreads();  // previous step's LDS reads are done
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(As + ar * LDA + ac + 8 * j) = av[j];
     __syncthreads();
+    WFrag<FMT> cur[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) cur[m] = wf[m];
+    if (kb + BK < K) gload(kb + BK);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
       floatx16_t part[2];
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(256) void k_grouped(
         for (int v = 0; v < 16; ++v) part[s][v] = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const bf16x8_t b = wf[m].operand(i);
+        const bf16x8_t b = cur[m].operand(i);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const bf16x8_t a = a_operand(As, 32 * s + (lane & 31), h, i);
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(256) void k_grouped(
         }
       }
       if (fp8) {
-        const float sg = wf[m].step_scale();
+        const float sg = cur[m].step_scale();
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll

@@ -66,67 +66,85 @@ hipError_t router_logits_nt(const uint16_t* x, const float* R, int H, int E, flo
 }
 
 // ---------------------------------------------------------- large-T router GEMM
-// logits[T][E] = x[T][H] . R[E][H]^T in fp32; 64x64 tile per block, 4x4 per thread,
-// K staged through LDS 32 at a time; each output is one sequential fp32 FMA chain.
-constexpr int RBM = 64, RBN = 64, RBK = 32;
+// logits[T][E] = x[T][H] . R[E][H]^T on bf16 MFMA with fp32 accuracy: every fp32
+// router weight splits exactly into three bf16 terms (hi + mid + lo covers the
+// 24-bit significand), x is already bf16, so each product is exact in fp32 and
+// the three MFMA chains accumulate in fp32.  64x64 tile per workgroup (4 waves
+// of 32x32), K staged through LDS 64 at a time with the next step's global
+// loads issued before the current step's MFMAs.
+typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rfloatx16_t __attribute__((ext_vector_type(16)));
+constexpr int RBM = 64, RBN = 64, RBK = 64, RLD = RBK + 8;
+
+__device__ __forceinline__ void split3(float r, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = f32_to_bf16_rne(r);
+  const float r1 = r - bf16_to_f32(hi);
+  mid = f32_to_bf16_rne(r1);
+  const float r2 = r1 - bf16_to_f32(mid);
+  lo = f32_to_bf16_rne(r2);
+}
 
 __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict__ x,
                                                      const float* __restrict__ R, int T, int H, int E,
                                                      float* __restrict__ logits) {
-  __shared__ float xs[RBK][RBM + 4];
-  __shared__ float rs[RBK][RBN + 4];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[RBM * RLD];
+  __shared__ __attribute__((aligned(16))) uint16_t rs[3][RBN * RLD];
   const int tm = blockIdx.y * RBM, tn = blockIdx.x * RBN;
-  const int tid = threadIdx.x;
-  const int ty = tid / 16, tx = tid % 16;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < H; k0 += RBK) {
-    // x tile: 64 rows x 32 k bf16 -> 8 elements per thread
-    {
-      const int r = tid / 4, c = (tid % 4) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (tm + r < T) v = *reinterpret_cast<const uint4*>(x + (size_t)(tm + r) * H + k0 + c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
+  // staging: thread -> row tid/4, 16 columns at (tid%4)*16
+  const int sr = tid >> 2, sc = (tid & 3) * 16;
+  const bool xrow_ok = tm + sr < T, rrow_ok = tn + sr < E;
+  const uint16_t* xp = x + (size_t)(xrow_ok ? tm + sr : 0) * H + sc;
+  const float* rp = R + (size_t)(rrow_ok ? tn + sr : 0) * H + sc;
+  uint4 xa[2];
+  float4 ra[4];
+  auto gload = [&](int kb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xs[c + 2 * i][r] = bf16_to_f32(w[i] & 0xffff);
-        xs[c + 2 * i + 1][r] = bf16_to_f32(w[i] >> 16);
-      }
-    }
-    // R tile: 64 rows x 32 k fp32 -> 8 per thread
-    {
-      const int r = tid / 4, c = (tid % 4) * 8;
-      float4 a = make_float4(0, 0, 0, 0), b = a;
-      if (tn + r < E) {
-        const float4* p = reinterpret_cast<const float4*>(R + (size_t)(tn + r) * H + k0 + c);
-        a = p[0];
-        b = p[1];
-      }
-      rs[c + 0][r] = a.x; rs[c + 1][r] = a.y; rs[c + 2][r] = a.z; rs[c + 3][r] = a.w;
-      rs[c + 4][r] = b.x; rs[c + 5][r] = b.y; rs[c + 6][r] = b.z; rs[c + 7][r] = b.w;
-    }
+    for (int j = 0; j < 2; ++j) xa[j] = xrow_ok ? reinterpret_cast<const uint4*>(xp + kb)[j] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ra[j] = rrow_ok ? reinterpret_cast<const float4*>(rp + kb)[j] : make_float4(0, 0, 0, 0);
+  };
+  rfloatx16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  gload(0);
+  for (int kb = 0; kb < H; kb += RBK) {
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < RBK; ++kk) {
-      float xa[4], rb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xa[i] = xs[kk][ty * 4 + i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rb[i] = rs[kk][tx * 4 + i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], rb[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = tm + ty * 4 + i;
-    if (t >= T) continue;
+    for (int j = 0; j < 2; ++j) *reinterpret_cast<uint4*>(xs + sr * RLD + sc + 8 * j) = xa[j];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = tn + tx * 4 + j;
-      if (e < E) logits[(size_t)t * E + e] = acc[i][j];
+      const float f[4] = {ra[j].x, ra[j].y, ra[j].z, ra[j].w};
+      uint16_t hh[4], mm[4], ll[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split3(f[q], hh[q], mm[q], ll[q]);
+      uint2 vh, vm, vl;
+      vh.x = hh[0] | ((uint32_t)hh[1] << 16); vh.y = hh[2] | ((uint32_t)hh[3] << 16);
+      vm.x = mm[0] | ((uint32_t)mm[1] << 16); vm.y = mm[2] | ((uint32_t)mm[3] << 16);
+      vl.x = ll[0] | ((uint32_t)ll[1] << 16); vl.y = ll[2] | ((uint32_t)ll[3] << 16);
+      *reinterpret_cast<uint2*>(rs[0] + sr * RLD + sc + 4 * j) = vh;
+      *reinterpret_cast<uint2*>(rs[1] + sr * RLD + sc + 4 * j) = vm;
+      *reinterpret_cast<uint2*>(rs[2] + sr * RLD + sc + 4 * j) = vl;
+    }
+    __syncthreads();
+    if (kb + RBK < H) gload(kb + RBK);
+#pragma unroll
+    for (int i = 0; i < RBK / 16; ++i) {
+      const rbf16x8_t a = *reinterpret_cast<const rbf16x8_t*>(xs + (32 * wm + (lane & 31)) * RLD + 16 * i + 8 * h);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const rbf16x8_t b = *reinterpret_cast<const rbf16x8_t*>(rs[p] + (32 * wn + (lane & 31)) * RLD + 16 * i + 8 * h);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      }
+    }
+  }
+  const int e = tn + 32 * wn + (lane & 31);
+  if (e < E) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int t = tm + 32 * wm + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (t < T) logits[(size_t)t * E + e] = acc[v];
     }
   }
 }
@@ -180,8 +198,10 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int nchunk, int E, int32_t* 
   __shared__ int wsum[16];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   int s = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 16
     for (int c = 0; c < nchunk; ++c) s += chunk_cnt[(size_t)c * E + e];
+  }
   // exclusive scan of the per-expert totals over the block
   int incl = s;
 #pragma unroll
@@ -198,6 +218,7 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int nchunk, int E, int32_t* 
     expert_off[e] = excl;
     tot[e] = excl;
     int run = excl;
+#pragma unroll 16
     for (int c = 0; c < nchunk; ++c) {
       const size_t i = (size_t)c * E + e;
       const int v = chunk_cnt[i];

@@ -8,7 +8,7 @@ E8M0: unsigned exponent, value 2^(v-127); v=255 is NaN ([OCP-MX]).
 
 Block-scaled weight tensors (the formats named in [39TOK] section "局限"), for a
 matrix W of shape [N, K] whose blocks run along K (the reduction dimension) of
-each output row (reading R5):
+each output row (a stated reading; 16/32/128 divide every K used):
     NVFP4 : W[n,i] = e2m1(c[n,i]) * e4m3(s[n, i//16]) * tau           ([NVFP4])
     MXFP4 : W[n,i] = e2m1(c[n,i]) * 2^(s[n, i//32] - 127)            ([OCP-MX])
     FP8   : W[n,i] = e4m3(c[n,i]) * sigma[n, i//128]   (sigma fp32 per 128)
@@ -82,7 +82,7 @@ def _expand_blocks(scale_vals: np.ndarray, block: int) -> np.ndarray:
 
 
 def dequant_nvfp4(codes, scales, tau) -> np.ndarray:
-    """NVFP4 matrix -> float64 [N, K] ([NVFP4]; reading R6: tau is a multiplier)."""
+    """NVFP4 matrix -> float64 [N, K] ([NVFP4]; tau is read as a dequant multiplier)."""
     v = E2M1_TABLE[unpack_fp4(codes)]
     s = E4M3_TABLE[np.asarray(scales, dtype=np.uint8)]
     return v * _expand_blocks(s, 16) * float(np.float32(tau))

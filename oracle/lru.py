@@ -4,7 +4,7 @@
 routing overlap of adjacent tokens; what misses is filled into the GPU cache.
 [753B] section "按带宽动态分配参数存储": frequently used experts stay resident,
 the rest are fetched on demand.  The pages give no further policy detail; the
-batch-aware rule below is the stated reading (R11, R16):
+batch-aware rule below is a stated reading (one pool per layer, cold start):
 
 * One pool of S slots per layer over E experts; it starts cold (all empty).
 * A step presents T*k accesses in pair order q = t*k + j.

@@ -4,21 +4,25 @@ Gate ([753B] section "混合专家架构（MoE）的天然稀疏性"): a linear 
 softmax giving each expert's selection probability; the top-K experts are
 evaluated and their outputs combined by a weighted sum.  Each expert is an
 independent FFN.  Weights are dequantized at compute time ([8GB] §2.1); the
-activations stay in bf16/fp64 (reading R9: weight-only quantization).
+activations stay in bf16/fp64 (a stated reading: quantization is weight-only).
 
 Per token t (x_t a bf16 row of width H; R the fp32 router [E, H]):
   1. z_t[e]  = fp32( sum_h x_t[h] * R[e,h] )           summed in fp64, rounded once
-  2. p_t     = softmax(z_t) over all E experts          fp64 (reading R1)
-  3. S_t     = first k experts by (z desc, index asc)   (readings R3, R4)
-  4. w_tj    = fp32(p_t[S_tj]); with renorm, fp32(p_t[S_tj] / sum_j p_t[S_tj]) (R2)
+  2. p_t     = softmax(z_t) over all E experts          fp64 (softmax, then selection)
+  3. S_t     = first k experts by (z desc, index asc)   (select on fp32 logits; ties
+                                                          go to the lower index)
+  4. w_tj    = fp32(p_t[S_tj]); with renorm, fp32(p_t[S_tj] / sum_j p_t[S_tj])
+                                      (no renormalisation unless asked for)
   5. for each pair (t, j), e = S_tj, with G, U [F, H] and D [H, F] dequantized:
          g = G x_t,  u = U x_t                           fp64
-         h = bf16( g / (1 + exp(-g)) * u )                one rounding (R10, R12)
+         h = bf16( g / (1 + exp(-g)) * u )                one rounding; gate is the
+                                                          first matrix, no bias/clamp
          y_tj = D h                                        fp64
   6. out_t = bf16( sum_{j=0..k-1} w_tj * y_tj )           fp64 sum in j order
 
 Stacked layers are not chained: every layer of a step receives the same input
-(reading R15).
+(a stated reading; chaining without norm or residual would shrink the
+activations and carry rounding differences into later routing decisions).
 """
 
 import numpy as np
