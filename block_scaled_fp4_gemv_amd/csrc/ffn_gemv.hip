@@ -105,6 +105,15 @@ struct Gemv {
   }
 };
 
+// Rows per wave for a matrix of C chunks per row: about four 16-byte slots per lane.
+constexpr int rows_per_wave(int C) { return C >= 256 ? 1 : 256 / C; }
+// Down + combine: at most 8 rows per workgroup so that a 2048-row layer spreads
+// over >= 256 workgroups (one wave per routed pair in each).
+constexpr int rows_per_wave_down(int C) {
+  return (64 / C > (rows_per_wave(C) < 8 ? rows_per_wave(C) : 8)) ? 64 / C
+                                                                    : (rows_per_wave(C) < 8 ? rows_per_wave(C) : 8);
+}
+
 template <int FMT, int C, int RB, int WPB>
 __global__ __launch_bounds__(WPB * 64) void k_gateup_gemv(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F,
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(WPB * 64) void k_gateup_gemv_topk(
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint16_t* __restrict__ hbuf) {
   using G = Gemv<FMT, C, RB>;
   __shared__ int s_expert;
-  __shared__ uint32_t s_list[32];
+  __shared__ TopkScratch s_topk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = blockIdx.y, t = q / k, j = q % k;
   uint32_t xs[G::XS][G::XW];
@@ -161,7 +170,7 @@ __global__ __launch_bounds__(WPB * 64) void k_gateup_gemv_topk(
     wave_load_logits<NV>(logits + (size_t)t * E, E, v);
     int idx;
     float w;
-    wave_topk_regs<NV>(v, E, k, flags, idx, w, s_list);
+    wave_topk_regs<NV>(v, E, k, flags, idx, w, s_topk);
     if (lane == j) s_expert = idx;
     if (blockIdx.x == 0 && j == 0 && lane < k) {
       topk_idx[(size_t)t * k + lane] = idx;
@@ -258,14 +267,7 @@ __global__ __launch_bounds__(1024) void k_down_combine_gemv(
   }
 }
 
-// Rows per wave for a matrix of C chunks per row: about four 16-byte slots per lane.
-constexpr int rows_per_wave(int C) { return C >= 256 ? 1 : 256 / C; }
-// Down + combine: at most 8 rows per workgroup so that a 2048-row layer spreads
-// over >= 256 workgroups (one wave per routed pair in each).
-constexpr int rows_per_wave_down(int C) {
-  return (64 / C > (rows_per_wave(C) < 8 ? rows_per_wave(C) : 8)) ? 64 / C
-                                                                    : (rows_per_wave(C) < 8 ? rows_per_wave(C) : 8);
-}
+
 
 template <int FMT, int C>
 hipError_t launch_gateup_c(const FfnArgs& a, hipStream_t s) {

@@ -153,14 +153,14 @@ template <int NV>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               unsigned flags, int32_t* __restrict__ topk_idx,
                                               float* __restrict__ topk_w) {
-  __shared__ uint32_t lists[4][32];
+  __shared__ TopkScratch scr[4];
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (t >= T) return;
   float v[NV];
   wave_load_logits<NV>(logits + (size_t)t * E, E, v);
   int idx;
   float w;
-  wave_topk_regs<NV>(v, E, k, flags, idx, w, lists[threadIdx.x >> 6]);
+  wave_topk_regs<NV>(v, E, k, flags, idx, w, scr[threadIdx.x >> 6]);
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = idx;
     topk_w[(size_t)t * k + lane] = w;

@@ -62,8 +62,8 @@ __device__ __forceinline__ uint32_t logit_key(float z) {
 // equal to T form the top-k set, which is compacted into `list` and ordered
 // by (logit desc, index asc) with k*k comparisons.
 template <int NV>
-__device__ __forceinline__ void wave_topk_regs(const float (&v)[NV], int E, int k, unsigned flags,
-                                               int& my_idx, float& my_w, uint32_t* list) {
+__device__ __forceinline__ void wave_topk_radix(const float (&v)[NV], int E, int k, unsigned flags,
+                                                int& my_idx, float& my_w, uint32_t* list) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   uint32_t key[NV];
@@ -136,6 +136,115 @@ __device__ __forceinline__ void wave_topk_regs(const float (&v)[NV], int E, int 
   if (lane < k) {
     my_w = __uint_as_float(list[lane]);
     my_idx = (int)list[16 + lane];
+  }
+  if (flags & MOE_ROUTE_RENORM) {
+    const float tot = wave_sum(lane < k ? my_w : 0.0f);
+    my_w /= tot;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Scratch (LDS, private to one wave) for wave_topk_regs.
+struct TopkScratch {
+  uint32_t hist[256];
+  uint32_t cz[64];   // candidate logits (fp32 bits)
+  uint32_t ce[64];   // candidate experts
+  uint32_t list[32]; // radix fallback scratch
+};
+
+// Lane l holds logits of experts l, l+64, ..., l+64*(NV-1) (E <= 64*NV; values
+// beyond E are ignored), k <= 16.  On return lane r < k holds the rank-r expert
+// (logit desc, index asc) and its softmax weight over all E experts.
+//
+// Selection: each logit falls in bin floor((zmax - z) * 16) (clamped to 255); a
+// 256-bin LDS histogram and one wave scan give the bin B holding the k-th
+// largest logit; the experts in bins <= B (at least k, usually a few more) are
+// ranked exactly against each other.  More than 64 candidates (many equal
+// logits) fall back to an exact radix select over all keys.
+template <int NV>
+__device__ __forceinline__ void wave_topk_regs(const float (&v)[NV], int E, int k, unsigned flags,
+                                               int& my_idx, float& my_w, TopkScratch& sc) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  float zmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (lane + 64 * i < E) zmax = fmaxf(zmax, v[i]);
+  zmax = wave_max(zmax);
+  float se = 0.0f;
+  int bin[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const bool ok = lane + 64 * i < E;
+    se += ok ? __expf(v[i] - zmax) : 0.0f;
+    const float d = (zmax - v[i]) * 16.0f;
+    bin[i] = ok ? (d < 255.0f ? (int)d : 255) : 256;
+  }
+  const float inv_se = 1.0f / wave_sum(se);
+  *reinterpret_cast<uint4*>(&sc.hist[lane * 4]) = make_uint4(0u, 0u, 0u, 0u);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (bin[i] < 256) atomicAdd(&sc.hist[bin[i]], 1u);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // lane l owns bins 4l .. 4l+3; exclusive prefix of the lane totals from bit-plane ballots
+  const uint4 hq = *reinterpret_cast<const uint4*>(&sc.hist[lane * 4]);
+  const int c0 = hq.x, c1 = c0 + hq.y, c2 = c1 + hq.z, c3 = c2 + hq.w;
+  int before = 0;
+#pragma unroll
+  for (int bit = 0; bit < 9; ++bit) before += __popcll(__ballot((c3 >> bit) & 1) & lt_mask) << bit;
+  const uint64_t reach = __ballot(before + c3 >= k);
+  const int ln = __builtin_ctzll(reach);
+  const int b0 = __builtin_amdgcn_readlane(before, ln), b1 = __builtin_amdgcn_readlane(c0, ln),
+            b2 = __builtin_amdgcn_readlane(c1, ln), b3 = __builtin_amdgcn_readlane(c2, ln),
+            b4 = __builtin_amdgcn_readlane(c3, ln);
+  // cumulative counts through bins 4ln .. 4ln+3 are b0+b1 .. b0+b4
+  const int jb = b0 + b1 >= k ? 0 : b0 + b2 >= k ? 1 : b0 + b3 >= k ? 2 : 3;
+  const int B = 4 * ln + jb;
+  const int m = b0 + (jb == 0 ? b1 : jb == 1 ? b2 : jb == 2 ? b3 : b4);  // experts in bins <= B
+  if (m > 64) {  // degenerate: many logits in one bin
+    wave_topk_radix<NV>(v, E, k, flags, my_idx, my_w, sc.list);
+    return;
+  }
+  // compact the candidates (bins <= B) into lanes 0 .. m-1 through LDS
+  int pos_base = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const bool c = bin[i] <= B;
+    const uint64_t cm = __ballot(c);
+    if (c) {
+      const int pos = pos_base + __popcll(cm & lt_mask);
+      sc.cz[pos] = __float_as_uint(v[i]);
+      sc.ce[pos] = (uint32_t)(lane + 64 * i);
+    }
+    pos_base += __popcll(cm);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  float z = -INFINITY;
+  int e = 0x7fffffff;
+  if (lane < m) {
+    z = __uint_as_float(sc.cz[lane]);
+    e = (int)sc.ce[lane];
+  }
+  int rank = 0;
+  for (int s2 = 0; s2 < m; ++s2)
+    rank += better(readlane_f32(z, s2), __builtin_amdgcn_readlane(e, s2), z, e) ? 1 : 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  if (lane < m && rank < k) {
+    sc.cz[rank] = __float_as_uint(__expf(z - zmax) * inv_se);
+    sc.ce[rank] = (uint32_t)e;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  my_idx = 0;
+  my_w = 0.0f;
+  if (lane < k) {
+    my_w = __uint_as_float(sc.cz[lane]);
+    my_idx = (int)sc.ce[lane];
   }
   if (flags & MOE_ROUTE_RENORM) {
     const float tot = wave_sum(lane < k ? my_w : 0.0f);

@@ -229,7 +229,8 @@ int moe_combine(const float* y, const float* topk_w, int T, int H, int k, uint16
 
 /* -------------------------------------------------------- whole layer */
 
-/* Workspace bytes for moe_layer_forward. */
+/* Workspace bytes for moe_layer_forward (device memory, 256-byte aligned, no
+ * initialisation needed; one stream at a time). */
 size_t moe_layer_workspace(int fmt, int T, int H, int F, int k, int E);
 
 /* The whole layer for experts resident in `pool` (blob e at e*stride):
