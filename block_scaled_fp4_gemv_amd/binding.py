@@ -35,7 +35,7 @@ SIGNATURES = {
     "moe_expert_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_pack_expert": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_vp), _vp]),
     "moe_unpack_expert": (_i32, [_i32, _i32, _i32, _vp, ctypes.POINTER(_vp)]),
-    "moe_route_workspace": (_sz, [_i32, _i32, _i32]),
+    "moe_route_workspace": (_sz, [_i32, _i32, _i32, _i32]),
     "moe_route": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_lru_reset": (_i32, [ctypes.POINTER(moe_lru), _vp]),
     "moe_miss_record_words": (_sz, [_i32, _i32, _i32]),
@@ -162,13 +162,13 @@ def pack_layer(fmt, H, F, batch, dst, stride):
 
 # ---------------------------------------------------------------- routing
 
-def moe_route_workspace(T, E, k):
-    return int(lib().moe_route_workspace(T, E, k))
+def moe_route_workspace(T, H, E, k):
+    return int(lib().moe_route_workspace(T, H, E, k))
 
 
-def new_route_workspace(T, E, k, device="cuda"):
+def new_route_workspace(T, H, E, k, device="cuda"):
     import torch
-    return torch.zeros(moe_route_workspace(T, E, k) + 256, dtype=torch.uint8, device=device)
+    return torch.empty(moe_route_workspace(T, H, E, k) + 256, dtype=torch.uint8, device=device)
 
 
 def moe_route(x, router, k, flags=0, topk_idx=None, topk_w=None, pair_perm=None, expert_off=None,
@@ -185,7 +185,7 @@ def moe_route(x, router, k, flags=0, topk_idx=None, topk_w=None, pair_perm=None,
         pair_perm = torch.empty(T * k, dtype=torch.int32, device=dev)
         expert_off = torch.empty(E + 1, dtype=torch.int32, device=dev)
     if ws is None:
-        ws = new_route_workspace(T, E, k, dev)
+        ws = new_route_workspace(T, H, E, k, dev)
     st = lib().moe_route(_ptr(x), _ptr(router), T, H, E, k, flags, _ptr(topk_idx), _ptr(topk_w),
                          _ptr(pair_perm), _ptr(expert_off), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_route")

@@ -150,7 +150,11 @@ __global__ __launch_bounds__(256) void k_grouped(
     const int32_t* __restrict__ tile_m0, const int32_t* __restrict__ n_tiles, int n_col_tiles,
     uint16_t* __restrict__ hout, float* __restrict__ yout) {
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
-  const int tile = blockIdx.x / n_col_tiles, ct = blockIdx.x % n_col_tiles;
+  // Workgroups are handed to the 8 XCDs round-robin by index; within each run of
+  // 8 * n_col_tiles indices, the column tiles of one row tile share an XCD (and
+  // its L2 copy of the gathered activation rows).
+  const int grp = blockIdx.x / (8 * n_col_tiles), r8 = blockIdx.x % (8 * n_col_tiles);
+  const int tile = grp * 8 + (r8 & 7), ct = r8 >> 3;
   if (tile >= *n_tiles) return;
   const int e = tile_e[tile], m0 = tile_m0[tile];
   const int row_base = expert_off[e] + m0;
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(256) void k_grouped(
 template <int FMT>
 hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
   const int n_pairs = a.T * a.k;
-  const int max_tiles = (n_pairs + BM - 1) / BM + a.E;
+  const int max_tiles = ((n_pairs + BM - 1) / BM + a.E + 7) / 8 * 8;
   int32_t *tile_e = tiles, *tile_m0 = tiles + max_tiles, *n_tiles = tiles + 2 * max_tiles;
   hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E, tile_e, tile_m0,
                      n_tiles);
@@ -281,7 +285,7 @@ hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
 }  // namespace
 
 size_t grouped_tiles_bytes(int T, int k, int E) {
-  const int max_tiles = (T * k + BM - 1) / BM + E;
+  const int max_tiles = ((T * k + BM - 1) / BM + E + 7) / 8 * 8;
   return align256((size_t)(2 * max_tiles + 1) * 4);
 }
 

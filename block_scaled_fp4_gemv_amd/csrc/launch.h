@@ -44,13 +44,17 @@ struct RouteArgs {
   // workspace carve-up
   float* logits;       // [T][E]
   int32_t* chunk_cnt;  // [n_chunks][E]
+  uint16_t* planes;    // [3][E][H] bf16 split of the router (T > 4)
 };
-size_t route_ws_bytes(int T, int E, int k);
+size_t route_ws_bytes(int T, int H, int E, int k);
 void route_ws_carve(RouteArgs& a, void* ws);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
-// Router logits only ([T][E] fp32): GEMV kernel for T <= 4, tiled GEMM otherwise.
+// Router logits ([T][E] fp32): GEMV kernel for T <= 4 (launch_router_logits),
+// bf16x3 MFMA GEMM otherwise (launch_router_gemm, planes = [3][E][H] bf16 scratch).
 hipError_t launch_router_logits(const uint16_t* x, const float* R, int T, int H, int E, float* logits,
                                 hipStream_t s);
+hipError_t launch_router_gemm(const uint16_t* x, const float* R, int T, int H, int E, float* logits,
+                              uint16_t* planes, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, unsigned flags, int32_t* idx,
                        float* w, hipStream_t s);
 

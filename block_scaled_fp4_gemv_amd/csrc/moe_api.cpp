@@ -130,9 +130,9 @@ int moe_unpack_expert(int fmt, int H, int F, const void* blob, void* const canon
 
 // ---------------------------------------------------------------- routing
 
-size_t moe_route_workspace(int T, int E, int k) {
-  if (T < 0 || E < 1 || k < 1) return 0;
-  return route_ws_bytes(T, E, k);
+size_t moe_route_workspace(int T, int H, int E, int k) {
+  if (T < 0 || E < 1 || k < 1 || !valid_dim(H)) return 0;
+  return route_ws_bytes(T, H, E, k);
 }
 
 int moe_route(const uint16_t* x, const float* router, int T, int H, int E, int k, unsigned flags,
@@ -147,8 +147,8 @@ int moe_route(const uint16_t* x, const float* router, int T, int H, int E, int k
   if (T > 0 && (!x || !router || !topk_idx || !topk_w))
     return fail(MOE_E_ARG, "NULL x/router/topk_idx/topk_w");
   if (!aligned(x, 16) || !aligned(router, 16)) return fail(MOE_E_ARG, "x and router must be 16-byte aligned");
-  if (!ws || !aligned(ws, 256) || ws_bytes < route_ws_bytes(T, E, k))
-    return fail(MOE_E_WORKSPACE, "route workspace needs %zu bytes, 256-aligned", route_ws_bytes(T, E, k));
+  if (!ws || !aligned(ws, 256) || ws_bytes < route_ws_bytes(T, H, E, k))
+    return fail(MOE_E_WORKSPACE, "route workspace needs %zu bytes, 256-aligned", route_ws_bytes(T, H, E, k));
   RouteArgs a{};
   a.x = x; a.router = router; a.T = T; a.H = H; a.E = E; a.k = k; a.flags = flags;
   a.topk_idx = topk_idx; a.topk_w = topk_w; a.pair_perm = pair_perm; a.expert_off = expert_off;
@@ -289,7 +289,7 @@ size_t moe_layer_workspace(int fmt, int T, int H, int F, int k, int E) {
   const size_t ffn = moe_ffn_workspace(fmt, T, H, F, k, E);
   if (!ffn || E > 1024) return 0;
   const size_t n = (size_t)T * k;
-  return align256(route_ws_bytes(T, E, k)) + align256(n * 4) + align256((size_t)(E + 1) * 4) + ffn;
+  return align256(route_ws_bytes(T, H, E, k)) + align256(n * 4) + align256((size_t)(E + 1) * 4) + ffn;
 }
 
 int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, int E, int k,
@@ -319,7 +319,7 @@ int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, in
   r.x = x; r.router = router; r.T = T; r.H = H; r.E = E; r.k = k; r.flags = route_flags;
   r.topk_idx = topk_idx; r.topk_w = topk_w;
   route_ws_carve(r, p);
-  p += align256(route_ws_bytes(T, E, k));
+  p += align256(route_ws_bytes(T, H, E, k));
   int32_t* perm = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)T * k * 4);
   int32_t* off = reinterpret_cast<int32_t*>(p);

@@ -68,42 +68,57 @@ hipError_t router_logits_nt(const uint16_t* x, const float* R, int H, int E, flo
 // ---------------------------------------------------------- large-T router GEMM
 // logits[T][E] = x[T][H] . R[E][H]^T on bf16 MFMA with fp32 accuracy: every fp32
 // router weight splits exactly into three bf16 terms (hi + mid + lo covers the
-// 24-bit significand), x is already bf16, so each product is exact in fp32 and
-// the three MFMA chains accumulate in fp32.  64x64 tile per workgroup (4 waves
-// of 32x32), K staged through LDS 64 at a time with the next step's global
-// loads issued before the current step's MFMAs.
+// 24-bit significand; a small kernel writes the three planes once per call), x
+// is already bf16, so each product is exact in fp32 and the three MFMA chains
+// accumulate in fp32.  64x64 tile per workgroup (4 waves of 32x32), K staged
+// through LDS 64 at a time with the next step's global loads issued before the
+// current step's MFMAs.
 typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float rfloatx16_t __attribute__((ext_vector_type(16)));
 constexpr int RBM = 64, RBN = 64, RBK = 64, RLD = RBK + 8;
 
-__device__ __forceinline__ void split3(float r, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
-  hi = f32_to_bf16_rne(r);
-  const float r1 = r - bf16_to_f32(hi);
-  mid = f32_to_bf16_rne(r1);
-  const float r2 = r1 - bf16_to_f32(mid);
-  lo = f32_to_bf16_rne(r2);
+__global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ R, size_t n,
+                                                      uint16_t* __restrict__ planes) {
+  const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  const float4 v = *reinterpret_cast<const float4*>(R + i);
+  const float f[4] = {v.x, v.y, v.z, v.w};
+  uint16_t hh[4], mm[4], ll[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hh[q] = f32_to_bf16_rne(f[q]);
+    const float r1 = f[q] - bf16_to_f32(hh[q]);
+    mm[q] = f32_to_bf16_rne(r1);
+    ll[q] = f32_to_bf16_rne(r1 - bf16_to_f32(mm[q]));
+  }
+  *reinterpret_cast<uint2*>(planes + i) = make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
+  *reinterpret_cast<uint2*>(planes + n + i) = make_uint2(mm[0] | ((uint32_t)mm[1] << 16), mm[2] | ((uint32_t)mm[3] << 16));
+  *reinterpret_cast<uint2*>(planes + 2 * n + i) = make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
 }
 
 __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict__ x,
-                                                     const float* __restrict__ R, int T, int H, int E,
-                                                     float* __restrict__ logits) {
+                                                     const uint16_t* __restrict__ planes, int T, int H,
+                                                     int E, float* __restrict__ logits) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[RBM * RLD];
   __shared__ __attribute__((aligned(16))) uint16_t rs[3][RBN * RLD];
   const int tm = blockIdx.y * RBM, tn = blockIdx.x * RBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
-  // staging: thread -> row tid/4, 16 columns at (tid%4)*16
+  // staging: thread -> row tid/4, 16 columns at (tid%4)*16 of each of x and the 3 planes
   const int sr = tid >> 2, sc = (tid & 3) * 16;
   const bool xrow_ok = tm + sr < T, rrow_ok = tn + sr < E;
+  const size_t plane = (size_t)E * H;
   const uint16_t* xp = x + (size_t)(xrow_ok ? tm + sr : 0) * H + sc;
-  const float* rp = R + (size_t)(rrow_ok ? tn + sr : 0) * H + sc;
-  uint4 xa[2];
-  float4 ra[4];
+  const uint16_t* rp = planes + (size_t)(rrow_ok ? tn + sr : 0) * H + sc;
+  uint4 xa[2], ra[3][2];
   auto gload = [&](int kb) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) xa[j] = xrow_ok ? reinterpret_cast<const uint4*>(xp + kb)[j] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ra[j] = rrow_ok ? reinterpret_cast<const float4*>(rp + kb)[j] : make_float4(0, 0, 0, 0);
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        ra[p][j] = rrow_ok ? reinterpret_cast<const uint4*>(rp + p * plane + kb)[j] : make_uint4(0, 0, 0, 0);
   };
   rfloatx16_t acc;
 #pragma unroll
@@ -112,20 +127,10 @@ __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict_
   for (int kb = 0; kb < H; kb += RBK) {
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 2; ++j) *reinterpret_cast<uint4*>(xs + sr * RLD + sc + 8 * j) = xa[j];
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<uint4*>(xs + sr * RLD + sc + 8 * j) = xa[j];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float f[4] = {ra[j].x, ra[j].y, ra[j].z, ra[j].w};
-      uint16_t hh[4], mm[4], ll[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) split3(f[q], hh[q], mm[q], ll[q]);
-      uint2 vh, vm, vl;
-      vh.x = hh[0] | ((uint32_t)hh[1] << 16); vh.y = hh[2] | ((uint32_t)hh[3] << 16);
-      vm.x = mm[0] | ((uint32_t)mm[1] << 16); vm.y = mm[2] | ((uint32_t)mm[3] << 16);
-      vl.x = ll[0] | ((uint32_t)ll[1] << 16); vl.y = ll[2] | ((uint32_t)ll[3] << 16);
-      *reinterpret_cast<uint2*>(rs[0] + sr * RLD + sc + 4 * j) = vh;
-      *reinterpret_cast<uint2*>(rs[1] + sr * RLD + sc + 4 * j) = vm;
-      *reinterpret_cast<uint2*>(rs[2] + sr * RLD + sc + 4 * j) = vl;
+      for (int p = 0; p < 3; ++p) *reinterpret_cast<uint4*>(rs[p] + sr * RLD + sc + 8 * j) = ra[p][j];
     }
     __syncthreads();
     if (kb + RBK < H) gload(kb + RBK);
@@ -271,8 +276,15 @@ hipError_t launch_router_logits(const uint16_t* x, const float* R, int T, int H,
       default: return router_logits_nt<4>(x, R, H, E, logits, s);
     }
   }
+  return hipErrorInvalidValue;  // large T needs the split planes (launch_router_gemm)
+}
+
+hipError_t launch_router_gemm(const uint16_t* x, const float* R, int T, int H, int E, float* logits,
+                              uint16_t* planes, hipStream_t s) {
+  const size_t n = (size_t)E * H;
+  hipLaunchKernelGGL(k_router_split, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, R, n, planes);
   dim3 grid((E + RBN - 1) / RBN, (T + RBM - 1) / RBM);
-  hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, x, R, T, H, E, logits);
+  hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, x, planes, T, H, E, logits);
   return hipGetLastError();
 }
 
@@ -281,10 +293,11 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, unsigned flags,
   return topk_impl(logits, T, E, k, flags, idx, w, s);
 }
 
-size_t route_ws_bytes(int T, int E, int k) {
+size_t route_ws_bytes(int T, int H, int E, int k) {
   const size_t n = (size_t)T * k;
   const size_t nchunk = (n + kPermChunk - 1) / kPermChunk;
-  return align256((size_t)T * E * 4) + align256(nchunk * E * 4 + 4);
+  const size_t planes = T > kGemvMaxT ? align256((size_t)3 * E * H * 2) : 0;
+  return align256((size_t)T * E * 4) + align256(nchunk * E * 4 + 4) + planes;
 }
 
 void route_ws_carve(RouteArgs& a, void* ws) {
@@ -292,6 +305,8 @@ void route_ws_carve(RouteArgs& a, void* ws) {
   a.logits = reinterpret_cast<float*>(p);
   p += align256((size_t)a.T * a.E * 4);
   a.chunk_cnt = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)((a.T * a.k + kPermChunk - 1) / kPermChunk) * a.E * 4 + 4);
+  a.planes = a.T > kGemvMaxT ? reinterpret_cast<uint16_t*>(p) : nullptr;
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
@@ -300,7 +315,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(k_fill_zero, dim3((a.E + 1 + 255) / 256), dim3(256), 0, s, a.expert_off, a.E + 1);
     return hipGetLastError();
   }
-  hipError_t e = launch_router_logits(a.x, a.router, a.T, a.H, a.E, a.logits, s);
+  hipError_t e = a.T <= kGemvMaxT ? launch_router_logits(a.x, a.router, a.T, a.H, a.E, a.logits, s)
+                                  : launch_router_gemm(a.x, a.router, a.T, a.H, a.E, a.logits, a.planes, s);
   if (e != hipSuccess) return e;
   e = launch_topk(a.logits, a.T, a.E, a.k, a.flags, a.topk_idx, a.topk_w, s);
   if (e != hipSuccess || !a.pair_perm) return e;

@@ -116,7 +116,7 @@ int moe_unpack_expert(int fmt, int H, int F, const void* blob, void* const canon
 
 /* Workspace bytes for moe_route (device memory, 256-byte aligned, no
  * initialisation needed). */
-size_t moe_route_workspace(int T, int E, int k);
+size_t moe_route_workspace(int T, int H, int E, int k);
 
 /* Router, softmax and top-k for T tokens (page "753B...", section
  * "混合专家架构（MoE）的天然稀疏性").
