@@ -150,13 +150,24 @@ def moe_unpack_expert(fmt, H, F, blob):
     return out
 
 
-def pack_layer(fmt, H, F, batch, dst, stride):
-    """Pack a synth ``experts`` batch (leading axis = expert) into ``dst`` at ``stride``."""
+def pack_layer(fmt, H, F, batch, dst, stride, threads=8):
+    """Pack a synth ``experts`` batch (leading axis = expert) into ``dst`` at ``stride``.
+
+    Experts are packed on a small thread pool (the C call releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
     n = batch["codes_g"].shape[0]
-    for i in range(n):
+
+    def one(i):
         canon = {k: batch[k][i] for k in ("codes_g", "codes_u", "codes_d", "scales_g", "scales_u", "scales_d")}
         canon["tau_g"], canon["tau_u"], canon["tau_d"] = batch["tau"][i]
         moe_pack_expert(fmt, H, F, canon, dst[i * stride:(i + 1) * stride])
+
+    if threads <= 1 or n < 4:
+        for i in range(n):
+            one(i)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(n)))
     return dst
 
 

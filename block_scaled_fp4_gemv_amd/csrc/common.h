@@ -10,10 +10,24 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- blob geometry
 // One expert blob: gate/up/down codes, then their scales, then tau[3]; every
-// section begins on a 256-byte boundary.  Codes and scales keep the canonical
-// row-major order: for a matrix [N][K] the 16-byte code chunk g (= n*C + c,
-// C = chunks per row) has its NVFP4 scale pair at byte 2g, its MXFP4 scale at
-// byte g and its FP8 scale at float g/8 of the scale section.
+// section begins on a 256-byte boundary.  A matrix [N][K] (blocks along K) is
+// stored as fragments of 16 rows x 128 k, N/16 row groups by S = K/128 steps,
+// fragment f = g*S + s.  Lane l (0..63) of a wavefront owns row 16g + l%16 and
+// the 32 consecutive elements 128s + 32(l/16) .. +31 of fragment f: the k set
+// lane l supplies to four consecutive v_mfma_f32_16x16x32_bf16 operands, and a
+// 32-element dot product for a GEMV lane.  Inside a fragment:
+//   FP4 codes    64 x 16 B: lane l at byte 16l (canonical byte order inside)
+//   FP8 codes    2 pieces x 64 x 16 B: elements 16p..16p+15 of lane l at 1024p + 16l
+//   NVFP4 scales 64 x 2 B: the lane's two 16-element blocks, lower k first
+//   MXFP4 scales 64 x 1 B: the lane's 32-element block
+//   FP8 scales   16 x fp32: row r's scale for the step at float r
+// so each wavefront-wide 16-byte load of a fragment reads 1 KiB contiguously.
+constexpr int kFragRows = 16, kFragK = 128;
+__host__ __device__ constexpr size_t frag_code_bytes(int fmt) { return fmt == MOE_FMT_FP8_E4M3 ? 2048 : 1024; }
+__host__ __device__ constexpr size_t frag_scale_bytes(int fmt) {
+  return fmt == MOE_FMT_NVFP4 ? 128 : 64;
+}
+
 struct BlobLayout {
   size_t cg, cu, cd, sg, su, sd, tau, total;
 };

@@ -6,388 +6,382 @@
 // "混合专家架构（MoE）的天然稀疏性"; dequantization at compute time: page
 // "8GB显存跑35B MoE模型：FreeToken引擎本地部署实战", §2.1).
 //
-// Mapping onto a 64-lane wavefront: a matrix row of K elements is C 16-byte
-// chunks (C = K/32 for FP4, K/16 for FP8).  A wave owns RB consecutive rows
-// (RB*C chunks) and lane l loads chunks l, l+64, ... of that run: one fully
-// coalesced 1 KiB dwordx4 load per "slot".  Because C divides 64 or 64 divides
-// C, each lane always meets the same chunk columns, so its slice of the input
-// vector stays in registers for every row.  Partial dot products use the gfx950
-// FP4/FP8 -> bf16 conversions and v_dot2_f32_bf16 (fp32 accumulate), and rows
-// are finished with cross-lane reductions.
+// Mapping onto 64-lane wavefronts: the blob stores every matrix as fragments of
+// 16 rows x 128 k in which lane l owns row l%16 and 32 consecutive k (common.h).
+// A workgroup owns one 16-row group (of gate and up together for gate/up); its
+// waves take the K steps round-robin.  Every lane issues all loads of a batch
+// of steps first (one contiguous 1 KiB load per fragment per wavefront), then
+// dots its 32 elements with the matching slice of the input vector using the
+// gfx950 FP4/FP8 -> bf16 conversions and v_dot2_f32_bf16 (fp32 accumulate).
+// A row is finished by two lane shuffles (its four lanes) and a fixed-order sum
+// over the waves in LDS, so results do not depend on timing.
 #include "common.h"
 #include "launch.h"
 #include "topk.h"
 
 namespace {
 
-template <int FMT, int C, int RB>
-struct Gemv {
-  static constexpr bool kFP8 = FMT == MOE_FMT_FP8_E4M3;
-  static constexpr int NS = RB * C / 64;            // 16-byte slots per lane
-  static constexpr int XS = C >= 64 ? C / 64 : 1;   // x slices per lane
-  static constexpr int XW = kFP8 ? 8 : 16;          // bf16 pairs per x slice
-  static constexpr int EPC = kFP8 ? 16 : 32;        // elements per chunk
-  static constexpr int RPS = C >= 64 ? 1 : 64 / C;  // rows per slot
-  static constexpr int NOUT = C >= 64 ? RB : NS;    // per-lane results
-  static_assert(NS >= 1 && (RB * C) % 64 == 0, "bad row block");
-  static_assert(C % 64 == 0 || 64 % C == 0, "bad chunk count");
+constexpr int kMaxDim = 8192;
 
-  uint4 code[NS];
-  uint32_t sc[NS];
+template <int FMT>
+struct Frag {
+  static constexpr bool kFP8 = FMT == MOE_FMT_FP8_E4M3;
+  uint4 c[kFP8 ? 2 : 1];
+  uint32_t sc;
 
   __device__ __forceinline__ void load(const uint8_t* __restrict__ codes,
-                                       const uint8_t* __restrict__ scales, int row0, int lane) {
-    const size_t g0 = (size_t)row0 * C + lane;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const size_t g = g0 + 64 * s;
-      code[s] = reinterpret_cast<const uint4*>(codes)[g];
-      if constexpr (FMT == MOE_FMT_NVFP4)
-        sc[s] = reinterpret_cast<const uint16_t*>(scales)[g];
-      else if constexpr (FMT == MOE_FMT_MXFP4)
-        sc[s] = scales[g];
-      else
-        sc[s] = reinterpret_cast<const uint32_t*>(scales)[g >> 3];
-    }
-  }
-
-  static __device__ __forceinline__ void load_x(const uint16_t* __restrict__ xrow, int lane,
-                                                uint32_t (&xs)[XS][XW]) {
-#pragma unroll
-    for (int i = 0; i < XS; ++i) {
-      const int col = C >= 64 ? 64 * i + lane : lane % C;
-      const uint4* p = reinterpret_cast<const uint4*>(xrow + (size_t)col * EPC);
-#pragma unroll
-      for (int j = 0; j < XW / 4; ++j) {
-        uint4 v = p[j];
-        xs[i][4 * j + 0] = v.x;
-        xs[i][4 * j + 1] = v.y;
-        xs[i][4 * j + 2] = v.z;
-        xs[i][4 * j + 3] = v.w;
-      }
-    }
-  }
-
-  __device__ __forceinline__ void compute(const uint32_t (&xs)[XS][XW], float (&out)[NOUT]) const {
-    float p[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int xi = C >= 64 ? s % XS : 0;
-      if constexpr (FMT == MOE_FMT_NVFP4) {
-        const float slo = e4m3_byte0_to_f32(sc[s]), shi = e4m3_byte0_to_f32(sc[s] >> 8);
-        p[s] = chunk_dot_nvfp4(code[s], slo, shi, xs[xi]);
-      } else if constexpr (FMT == MOE_FMT_MXFP4) {
-        p[s] = chunk_dot_mxfp4(code[s], e8m0_to_f32(sc[s]), xs[xi], 0.0f);
-      } else {
-        p[s] = __uint_as_float(sc[s]) * chunk_dot_fp8(code[s], xs[xi], 0.0f);
-      }
-    }
-    if constexpr (C >= 64) {
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        float a = 0.0f;
-#pragma unroll
-        for (int i = 0; i < XS; ++i) a += p[r * XS + i];
-        out[r] = wave_sum(a);
-      }
+                                       const uint8_t* __restrict__ scales, size_t f, int lane) {
+    if constexpr (kFP8) {
+      c[0] = reinterpret_cast<const uint4*>(codes + f * 2048)[lane];
+      c[1] = reinterpret_cast<const uint4*>(codes + f * 2048 + 1024)[lane];
+      sc = reinterpret_cast<const uint32_t*>(scales + f * 64)[lane & 15];
     } else {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) out[s] = group_sum<C>(p[s]);
+      c[0] = reinterpret_cast<const uint4*>(codes + f * 1024)[lane];
+      if constexpr (FMT == MOE_FMT_NVFP4)
+        sc = reinterpret_cast<const uint16_t*>(scales + f * 128)[lane];
+      else
+        sc = scales[f * 64 + lane];
     }
   }
 
-  // Row (relative to row0) of result i in this lane, and whether this lane writes it.
-  static __device__ __forceinline__ int row_of(int i, int lane) {
-    return C >= 64 ? i : i * RPS + lane / C;
-  }
-  static __device__ __forceinline__ bool owner(int i, int lane) {
-    return C >= 64 ? lane == (i & 63) : (lane % C) == 0;
+  // The lane's 32 elements against xs (16 bf16 pairs of the same k).
+  __device__ __forceinline__ float dot(const uint32_t* xs) const {
+    if constexpr (FMT == MOE_FMT_NVFP4)
+      return chunk_dot_nvfp4(c[0], e4m3_byte0_to_f32(sc), e4m3_byte0_to_f32(sc >> 8), xs);
+    else if constexpr (FMT == MOE_FMT_MXFP4)
+      return chunk_dot_mxfp4(c[0], e8m0_to_f32(sc), xs, 0.0f);
+    else
+      return __uint_as_float(sc) * chunk_dot_fp8(c[1], xs + 8, chunk_dot_fp8(c[0], xs, 0.0f));
   }
 };
 
-// Rows per wave for a matrix of C chunks per row: about four 16-byte slots per lane.
-constexpr int rows_per_wave(int C) { return C >= 256 ? 1 : 256 / C; }
-// Down + combine: at most 8 rows per workgroup so that a 2048-row layer spreads
-// over >= 256 workgroups (one wave per routed pair in each).
-constexpr int rows_per_wave_down(int C) {
-  return (64 / C > (rows_per_wave(C) < 8 ? rows_per_wave(C) : 8)) ? 64 / C
-                                                                    : (rows_per_wave(C) < 8 ? rows_per_wave(C) : 8);
+// 32 bf16 (16 pairs) starting at p (16-byte aligned).
+__device__ __forceinline__ void load_xslice(const uint16_t* p, uint32_t (&xs)[16]) {
+  const uint4* v = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 u = v[j];
+    xs[4 * j + 0] = u.x;
+    xs[4 * j + 1] = u.y;
+    xs[4 * j + 2] = u.z;
+    xs[4 * j + 3] = u.w;
+  }
 }
 
-template <int FMT, int C, int RB, int WPB>
-__global__ __launch_bounds__(WPB * 64) void k_gateup_gemv(
-    const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F,
-    const uint16_t* __restrict__ x, int k, const int32_t* __restrict__ topk_idx,
-    const int32_t* __restrict__ pair_slot, const int32_t* __restrict__ pair_subset,
-    uint16_t* __restrict__ hbuf) {
-  using G = Gemv<FMT, C, RB>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q = pair_subset ? pair_subset[blockIdx.y] : (int)blockIdx.y;
-  const int slot = pair_slot ? pair_slot[q] : topk_idx[q];
-  const uint8_t* blob = pool + (size_t)slot * stride;
-  const int row0 = (blockIdx.x * WPB + wave) * RB;
-  G g, u;
-  g.load(blob + L.cg, blob + L.sg, row0, lane);
-  u.load(blob + L.cu, blob + L.su, row0, lane);
-  uint32_t xs[G::XS][G::XW];
-  G::load_x(x + (size_t)(q / k) * H, lane, xs);
-  float og[G::NOUT], ou[G::NOUT];
-  g.compute(xs, og);
-  u.compute(xs, ou);
-  float tg = 1.0f, tu = 1.0f;
-  if constexpr (FMT == MOE_FMT_NVFP4) {
-    const float* tau = reinterpret_cast<const float*>(blob + L.tau);
-    tg = tau[0];
-    tu = tau[1];
-  }
+// Sum of the four lanes l, l^16, l^32, l^48 (the lanes of one fragment row).
+__device__ __forceinline__ float row_lanes_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Waves per workgroup and steps per load batch for S steps of 128 k.
+constexpr int gemv_waves(int S) { return S < 8 ? S : 8; }
+inline int gemv_batch(int S) {
+  const int per = (S + gemv_waves(S) - 1) / gemv_waves(S);
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
+}
+
+// Gate and up rows 16g.. of one pair: steps w, w+nw, ... of S, in batches of NB
+// with every load of a batch issued before its arithmetic.
+template <int FMT, int NB>
+__device__ __forceinline__ void gateup_partial(const uint8_t* __restrict__ blob, const BlobLayout& L,
+                                               int S, int g, const uint16_t* xl, int w, int nw,
+                                               int lane, float& ag, float& au) {
+  const int q = lane >> 4;
+  for (int s0 = w; s0 < S; s0 += NB * nw) {
+    Frag<FMT> fg[NB], fu[NB];
 #pragma unroll
-  for (int i = 0; i < G::NOUT; ++i) {
-    if (G::owner(i, lane)) {
-      const float gv = og[i] * tg, uv = ou[i] * tu;
-      hbuf[(size_t)q * F + row0 + G::row_of(i, lane)] = f32_to_bf16_rne(silu_f32(gv) * uv);
+    for (int i = 0; i < NB; ++i) {
+      const int s = s0 + i * nw;
+      if (s < S) {
+        const size_t f = (size_t)g * S + s;
+        fg[i].load(blob + L.cg, blob + L.sg, f, lane);
+        fu[i].load(blob + L.cu, blob + L.su, f, lane);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int s = s0 + i * nw;
+      if (s < S) {
+        uint32_t xs[16];
+        load_xslice(xl + kFragK * s + 32 * q, xs);
+        ag += fg[i].dot(xs);
+        au += fu[i].dot(xs);
+      }
     }
   }
 }
 
-// Gate/up for a decode layer that starts from the router logits: wave 0 of
-// every workgroup runs the softmax + top-k of its token (identical in every
-// workgroup), which saves a dependent kernel between routing and the experts.
-// The token's first pair, column-block 0, writes topk_idx / topk_w.
-template <int FMT, int C, int RB, int WPB, int NV>
-__global__ __launch_bounds__(WPB * 64) void k_gateup_gemv_topk(
+// Rows 16g.. of one matrix (down) for one pair over steps w, w+nw, ... of S in
+// batches of NB.  The caller issues the first batch (load) before staging the
+// pair's h row in LDS, so the weight latency overlaps the staging.
+template <int FMT, int NB>
+struct DownRows {
+  Frag<FMT> fd[NB];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                       int S, int g, int s0, int nw, int lane) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      if (s0 + i * nw < S) fd[i].load(codes, scales, (size_t)g * S + s0 + i * nw, lane);
+  }
+
+  __device__ __forceinline__ float dot(const uint16_t* xrow, int S, int s0, int nw, int lane) const {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int s = s0 + i * nw;
+      if (s < S) {
+        uint32_t xs[16];
+        load_xslice(xrow + kFragK * s + 32 * (lane >> 4), xs);
+        a += fd[i].dot(xs);
+      }
+    }
+    return a;
+  }
+};
+
+// Gate/up + SwiGLU for rows 16*blockIdx.x.. of pair blockIdx.y (or pair_subset
+// entry).  TOPK: the pair's expert comes from the softmax/top-k of `logits`,
+// which wave 0 of every workgroup computes (identical everywhere); column
+// group 0 of the token's first pair writes topk_idx / topk_w.
+template <int FMT, int NB, bool TOPK, int NV>
+__global__ __launch_bounds__(512) void k_gateup_gemv(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F, int E, int k,
     unsigned flags, const uint16_t* __restrict__ x, const float* __restrict__ logits,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint16_t* __restrict__ hbuf) {
-  using G = Gemv<FMT, C, RB>;
-  __shared__ int s_expert;
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, const int32_t* __restrict__ pair_slot,
+    const int32_t* __restrict__ pair_subset, uint16_t* __restrict__ hbuf) {
+  __shared__ __attribute__((aligned(16))) uint16_t xl[kMaxDim];
+  __shared__ float red[8][2][16];
+  __shared__ int s_slot;
   __shared__ TopkScratch s_topk;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q = blockIdx.y, t = q / k, j = q % k;
-  uint32_t xs[G::XS][G::XW];
-  G::load_x(x + (size_t)t * H, lane, xs);
-  if (wave == 0) {
-    float v[NV];
-    wave_load_logits<NV>(logits + (size_t)t * E, E, v);
-    int idx;
-    float w;
-    wave_topk_regs<NV>(v, E, k, flags, idx, w, s_topk);
-    if (lane == j) s_expert = idx;
-    if (blockIdx.x == 0 && j == 0 && lane < k) {
-      topk_idx[(size_t)t * k + lane] = idx;
-      topk_w[(size_t)t * k + lane] = w;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int q = TOPK ? (int)blockIdx.y : (pair_subset ? pair_subset[blockIdx.y] : (int)blockIdx.y);
+  const int t = q / k, j = q % k, g = blockIdx.x;
+  const uint4* xs4 = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+  for (int i = threadIdx.x; i < H / 8; i += blockDim.x) reinterpret_cast<uint4*>(xl)[i] = xs4[i];
+  if constexpr (TOPK) {
+    if (w == 0) {
+      float v[NV];
+      wave_load_logits<NV>(logits + (size_t)t * E, E, v);
+      int idx;
+      float wt;
+      wave_topk_regs<NV>(v, E, k, flags, idx, wt, s_topk);
+      if (lane == j) s_slot = idx;
+      if (g == 0 && j == 0 && lane < k) {
+        topk_idx[(size_t)t * k + lane] = idx;
+        topk_w[(size_t)t * k + lane] = wt;
+      }
     }
+  } else {
+    if (threadIdx.x == 0) s_slot = pair_slot ? pair_slot[q] : topk_idx[q];
   }
   __syncthreads();
-  const uint8_t* blob = pool + (size_t)s_expert * stride;
-  const int row0 = (blockIdx.x * WPB + wave) * RB;
-  G g, u;
-  g.load(blob + L.cg, blob + L.sg, row0, lane);
-  u.load(blob + L.cu, blob + L.su, row0, lane);
-  float og[G::NOUT], ou[G::NOUT];
-  g.compute(xs, og);
-  u.compute(xs, ou);
-  float tg = 1.0f, tu = 1.0f;
-  if constexpr (FMT == MOE_FMT_NVFP4) {
-    const float* tau = reinterpret_cast<const float*>(blob + L.tau);
-    tg = tau[0];
-    tu = tau[1];
+  const uint8_t* blob = pool + (size_t)s_slot * stride;
+  float ag = 0.0f, au = 0.0f;
+  gateup_partial<FMT, NB>(blob, L, H / kFragK, g, xl, w, nw, lane, ag, au);
+  ag = row_lanes_sum(ag);
+  au = row_lanes_sum(au);
+  if (lane < 16) {
+    red[w][0][lane] = ag;
+    red[w][1][lane] = au;
   }
-#pragma unroll
-  for (int i = 0; i < G::NOUT; ++i) {
-    if (G::owner(i, lane)) {
-      const float gv = og[i] * tg, uv = ou[i] * tu;
-      hbuf[(size_t)q * F + row0 + G::row_of(i, lane)] = f32_to_bf16_rne(silu_f32(gv) * uv);
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float G = 0.0f, U = 0.0f;
+    for (int i = 0; i < nw; ++i) {
+      G += red[i][0][threadIdx.x];
+      U += red[i][1][threadIdx.x];
     }
+    if constexpr (FMT == MOE_FMT_NVFP4) {
+      const float* tau = reinterpret_cast<const float*>(blob + L.tau);
+      G *= tau[0];
+      U *= tau[1];
+    }
+    hbuf[(size_t)q * F + kFragRows * g + threadIdx.x] = f32_to_bf16_rne(silu_f32(G) * U);
   }
 }
 
-template <int FMT, int C, int RB, int WPB>
-__global__ __launch_bounds__(WPB * 64) void k_down_gemv(
+// y rows 16*blockIdx.x.. of pair blockIdx.y (or pair_subset entry).
+template <int FMT, int NB>
+__global__ __launch_bounds__(512) void k_down_gemv(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F, int k,
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ pair_slot,
-    const int32_t* __restrict__ pair_subset, const uint16_t* __restrict__ hbuf,
-    float* __restrict__ y) {
-  using G = Gemv<FMT, C, RB>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int32_t* __restrict__ pair_subset, const uint16_t* __restrict__ hbuf, float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t hl[kMaxDim];
+  __shared__ float red[8][16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int q = pair_subset ? pair_subset[blockIdx.y] : (int)blockIdx.y;
   const int slot = pair_slot ? pair_slot[q] : topk_idx[q];
   const uint8_t* blob = pool + (size_t)slot * stride;
-  const int row0 = (blockIdx.x * WPB + wave) * RB;
-  G d;
-  d.load(blob + L.cd, blob + L.sd, row0, lane);
-  uint32_t xs[G::XS][G::XW];
-  G::load_x(hbuf + (size_t)q * F, lane, xs);
-  float o[G::NOUT];
-  d.compute(xs, o);
-  float td = 1.0f;
-  if constexpr (FMT == MOE_FMT_NVFP4) td = reinterpret_cast<const float*>(blob + L.tau)[2];
-#pragma unroll
-  for (int i = 0; i < G::NOUT; ++i)
-    if (G::owner(i, lane)) y[(size_t)q * H + row0 + G::row_of(i, lane)] = o[i] * td;
+  const int g = blockIdx.x;
+  const int S = F / kFragK;
+  DownRows<FMT, NB> d;
+  d.load(blob + L.cd, blob + L.sd, S, g, w, nw, lane);
+  const uint4* h4 = reinterpret_cast<const uint4*>(hbuf + (size_t)q * F);
+  for (int i = threadIdx.x; i < F / 8; i += blockDim.x) reinterpret_cast<uint4*>(hl)[i] = h4[i];
+  __syncthreads();
+  float a = d.dot(hl, S, w, nw, lane);
+  for (int s0 = w + NB * nw; s0 < S; s0 += NB * nw) {
+    d.load(blob + L.cd, blob + L.sd, S, g, s0, nw, lane);
+    a += d.dot(hl, S, s0, nw, lane);
+  }
+  a = row_lanes_sum(a);
+  if (lane < 16) red[w][lane] = a;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float v = 0.0f;
+    for (int i = 0; i < nw; ++i) v += red[i][threadIdx.x];
+    if constexpr (FMT == MOE_FMT_NVFP4) v *= reinterpret_cast<const float*>(blob + L.tau)[2];
+    y[(size_t)q * H + kFragRows * g + threadIdx.x] = v;
+  }
 }
 
-// Down GEMV for all k pairs of one token with the gate-weighted combine fused:
-// wave j computes y[t*k+j] on RB rows, then out[t] = bf16(sum_j w_j * y_j).
-template <int FMT, int C, int RB>
+// Down for all k pairs of token blockIdx.y (wave j = pair j) on rows
+// 16*blockIdx.x.., with the gate-weighted combine fused:
+// out[t] = bf16(sum_j w_j * y_j) accumulated in fp32 in j order.
+// Dynamic LDS: k rows of h (F bf16 each).
+template <int FMT, int NB>
 __global__ __launch_bounds__(1024) void k_down_combine_gemv(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F, int k,
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ pair_slot,
     const uint16_t* __restrict__ hbuf, const float* __restrict__ topk_w, float* __restrict__ y,
     uint16_t* __restrict__ out) {
-  using G = Gemv<FMT, C, RB>;
-  __shared__ float ys[16][RB];
+  extern __shared__ __attribute__((aligned(16))) uint16_t hl_dyn[];
+  __shared__ float ys[16][16];
   const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
-  const int t = blockIdx.y, q = t * k + j;
+  const int t = blockIdx.y, q = t * k + j, g = blockIdx.x;
   const int slot = pair_slot ? pair_slot[q] : topk_idx[q];
   const uint8_t* blob = pool + (size_t)slot * stride;
-  const int row0 = blockIdx.x * RB;
-  G d;
-  d.load(blob + L.cd, blob + L.sd, row0, lane);
-  uint32_t xs[G::XS][G::XW];
-  G::load_x(hbuf + (size_t)q * F, lane, xs);
-  float o[G::NOUT];
-  d.compute(xs, o);
-  float td = 1.0f;
-  if constexpr (FMT == MOE_FMT_NVFP4) td = reinterpret_cast<const float*>(blob + L.tau)[2];
-#pragma unroll
-  for (int i = 0; i < G::NOUT; ++i) {
-    if (G::owner(i, lane)) {
-      const int r = G::row_of(i, lane);
-      const float v = o[i] * td;
-      ys[j][r] = v;
-      if (y) y[(size_t)q * H + row0 + r] = v;
-    }
+  uint16_t* hl = hl_dyn + (size_t)j * F;
+  const int S = F / kFragK;
+  DownRows<FMT, NB> d;
+  d.load(blob + L.cd, blob + L.sd, S, g, 0, 1, lane);
+  const uint4* h4 = reinterpret_cast<const uint4*>(hbuf + (size_t)q * F);
+  for (int i = lane; i < F / 8; i += 64) reinterpret_cast<uint4*>(hl)[i] = h4[i];
+  __syncthreads();
+  float a = d.dot(hl, S, 0, 1, lane);
+  for (int s0 = NB; s0 < S; s0 += NB) {
+    d.load(blob + L.cd, blob + L.sd, S, g, s0, 1, lane);
+    a += d.dot(hl, S, s0, 1, lane);
+  }
+  a = row_lanes_sum(a);
+  if (lane < 16) {
+    if constexpr (FMT == MOE_FMT_NVFP4) a *= reinterpret_cast<const float*>(blob + L.tau)[2];
+    ys[j][lane] = a;
+    if (y) y[(size_t)q * H + kFragRows * g + lane] = a;
   }
   __syncthreads();
-  if (threadIdx.x < RB) {
-    const float* w = topk_w + (size_t)t * k;
+  if (threadIdx.x < 16) {
+    const float* wt = topk_w + (size_t)t * k;
     float acc = 0.0f;
-    for (int jj = 0; jj < k; ++jj) acc = fmaf(w[jj], ys[jj][threadIdx.x], acc);
-    out[(size_t)t * H + row0 + threadIdx.x] = f32_to_bf16_rne(acc);
+    for (int jj = 0; jj < k; ++jj) acc = fmaf(wt[jj], ys[jj][threadIdx.x], acc);
+    out[(size_t)t * H + kFragRows * g + threadIdx.x] = f32_to_bf16_rne(acc);
   }
 }
 
-
-
-template <int FMT, int C>
-hipError_t launch_gateup_c(const FfnArgs& a, hipStream_t s) {
-  constexpr int RB = rows_per_wave(C), WPB = 4;
-  if (a.F % (RB * WPB)) return hipErrorInvalidValue;
-  dim3 grid(a.F / (RB * WPB), a.n_pairs);
-  hipLaunchKernelGGL((k_gateup_gemv<FMT, C, RB, WPB>), grid, dim3(WPB * 64), 0, s, a.pool, a.stride,
-                     a.L, a.H, a.F, a.x, a.k, a.topk_idx, a.pair_slot, a.pair_subset, a.hbuf);
+template <int FMT, bool TOPK, int NV>
+hipError_t launch_gateup_t(const FfnArgs& a, const float* logits, unsigned flags, int32_t* idx, float* w,
+                           hipStream_t s) {
+  const int S = a.H / kFragK, nw = gemv_waves(S);
+  dim3 grid(a.F / kFragRows, TOPK ? a.T * a.k : a.n_pairs), block(64 * nw);
+#define L(NB)                                                                                          \
+  case NB:                                                                                             \
+    hipLaunchKernelGGL((k_gateup_gemv<FMT, NB, TOPK, NV>), grid, block, 0, s, a.pool, a.stride, a.L, \
+                       a.H, a.F, a.E, a.k, flags, a.x, logits, TOPK ? idx : const_cast<int32_t*>(a.topk_idx), \
+                       w, a.pair_slot, a.pair_subset, a.hbuf);                                         \
+    break;
+  switch (gemv_batch(S)) {
+    L(1) L(2) L(4) L(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef L
   return hipGetLastError();
 }
 
-template <int FMT, int C>
-hipError_t launch_down_c(const FfnArgs& a, hipStream_t s) {
-  constexpr int RB = rows_per_wave(C);
-  constexpr int RBC = rows_per_wave_down(C);
-  if (a.out) {
-    if (a.H % RBC || a.k > 16) return hipErrorInvalidValue;
-    dim3 grid(a.H / RBC, a.T);
-    hipLaunchKernelGGL((k_down_combine_gemv<FMT, C, RBC>), grid, dim3(64 * a.k), 0, s, a.pool,
-                       a.stride, a.L, a.H, a.F, a.k, a.topk_idx, a.pair_slot, a.hbuf, a.topk_w,
-                       a.y, a.out);
+template <int FMT>
+hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
+  return launch_gateup_t<FMT, false, 1>(a, nullptr, 0, nullptr, nullptr, s);
+}
+
+template <int FMT>
+hipError_t launch_gateup_topk(const FfnArgs& a, const float* logits, unsigned flags, int32_t* idx, float* w,
+                              hipStream_t s) {
+  if (a.E <= 64) return launch_gateup_t<FMT, true, 1>(a, logits, flags, idx, w, s);
+  if (a.E <= 256) return launch_gateup_t<FMT, true, 4>(a, logits, flags, idx, w, s);
+  return launch_gateup_t<FMT, true, 16>(a, logits, flags, idx, w, s);
+}
+
+template <int FMT>
+hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
+  const int S = a.F / kFragK;
+#define LC(NB)                                                                                         \
+  case NB:                                                                                             \
+    hipLaunchKernelGGL((k_down_combine_gemv<FMT, NB>), grid, dim3(64 * a.k), lds, s, a.pool, a.stride, a.L, \
+                       a.H, a.F, a.k, a.topk_idx, a.pair_slot, a.hbuf, a.topk_w, a.y, a.out);         \
+    break;
+#define LD(NB)                                                                                         \
+  case NB:                                                                                             \
+    hipLaunchKernelGGL((k_down_gemv<FMT, NB>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.L, a.H, \
+                       a.F, a.k, a.topk_idx, a.pair_slot, a.pair_subset, a.hbuf, y);                 \
+    break;
+  const size_t lds = (size_t)a.k * a.F * 2;
+  if (a.out && a.k <= 16 && lds <= 64 * 1024 && !a.pair_subset) {
+    dim3 grid(a.H / kFragRows, a.T);
+    switch (S <= 1 ? 1 : S <= 2 ? 2 : 4) {  // one wave per pair: batches of <= 4 steps
+      LC(1) LC(2) LC(4)
+      default: return hipErrorInvalidValue;
+    }
   } else {
-    constexpr int WPB = 4;
-    if (a.H % (RB * WPB)) return hipErrorInvalidValue;
-    dim3 grid(a.H / (RB * WPB), a.n_pairs);
-    hipLaunchKernelGGL((k_down_gemv<FMT, C, RB, WPB>), grid, dim3(WPB * 64), 0, s, a.pool, a.stride,
-                       a.L, a.H, a.F, a.k, a.topk_idx, a.pair_slot, a.pair_subset, a.hbuf, a.y);
+    // plain down into y; with `out`, the combine follows as its own kernel
+    float* y = a.y ? a.y : (a.out ? a.ybuf : nullptr);
+    if (!y) return hipErrorInvalidValue;
+    const int nw = gemv_waves(S);
+    dim3 grid(a.H / kFragRows, a.n_pairs);
+    switch (gemv_batch(S)) {
+      LD(1) LD(2) LD(4) LD(8)
+      default: return hipErrorInvalidValue;
+    }
+    if (a.out) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_combine(y, a.topk_w, a.T, a.H, a.k, a.out, s);
+    }
   }
+#undef LC
+#undef LD
   return hipGetLastError();
 }
-
-template <int FMT, int C>
-hipError_t launch_gateup_topk_c(const FfnArgs& a, const float* logits, unsigned flags, int32_t* idx,
-                                float* w, hipStream_t s) {
-  constexpr int RB = rows_per_wave(C), WPB = 4;
-  if (a.F % (RB * WPB)) return hipErrorInvalidValue;
-  dim3 grid(a.F / (RB * WPB), a.T * a.k);
-  if (a.E <= 256)
-    hipLaunchKernelGGL((k_gateup_gemv_topk<FMT, C, RB, WPB, 4>), grid, dim3(WPB * 64), 0, s, a.pool,
-                       a.stride, a.L, a.H, a.F, a.E, a.k, flags, a.x, logits, idx, w, a.hbuf);
-  else
-    hipLaunchKernelGGL((k_gateup_gemv_topk<FMT, C, RB, WPB, 16>), grid, dim3(WPB * 64), 0, s, a.pool,
-                       a.stride, a.L, a.H, a.F, a.E, a.k, flags, a.x, logits, idx, w, a.hbuf);
-  return hipGetLastError();
-}
-
-// Chunks per row for the supported K values: FP4 K/32, FP8 K/16.
-#define MOE_FOR_FP4_C(X) X(8) X(16) X(32) X(64) X(128) X(192) X(256)
-#define MOE_FOR_FP8_C(X) X(16) X(32) X(64) X(128) X(256) X(384) X(512)
-
-template <int FMT>
-hipError_t gateup_fmt(const FfnArgs& a, int C, hipStream_t s) {
-#define CASE(c) \
-  case c: return launch_gateup_c<FMT, c>(a, s);
-  if constexpr (FMT == MOE_FMT_FP8_E4M3) {
-    switch (C) { MOE_FOR_FP8_C(CASE) }
-  } else {
-    switch (C) { MOE_FOR_FP4_C(CASE) }
-  }
-#undef CASE
-  return hipErrorInvalidValue;
-}
-
-template <int FMT>
-hipError_t gateup_topk_fmt(const FfnArgs& a, int C, const float* logits, unsigned flags, int32_t* idx,
-                           float* w, hipStream_t s) {
-#define CASE(c) \
-  case c: return launch_gateup_topk_c<FMT, c>(a, logits, flags, idx, w, s);
-  if constexpr (FMT == MOE_FMT_FP8_E4M3) {
-    switch (C) { MOE_FOR_FP8_C(CASE) }
-  } else {
-    switch (C) { MOE_FOR_FP4_C(CASE) }
-  }
-#undef CASE
-  return hipErrorInvalidValue;
-}
-
-template <int FMT>
-hipError_t down_fmt(const FfnArgs& a, int C, hipStream_t s) {
-#define CASE(c) \
-  case c: return launch_down_c<FMT, c>(a, s);
-  if constexpr (FMT == MOE_FMT_FP8_E4M3) {
-    switch (C) { MOE_FOR_FP8_C(CASE) }
-  } else {
-    switch (C) { MOE_FOR_FP4_C(CASE) }
-  }
-#undef CASE
-  return hipErrorInvalidValue;
-}
-
-int chunks_per_row(int fmt, int K) { return fmt == MOE_FMT_FP8_E4M3 ? K / 16 : K / 32; }
 
 }  // namespace
 
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s) {
   if (a.n_pairs == 0) return hipSuccess;
-  const int Cg = chunks_per_row(a.fmt, a.H), Cd = chunks_per_row(a.fmt, a.F);
+  if (a.H > kMaxDim || a.H % kFragK || a.F % kFragK) return hipErrorInvalidValue;
   hipError_t e;
   switch (a.fmt) {
-    case MOE_FMT_NVFP4: e = gateup_fmt<MOE_FMT_NVFP4>(a, Cg, s); break;
-    case MOE_FMT_MXFP4: e = gateup_fmt<MOE_FMT_MXFP4>(a, Cg, s); break;
-    default: e = gateup_fmt<MOE_FMT_FP8_E4M3>(a, Cg, s); break;
+    case MOE_FMT_NVFP4: e = launch_gateup<MOE_FMT_NVFP4>(a, s); break;
+    case MOE_FMT_MXFP4: e = launch_gateup<MOE_FMT_MXFP4>(a, s); break;
+    default: e = launch_gateup<MOE_FMT_FP8_E4M3>(a, s); break;
   }
   if (e != hipSuccess) return e;
   switch (a.fmt) {
-    case MOE_FMT_NVFP4: return down_fmt<MOE_FMT_NVFP4>(a, Cd, s);
-    case MOE_FMT_MXFP4: return down_fmt<MOE_FMT_MXFP4>(a, Cd, s);
-    default: return down_fmt<MOE_FMT_FP8_E4M3>(a, Cd, s);
+    case MOE_FMT_NVFP4: return launch_down<MOE_FMT_NVFP4>(a, s);
+    case MOE_FMT_MXFP4: return launch_down<MOE_FMT_MXFP4>(a, s);
+    default: return launch_down<MOE_FMT_FP8_E4M3>(a, s);
   }
 }
 
 hipError_t launch_decode_layer(const FfnArgs& a0, const float* logits, unsigned route_flags,
                                int32_t* topk_idx, float* topk_w, hipStream_t s) {
   if (a0.T == 0) return hipSuccess;
-  const int Cg = chunks_per_row(a0.fmt, a0.H), Cd = chunks_per_row(a0.fmt, a0.F);
+  if (a0.H > kMaxDim || a0.H % kFragK || a0.F % kFragK) return hipErrorInvalidValue;
   hipError_t e;
   switch (a0.fmt) {
-    case MOE_FMT_NVFP4: e = gateup_topk_fmt<MOE_FMT_NVFP4>(a0, Cg, logits, route_flags, topk_idx, topk_w, s); break;
-    case MOE_FMT_MXFP4: e = gateup_topk_fmt<MOE_FMT_MXFP4>(a0, Cg, logits, route_flags, topk_idx, topk_w, s); break;
-    default: e = gateup_topk_fmt<MOE_FMT_FP8_E4M3>(a0, Cg, logits, route_flags, topk_idx, topk_w, s); break;
+    case MOE_FMT_NVFP4: e = launch_gateup_topk<MOE_FMT_NVFP4>(a0, logits, route_flags, topk_idx, topk_w, s); break;
+    case MOE_FMT_MXFP4: e = launch_gateup_topk<MOE_FMT_MXFP4>(a0, logits, route_flags, topk_idx, topk_w, s); break;
+    default: e = launch_gateup_topk<MOE_FMT_FP8_E4M3>(a0, logits, route_flags, topk_idx, topk_w, s); break;
   }
   if (e != hipSuccess) return e;
   FfnArgs a = a0;
@@ -397,8 +391,8 @@ hipError_t launch_decode_layer(const FfnArgs& a0, const float* logits, unsigned 
   a.pair_subset = nullptr;
   a.n_pairs = a.T * a.k;
   switch (a.fmt) {
-    case MOE_FMT_NVFP4: return down_fmt<MOE_FMT_NVFP4>(a, Cd, s);
-    case MOE_FMT_MXFP4: return down_fmt<MOE_FMT_MXFP4>(a, Cd, s);
-    default: return down_fmt<MOE_FMT_FP8_E4M3>(a, Cd, s);
+    case MOE_FMT_NVFP4: return launch_down<MOE_FMT_NVFP4>(a, s);
+    case MOE_FMT_MXFP4: return launch_down<MOE_FMT_MXFP4>(a, s);
+    default: return launch_down<MOE_FMT_FP8_E4M3>(a, s);
   }
 }

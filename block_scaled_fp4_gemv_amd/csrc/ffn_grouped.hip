@@ -7,21 +7,29 @@
 // here in registers, straight into MFMA operands.
 //
 // Pairs arrive sorted by expert (pair_perm / expert_off).  A device-built tile
-// list holds one (expert, first row) entry per 64 rows of each expert.  A
-// workgroup (4 waves) owns one tile x 128 output columns per matrix: wave w
-// takes columns [32w, 32w+32) for all 64 rows (two 32x32 MFMA subtiles), so each
-// dequantized weight fragment feeds two MFMAs.
+// list holds one (expert, first row) entry per 96 rows of each expert (32 for
+// FP8, whose per-step partial sums need more registers).  A workgroup (4 waves) owns one tile x 128 output columns per matrix:
+// wave w takes the two 16-row weight fragments of columns [32w, 32w+32) and all
+// rows of the tile (up to six 16-row subtiles, v_mfma_f32_16x16x32_bf16), so
+// each dequantized weight operand feeds one MFMA per subtile and an expert's
+// weights are fetched and dequantized once per column tile whenever it has at
+// most 96 rows.  The subtile count is a template parameter chosen per tile,
+// so the inner loop has no branches.
 //
-// K runs in steps of 128.  Lane (n = l%32, h = l/32) loads the contiguous 64
-// weight elements [64h, 64h+64) of row n for the step (FP4: 32 bytes, FP8: 64
-// bytes) and MFMA i (0..7) takes elements 64h + 8i .. +7 from every lane; the
-// activation operand is read from LDS with the same k order, so the products
-// pair up exactly as in the plain k order.
+// K runs in steps of 128 (one weight fragment).  The pre-shuffled blob gives
+// lane l its 32 consecutive k of the fragment with one 16-byte load; MFMA i
+// (0..3) takes elements 8i..8i+7 of them, and the activation operand is read
+// from LDS with the same k order, so products pair up as in the plain k order.
 //   MXFP4: e2m1 -> bf16 with the E8M0 scale folded into the conversion (exact).
 //   NVFP4: e2m1 -> fp32, times the E4M3 block scale (exact in bf16: <= 6
 //          significant bits), high halves packed to bf16; tau in the epilogue.
 //   FP8  : e4m3 -> bf16 exactly; the fp32 scale of the 128-element block is
 //          applied to each step's partial sums.
+// Activation tiles (rows x 128 k bf16) are double-buffered in LDS with the
+// 16-byte chunks of row r stored at chunk ^ (r & 7), which keeps both the
+// staging writes and the MFMA operand reads free of bank conflicts; the next
+// step's activations and the step after next's weights are in flight while a
+// step computes, with one barrier per step.
 // Gate/up writes h = bf16(silu(g) * u) in expert-sorted row order; down
 // writes y (fp32) to the rows of the original pairs.
 #include "common.h"
@@ -30,19 +38,33 @@
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 64, BNW = 32, NWAVE = 4, BN = BNW * NWAVE, BK = 128;
-constexpr int LDA = BK + 8;  // bf16 elements per LDS row (16-byte pad)
+constexpr int NWAVE = 4;     // waves per workgroup
+constexpr int BK = kFragK;   // k per step
+// 16-column weight groups per wave: each activation operand read from LDS
+// feeds NMAT * CG MFMAs; down (one matrix) takes four groups so that LDS reads
+// stay at half the MFMA rate, gate/up two (its two matrices double the reuse).
+template <int NMAT>
+constexpr int kCG = NMAT == 2 ? 2 : 4;
+template <int NMAT>
+constexpr int kBN = NWAVE * kCG<NMAT> * kFragRows;  // output columns per matrix per column tile
+constexpr int ROWB = BK * 2;                 // LDS bytes per activation row per step
+
+template <int FMT>
+constexpr int kSubMax = FMT == MOE_FMT_FP8_E4M3 ? 2 : 6;  // 16-row subtiles per tile
+template <int FMT>
+constexpr int kTileRows = kFragRows * kSubMax<FMT>;
 
 __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict__ expert_off, int E,
-                                                      int32_t* __restrict__ tile_e,
+                                                      int rb, int32_t* __restrict__ tile_e,
                                                       int32_t* __restrict__ tile_m0,
                                                       int32_t* __restrict__ n_tiles) {
   __shared__ int wsum[16];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   const int ne = e < E ? expert_off[e + 1] - expert_off[e] : 0;
-  const int c = (ne + BM - 1) / BM;
+  const int c = (ne + rb - 1) / rb;
   int incl = c;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -59,57 +81,48 @@ __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict_
   base += incl - c;
   for (int j = 0; j < c; ++j) {
     tile_e[base + j] = e;
-    tile_m0[base + j] = j * BM;
+    tile_m0[base + j] = j * rb;
   }
   if (e == 0) *n_tiles = tot;
 }
 
+// One weight fragment (16 columns x 128 k) as held by a lane: 32 consecutive k.
 template <int FMT>
-struct WFrag {
+struct BFrag {
   static constexpr bool kFP8 = FMT == MOE_FMT_FP8_E4M3;
-  static constexpr int NQ = kFP8 ? 4 : 2;  // 16-byte code loads per lane per step
-  uint4 c[NQ];
-  uint32_t s;  // NVFP4: 4 scale bytes; MXFP4: 2 bytes; FP8: fp32 bits
+  u32x4_t c[kFP8 ? 2 : 1];
+  uint32_t s;  // NVFP4: 2 scale bytes; MXFP4: 1 byte; FP8: fp32 bits
 
   __device__ __forceinline__ void load(const uint8_t* __restrict__ codes,
-                                       const uint8_t* __restrict__ scales, int K, int n, int h,
-                                       int kb) {
-    const size_t rowb = kFP8 ? (size_t)n * K : (size_t)n * (K / 2);
-    const int off = kFP8 ? kb + 64 * h : (kb + 64 * h) / 2;
-    const uint4* p = reinterpret_cast<const uint4*>(codes + rowb + off);
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) c[i] = p[i];
-    if constexpr (FMT == MOE_FMT_NVFP4)
-      s = *reinterpret_cast<const uint32_t*>(scales + (size_t)n * (K / 16) + (kb + 64 * h) / 16);
-    else if constexpr (FMT == MOE_FMT_MXFP4)
-      s = *reinterpret_cast<const uint16_t*>(scales + (size_t)n * (K / 32) + (kb + 64 * h) / 32);
-    else
-      s = reinterpret_cast<const uint32_t*>(scales)[(size_t)n * (K / 128) + kb / 128];
-  }
-
-  __device__ __forceinline__ uint32_t word(int w) const {  // 4-byte word w of the lane's codes
-    const uint4& q = c[w >> 2];
-    switch (w & 3) {
-      case 0: return q.x;
-      case 1: return q.y;
-      case 2: return q.z;
-      default: return q.w;
+                                       const uint8_t* __restrict__ scales, size_t f, int lane) {
+    if constexpr (kFP8) {
+      c[0] = reinterpret_cast<const u32x4_t*>(codes + f * 2048)[lane];
+      c[1] = reinterpret_cast<const u32x4_t*>(codes + f * 2048 + 1024)[lane];
+      s = reinterpret_cast<const uint32_t*>(scales + f * 64)[lane & 15];
+    } else {
+      c[0] = reinterpret_cast<const u32x4_t*>(codes + f * 1024)[lane];
+      if constexpr (FMT == MOE_FMT_NVFP4)
+        s = reinterpret_cast<const uint16_t*>(scales + f * 128)[lane];
+      else
+        s = scales[f * 64 + lane];
     }
   }
 
-  // bf16 operand (8 elements) for MFMA i.
+  __device__ __forceinline__ static uint32_t word(const u32x4_t& q, int w) { return q[w]; }
+
+  // bf16 operand for MFMA i: elements 8i .. 8i+7 of the lane's 32.
   __device__ __forceinline__ bf16x8_t operand(int i) const {
     uint32_t o[4];
     if constexpr (FMT == MOE_FMT_MXFP4) {
-      const float sc = e8m0_to_f32((s >> (8 * (i >> 2))) & 0xff);
-      const uint32_t w = word(i);
+      const float sc = e8m0_to_f32(s & 0xff);
+      const uint32_t w = word(c[0], i);
       o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
       o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
       o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
       o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
     } else if constexpr (FMT == MOE_FMT_NVFP4) {
       const float sc = __builtin_amdgcn_cvt_f32_fp8((int)(s >> (8 * (i >> 1))), 0);
-      const uint32_t w = word(i);
+      const uint32_t w = word(c[0], i);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         float2 f;
@@ -121,7 +134,8 @@ struct WFrag {
         o[b] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // exact: low halves are zero
       }
     } else {
-      const uint32_t w0 = word(2 * i), w1 = word(2 * i + 1);
+      const u32x4_t& q = c[i >> 1];
+      const uint32_t w0 = word(q, 2 * (i & 1)), w1 = word(q, 2 * (i & 1) + 1);
       o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
       o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
       o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
@@ -130,153 +144,305 @@ struct WFrag {
     return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
   }
 
-  __device__ __forceinline__ float step_scale() const {  // FP8 block scale
-    return __uint_as_float(s);
-  }
+  __device__ __forceinline__ float step_scale() const { return __uint_as_float(s); }  // FP8
 };
 
-// A fragment for MFMA i: row m of the LDS tile, elements 64h + 8i .. +7.
-__device__ __forceinline__ bf16x8_t a_operand(const uint16_t* As, int row, int h, int i) {
-  return *reinterpret_cast<const bf16x8_t*>(As + row * LDA + 64 * h + 8 * i);
+struct TileArgs {
+  const uint8_t* blob;
+  BlobLayout L;
+  int K, N, k_top, a_by_token, ct, npass, row_base, rows;
+  const uint16_t* a_src;
+  const int32_t* pair_perm;
+  uint16_t* hout;
+  float* yout;
+};
+
+// Activation staging: thread -> rows tid/16 + 16j (j < NS), 16-byte chunk tid%16.
+// Row r's chunk c sits at slot c ^ (r & 15): sixteen lanes writing one row, or
+// reading one chunk of sixteen consecutive rows, touch sixteen distinct slots.
+template <int NS>
+__device__ __forceinline__ void a_load(u32x4_t (&av)[NS], const uint16_t* const (&arow)[NS], int s, int sc) {
+#pragma unroll
+  for (int j = 0; j < NS; ++j) av[j] = reinterpret_cast<const u32x4_t*>(arow[j] + s * BK)[sc];
+}
+
+template <int NS>
+__device__ __forceinline__ void a_store(const u32x4_t (&av)[NS], uint8_t* __restrict__ buf, int sr, int sc) {
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int r = sr + kFragRows * j;
+    *reinterpret_cast<u32x4_t*>(buf + r * ROWB + ((sc ^ (r & 15)) << 4)) = av[j];
+  }
+}
+
+template <int FMT, int NMAT>
+__device__ __forceinline__ void b_load(BFrag<FMT> (&dst)[NMAT][kCG<NMAT>], const uint8_t* const (&codes)[NMAT],
+                                       const uint8_t* const (&scales)[NMAT], int g0, int S, int s, int lane) {
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int cg = 0; cg < kCG<NMAT>; ++cg) dst[m][cg].load(codes[m], scales[m], (size_t)(g0 + cg) * S + s, lane);
+}
+
+// One step: MFMAs of every subtile against the step's weight fragments.
+// FP4: i outer, each dequantized operand feeds the NS subtiles at once.
+// FP8: per column group the step's operands are converted first, then subtile
+// by subtile a four-MFMA partial sum is scaled by the fragment's fp32 block
+// scale.
+template <int FMT, int NMAT, int NS>
+__device__ __forceinline__ void tile_step(floatx4_t (&acc)[NMAT][kCG<NMAT>][NS], const uint8_t* __restrict__ buf,
+                                          const BFrag<FMT> (&wf)[NMAT][kCG<NMAT>], int lane) {
+  const int am = lane & 15, aq = lane >> 4;
+  if constexpr (FMT != MOE_FMT_FP8_E4M3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x8_t b[NMAT][kCG<NMAT>];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int cg = 0; cg < kCG<NMAT>; ++cg) b[m][cg] = wf[m][cg].operand(i);
+      // row 16r + lane%16, chunk 4(lane/16) + i, swizzled by row & 15
+      const int slot = ((4 * aq + i) ^ am) << 4;
+#pragma unroll
+      for (int r = 0; r < NS; ++r) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(buf + (kFragRows * r + am) * ROWB + slot);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int cg = 0; cg < kCG<NMAT>; ++cg)
+            acc[m][cg][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[m][cg], acc[m][cg][r], 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int cg = 0; cg < kCG<NMAT>; ++cg) {
+      bf16x8_t b[4][NMAT];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) b[i][m] = wf[m][cg].operand(i);
+#pragma unroll
+      for (int r = 0; r < NS; ++r) {
+        floatx4_t part[NMAT];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) part[m] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = ((4 * aq + i) ^ am) << 4;
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(buf + (kFragRows * r + am) * ROWB + slot);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+            part[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[i][m], part[m], 0, 0, 0);
+        }
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const float sg = wf[m][cg].step_scale();
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[m][cg][r][v] = fmaf(sg, part[m][v], acc[m][cg][r][v]);
+        }
+      }
+    }
+  }
+}
+
+// Results of one column tile: lane holds column 16*g + lane%16 of each of its
+// groups, rows 16r + 4(lane/16) + v of the tile.
+template <int FMT, int NMAT, int NS>
+__device__ __forceinline__ void tile_epilogue(const TileArgs& t, const floatx4_t (&acc)[NMAT][kCG<NMAT>][NS], int g0,
+                                              int lane) {
+  const int am = lane & 15, aq = lane >> 4;
+  const float* tau = reinterpret_cast<const float*>(t.blob + t.L.tau);
+#pragma unroll
+  for (int cg = 0; cg < kCG<NMAT>; ++cg) {
+    const int col = (g0 + cg) * kFragRows + am;
+    if constexpr (NMAT == 2) {
+      const float tg = FMT == MOE_FMT_NVFP4 ? tau[0] : 1.0f, tu = FMT == MOE_FMT_NVFP4 ? tau[1] : 1.0f;
+#pragma unroll
+      for (int r = 0; r < NS; ++r)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = kFragRows * r + 4 * aq + v;
+          if (row < t.rows) {
+            const float gv = acc[0][cg][r][v] * tg, uv = acc[1][cg][r][v] * tu;
+            t.hout[(size_t)(t.row_base + row) * t.N + col] = f32_to_bf16_rne(silu_f32(gv) * uv);
+          }
+        }
+    } else {
+      const float td = FMT == MOE_FMT_NVFP4 ? tau[2] : 1.0f;
+#pragma unroll
+      for (int r = 0; r < NS; ++r)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = kFragRows * r + 4 * aq + v;
+          if (row < t.rows) t.yout[(size_t)t.pair_perm[t.row_base + row] * t.N + col] = acc[0][cg][r][v] * td;
+        }
+    }
+  }
+}
+
+template <int NMAT, int NS>
+__device__ __forceinline__ void zero_acc(floatx4_t (&acc)[NMAT][kCG<NMAT>][NS]) {
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int cg = 0; cg < kCG<NMAT>; ++cg)
+#pragma unroll
+      for (int r = 0; r < NS; ++r) acc[m][cg][r] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// One tile with NS 16-row subtiles (rows <= 16*NS).
+template <int FMT, int NMAT, int NS>
+__device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restrict__ As) {
+  constexpr int RB = kTileRows<FMT>;       // LDS rows per buffer
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = t.K / BK;
+
+  // weight fragments of this wave: column groups 2*(4ct + wave) + cg
+  const uint8_t* codes[NMAT];
+  const uint8_t* scales[NMAT];
+  codes[0] = t.blob + (NMAT == 2 ? t.L.cg : t.L.cd);
+  scales[0] = t.blob + (NMAT == 2 ? t.L.sg : t.L.sd);
+  if constexpr (NMAT == 2) {
+    codes[NMAT - 1] = t.blob + t.L.cu;
+    scales[NMAT - 1] = t.blob + t.L.su;
+  }
+
+  // activation staging rows (rows past the end repeat the last row; never stored)
+  const int sr = tid >> 4, sc = tid & 15;
+  const uint16_t* arow[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int p = t.row_base + min(sr + kFragRows * j, t.rows - 1);
+    arow[j] = t.a_by_token ? t.a_src + (size_t)(t.pair_perm[p] / t.k_top) * t.K : t.a_src + (size_t)p * t.K;
+  }
+  u32x4_t av[NS];
+  BFrag<FMT> wb0[NMAT][kCG<NMAT>], wb1[NMAT][kCG<NMAT>];
+  floatx4_t acc[NMAT][kCG<NMAT>][NS];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int cg = 0; cg < kCG<NMAT>; ++cg)
+#pragma unroll
+      for (int r = 0; r < NS; ++r) acc[m][cg][r] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // The workgroup sweeps npass column tiles (t.ct ...; npass = 1 for gate/up) of its row tile as one
+  // pipeline of U = npass * S steps; step u is k-step u % S of column tile
+  // t.ct + u / S.  Step u uses LDS buffer u&1 and weight registers wb(u&1);
+  // writing buffer u&1 is safe after the previous step's barrier, since its
+  // last reader was step u-2.  The activation tile does not depend on the
+  // column tile, so it is staged again (from L2) on each pass.
+  const int U = t.npass * S;
+  const int gw = wave * kCG<NMAT>;  // this wave's first group inside a column tile
+  uint8_t* buf0 = As;
+  uint8_t* buf1 = As + RB * ROWB;
+  a_load<NS>(av, arow, 0, sc);
+  b_load<FMT, NMAT>(wb0, codes, scales, t.ct * (kBN<NMAT> / kFragRows) + gw, S, 0, lane);
+  if (U > 1) b_load<FMT, NMAT>(wb1, codes, scales, (t.ct + 1 / S) * (kBN<NMAT> / kFragRows) + gw, S, 1 % S, lane);
+  for (int u = 0; u < U; u += 2) {
+    a_store<NS>(av, buf0, sr, sc);
+    if (u + 1 < U) a_load<NS>(av, arow, (u + 1) % S, sc);
+    __syncthreads();
+    tile_step<FMT, NMAT, NS>(acc, buf0, wb0, lane);
+    if (u + 2 < U)
+      b_load<FMT, NMAT>(wb0, codes, scales, (t.ct + (u + 2) / S) * (kBN<NMAT> / kFragRows) + gw, S, (u + 2) % S, lane);
+    if (u + 1 < U) {
+      a_store<NS>(av, buf1, sr, sc);
+      if (u + 2 < U) a_load<NS>(av, arow, (u + 2) % S, sc);
+      __syncthreads();
+      tile_step<FMT, NMAT, NS>(acc, buf1, wb1, lane);
+      if (u + 3 < U)
+        b_load<FMT, NMAT>(wb1, codes, scales, (t.ct + (u + 3) / S) * (kBN<NMAT> / kFragRows) + gw, S, (u + 3) % S, lane);
+      if constexpr (NMAT == 1) {  // sweeps (down only): S is even, a pass ends on the odd step
+        if ((u + 1) % S == S - 1) {
+          tile_epilogue<FMT, NMAT, NS>(t, acc, (t.ct + u / S) * (kBN<NMAT> / kFragRows) + gw, lane);
+          zero_acc<NMAT, NS>(acc);
+        }
+      }
+    }
+  }
+  if constexpr (NMAT == 2) tile_epilogue<FMT, NMAT, NS>(t, acc, t.ct * (kBN<NMAT> / kFragRows) + gw, lane);
 }
 
 // NMAT = 2: gate/up with SwiGLU into hout (expert-sorted rows, width N).
 // NMAT = 1: down into y rows of the original pairs.
 template <int FMT, int NMAT>
-__global__ __launch_bounds__(256) void k_grouped(
+__global__ __launch_bounds__(256, 2) void k_grouped(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int K, int N, int k_top,
     const uint16_t* __restrict__ a_src, int a_by_token, const int32_t* __restrict__ pair_perm,
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ tile_e,
-    const int32_t* __restrict__ tile_m0, const int32_t* __restrict__ n_tiles, int n_col_tiles,
+    const int32_t* __restrict__ tile_m0, const int32_t* __restrict__ n_tiles, int n_sweeps, int npass,
     uint16_t* __restrict__ hout, float* __restrict__ yout) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
-  // Workgroups are handed to the 8 XCDs round-robin by index; within each run of
-  // 8 * n_col_tiles indices, the column tiles of one row tile share an XCD (and
-  // its L2 copy of the gathered activation rows).
-  const int grp = blockIdx.x / (8 * n_col_tiles), r8 = blockIdx.x % (8 * n_col_tiles);
-  const int tile = grp * 8 + (r8 & 7), ct = r8 >> 3;
+  __shared__ __attribute__((aligned(16))) uint8_t As[2 * kTileRows<FMT> * ROWB];
+  // A workgroup takes one row tile and a sweep of npass consecutive column
+  // tiles.  Workgroups are handed to the 8 XCDs round-robin by index; within
+  // each run of 8 * n_sweeps indices, the sweeps of one row tile share an XCD
+  // (and its L2 copy of the gathered activation rows).
+  const int grp = blockIdx.x / (8 * n_sweeps), r8 = blockIdx.x % (8 * n_sweeps);
+  const int tile = grp * 8 + (r8 & 7);
   if (tile >= *n_tiles) return;
-  const int e = tile_e[tile], m0 = tile_m0[tile];
-  const int row_base = expert_off[e] + m0;
-  const int rows = min(BM, expert_off[e + 1] - row_base);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_lane = ct * BN + BNW * wave + (lane & 31), h = lane >> 5;
-  const uint8_t* blob = pool + (size_t)e * stride;
-  const uint8_t* codes0 = blob + (NMAT == 2 ? L.cg : L.cd);
-  const uint8_t* scales0 = blob + (NMAT == 2 ? L.sg : L.sd);
-
-  // A rows handled by this thread for LDS staging: row r = tid / 4, 32 columns each
-  const int ar = tid >> 2, ac = (tid & 3) * 32;
-  const uint16_t* arow = nullptr;
-  if (ar < rows) {
-    const int p = row_base + ar;
-    arow = a_by_token ? a_src + (size_t)(pair_perm[p] / k_top) * K : a_src + (size_t)p * K;
+  TileArgs t;
+  const int e = tile_e[tile];
+  t.row_base = expert_off[e] + tile_m0[tile];
+  t.rows = min(kTileRows<FMT>, expert_off[e + 1] - t.row_base);
+  t.blob = pool + (size_t)e * stride;
+  t.L = L;
+  t.K = K;
+  t.N = N;
+  t.k_top = k_top;
+  t.a_by_token = a_by_token;
+  t.ct = (r8 >> 3) * npass;
+  t.npass = npass;
+  t.a_src = a_src;
+  t.pair_perm = pair_perm;
+  t.hout = hout;
+  t.yout = yout;
+  switch ((t.rows + kFragRows - 1) / kFragRows) {
+    case 1: grouped_tile<FMT, NMAT, 1>(t, As); break;
+    case 2: grouped_tile<FMT, NMAT, 2>(t, As); break;
+    case 3: grouped_tile<FMT, NMAT, 3>(t, As); break;
+    case 4: grouped_tile<FMT, NMAT, 4>(t, As); break;
+    default:
+      if constexpr (kSubMax<FMT> >= 6) {
+        if (t.rows > 5 * kFragRows) grouped_tile<FMT, NMAT, 6>(t, As);
+        else grouped_tile<FMT, NMAT, 5>(t, As);
+      }
+      break;
   }
+}
 
-  floatx16_t acc[NMAT][2];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[m][s][v] = 0.0f;
+// Column tiles per workgroup: enough for about 16 k-steps in one pipeline,
+// a power of two that divides the column tile count.
+int sweep_len(int n_col_tiles, int S) {
+  int n = 1;
+  while (n * 2 * S <= 16 && n_col_tiles % (n * 2) == 0) n *= 2;
+  return n;
+}
 
-  // software pipeline: the next step's weights and activations are loaded into
-  // registers while the current step runs its MFMAs
-  WFrag<FMT> wf[NMAT];
-  uint4 av[4];
-  auto gload = [&](int kb) {
-    wf[0].load(codes0, scales0, K, n_lane, h, kb);
-    if constexpr (NMAT == 2) wf[1].load(blob + L.cu, blob + L.su, K, n_lane, h, kb);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      av[j] = arow ? reinterpret_cast<const uint4*>(arow + kb + ac)[j] : make_uint4(0, 0, 0, 0);
-  };
-  gload(0);
-  for (int kb = 0; kb < K; kb += BK) {
-    __syncthreads();  // previous step's LDS reads are done
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(As + ar * LDA + ac + 8 * j) = av[j];
-    __syncthreads();
-    WFrag<FMT> cur[NMAT];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) cur[m] = wf[m];
-    if (kb + BK < K) gload(kb + BK);
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      floatx16_t part[2];
-      const bool fp8 = FMT == MOE_FMT_FP8_E4M3;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) part[s][v] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16x8_t b = cur[m].operand(i);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8_t a = a_operand(As, 32 * s + (lane & 31), h, i);
-          if (fp8)
-            part[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, part[s], 0, 0, 0);
-          else
-            acc[m][s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m][s], 0, 0, 0);
-        }
-      }
-      if (fp8) {
-        const float sg = cur[m].step_scale();
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[m][s][v] = fmaf(sg, part[s][v], acc[m][s][v]);
-      }
-    }
-  }
-
-  // epilogue: lane holds column n_lane, rows 32s + 8(v/4) + 4h + v%4
-  const float* tau = reinterpret_cast<const float*>(blob + L.tau);
-  if constexpr (NMAT == 2) {
-    const float tg = FMT == MOE_FMT_NVFP4 ? tau[0] : 1.0f, tu = FMT == MOE_FMT_NVFP4 ? tau[1] : 1.0f;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 32 * s + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (r < rows) {
-          const float g = acc[0][s][v] * tg, u = acc[1][s][v] * tu;
-          hout[(size_t)(row_base + r) * N + n_lane] = f32_to_bf16_rne(silu_f32(g) * u);
-        }
-      }
-  } else {
-    const float td = FMT == MOE_FMT_NVFP4 ? tau[2] : 1.0f;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 32 * s + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (r < rows) yout[(size_t)pair_perm[row_base + r] * N + n_lane] = acc[0][s][v] * td;
-      }
-  }
+template <int FMT>
+int max_tiles_for(int n_pairs, int E) {
+  constexpr int RB = kTileRows<FMT>;
+  return ((n_pairs + RB - 1) / RB + E + 7) / 8 * 8;
 }
 
 template <int FMT>
 hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
   const int n_pairs = a.T * a.k;
-  const int max_tiles = ((n_pairs + BM - 1) / BM + a.E + 7) / 8 * 8;
+  const int max_tiles = max_tiles_for<FMT>(n_pairs, a.E);
   int32_t *tile_e = tiles, *tile_m0 = tiles + max_tiles, *n_tiles = tiles + 2 * max_tiles;
-  hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E, tile_e, tile_m0,
-                     n_tiles);
-  if (a.F % BN || a.H % BN || a.H % BK || a.F % BK) return hipErrorInvalidValue;
+  if (a.F % kBN<2> || a.H % kBN<1> || a.H % BK || a.F % BK) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E, kTileRows<FMT>, tile_e,
+                     tile_m0, n_tiles);
   // gate/up: A = x rows by token, K = H, N = F, h rows in expert order (hbuf)
-  const int nct_gu = a.F / BN;
-  hipLaunchKernelGGL((k_grouped<FMT, 2>), dim3(max_tiles * nct_gu), dim3(256), 0, s, a.pool,
+  const int nct_gu = a.F / kBN<2>, np_gu = 1;  // gate/up keeps its epilogue out of the loop
+  hipLaunchKernelGGL((k_grouped<FMT, 2>), dim3(max_tiles * (nct_gu / np_gu)), dim3(256), 0, s, a.pool,
                      a.stride, a.L, a.H, a.F, a.k, a.x, 1, a.pair_perm, a.expert_off, tile_e, tile_m0,
-                     n_tiles, nct_gu, a.hbuf, nullptr);
+                     n_tiles, nct_gu / np_gu, np_gu, a.hbuf, nullptr);
   // down: A = h rows in expert order, K = F, N = H, y rows of the pairs
   float* y = a.y ? a.y : a.ybuf;
-  const int nct_d = a.H / BN;
-  hipLaunchKernelGGL((k_grouped<FMT, 1>), dim3(max_tiles * nct_d), dim3(256), 0, s, a.pool, a.stride,
+  const int nct_d = a.H / kBN<1>, np_d = sweep_len(nct_d, a.F / BK);
+  hipLaunchKernelGGL((k_grouped<FMT, 1>), dim3(max_tiles * (nct_d / np_d)), dim3(256), 0, s, a.pool, a.stride,
                      a.L, a.F, a.H, a.k, a.hbuf, 0, a.pair_perm, a.expert_off, tile_e, tile_m0,
-                     n_tiles, nct_d, nullptr, y);
+                     n_tiles, nct_d / np_d, np_d, nullptr, y);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.out) return e;
   return launch_combine(y, a.topk_w, a.T, a.H, a.k, a.out, s);
@@ -285,7 +451,8 @@ hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
 }  // namespace
 
 size_t grouped_tiles_bytes(int T, int k, int E) {
-  const int max_tiles = ((T * k + BM - 1) / BM + E + 7) / 8 * 8;
+  // the FP4 formats use 128-row tiles and FP8 64-row tiles: size for the larger list
+  const int max_tiles = max_tiles_for<MOE_FMT_FP8_E4M3>(T * k, E);
   return align256((size_t)(2 * max_tiles + 1) * 4);
 }
 

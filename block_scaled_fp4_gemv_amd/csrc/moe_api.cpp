@@ -80,17 +80,42 @@ size_t moe_expert_bytes(int fmt, int H, int F) {
   return blob_layout(fmt, H, F).total;
 }
 
+// Canonical row-major matrix <-> fragment order (the blob geometry in common.h).
+// Every move is a whole 16-byte code chunk or a lane's scale bytes, so the two
+// directions are exact inverses.
+static void shuffle_matrix(int fmt, int N, int K, uint8_t* canon_codes, uint8_t* canon_scales,
+                           uint8_t* codes, uint8_t* scales, bool to_blob) {
+  const int S = K / kFragK;
+  auto mv = [to_blob](uint8_t* blob_p, uint8_t* canon_p, size_t n) {
+    if (to_blob) memcpy(blob_p, canon_p, n);
+    else memcpy(canon_p, blob_p, n);
+  };
+  for (int n = 0; n < N; ++n) {
+    const int g = n / kFragRows, r = n % kFragRows;
+    for (int s = 0; s < S; ++s) {
+      const size_t f = (size_t)g * S + s;
+      for (int q = 0; q < 4; ++q) {
+        const int l = q * 16 + r, k0 = s * kFragK + 32 * q;  // lane and its first element
+        if (fmt == MOE_FMT_FP8_E4M3) {
+          for (int p = 0; p < 2; ++p)
+            mv(codes + f * 2048 + p * 1024 + l * 16, canon_codes + (size_t)n * K + k0 + 16 * p, 16);
+        } else {
+          mv(codes + f * 1024 + l * 16, canon_codes + (size_t)n * (K / 2) + k0 / 2, 16);
+        }
+        if (fmt == MOE_FMT_NVFP4) mv(scales + f * 128 + l * 2, canon_scales + (size_t)n * (K / 16) + k0 / 16, 2);
+        if (fmt == MOE_FMT_MXFP4) mv(scales + f * 64 + l, canon_scales + (size_t)n * (K / 32) + k0 / 32, 1);
+      }
+      if (fmt == MOE_FMT_FP8_E4M3) mv(scales + f * 64 + r * 4, canon_scales + ((size_t)n * S + s) * 4, 4);
+    }
+  }
+}
+
 static void copy_sections(int fmt, int H, int F, const BlobLayout& L, uint8_t* blob,
                           void* const canon[9], bool to_blob) {
-  const size_t off[6] = {L.cg, L.cu, L.cd, L.sg, L.su, L.sd};
-  const size_t len[6] = {code_bytes(fmt, F, H), code_bytes(fmt, F, H), code_bytes(fmt, H, F),
-                         scale_bytes(fmt, F, H), scale_bytes(fmt, F, H), scale_bytes(fmt, H, F)};
-  for (int i = 0; i < 6; ++i) {
-    if (to_blob)
-      memcpy(blob + off[i], canon[i], len[i]);
-    else
-      memcpy(canon[i], blob + off[i], len[i]);
-  }
+  auto c = [&](int i) { return static_cast<uint8_t*>(canon[i]); };
+  shuffle_matrix(fmt, F, H, c(0), c(3), blob + L.cg, blob + L.sg, to_blob);
+  shuffle_matrix(fmt, F, H, c(1), c(4), blob + L.cu, blob + L.su, to_blob);
+  shuffle_matrix(fmt, H, F, c(2), c(5), blob + L.cd, blob + L.sd, to_blob);
   float* tau = reinterpret_cast<float*>(blob + L.tau);
   for (int i = 0; i < 3; ++i) {
     if (to_blob) {

@@ -90,9 +90,17 @@ int moe_abi_version(void);
 /* Bytes of one packed expert blob (gate, up, down with their scales and tensor
  * scales) for the given format and shape; 0 if the format or shape is invalid.
  * A blob holds, each section starting on a 256-byte boundary:
- *   gate codes [F][H*b], up codes [F][H*b], down codes [H][F*b]   (b = 1/2 FP4, 1 FP8)
- *   gate scales, up scales, down scales in the canonical layout below,
+ *   gate codes, up codes, down codes, gate scales, up scales, down scales,
  *   tau[3] (fp32; 1.0 for MXFP4/FP8).
+ * Each matrix [N][K] is pre-shuffled into fragments of 16 rows x 128 k
+ * (N/16 row groups x K/128 steps, group-major).  Lane l of a wavefront owns row
+ * 16g + l%16, elements 128s + 32(l/16) .. +31 of fragment (g, s):
+ *   FP4 codes 1 KiB per fragment, lane l's 16 bytes at 16l (low nibble = lower k);
+ *   FP8 codes 2 KiB, two pieces of 64 x 16 bytes (elements 0-15, 16-31 of a lane);
+ *   NVFP4 scales 2 bytes per lane (128 B), MXFP4 1 byte (64 B), FP8 one float
+ *   per row of the fragment (64 B).
+ * Code and scale sections have the canonical sizes; use moe_pack_expert /
+ * moe_unpack_expert to convert.
  * The slot pool and the host pool hold blobs at a caller-chosen stride that is
  * >= moe_expert_bytes and a multiple of 256. */
 size_t moe_expert_bytes(int fmt, int H, int F);

@@ -66,8 +66,38 @@ def test_pack_unpack_round_trip(fmt):
         assert (back["tau_g"], back["tau_u"], back["tau_d"]) == (canon["tau_g"], canon["tau_u"], canon["tau_d"])
     else:
         assert back["tau_g"] == 1.0
-    # sections sit where the header says: gate codes first, 256-aligned sections
-    assert np.array_equal(blob[:canon["codes_g"].size], canon["codes_g"].ravel())
+    # every section holds the fragment order the header documents, 256-aligned
+    assert np.array_equal(blob, _documented_blob(fmt, H, F, canon))
+
+
+def _frag_order(fmt, a, is_scale):
+    """Canonical [N][...] array -> bytes in the documented fragment order: row
+    groups of 16, steps of 128 k, lane l = 16*q + r owning k 32q..32q+31 of the step."""
+    N = a.shape[0]
+    if not is_scale:
+        if fmt == 3:   # bytes k = 128s + 32q + 16p + j -> [g][s][p][q][r][j]
+            v = a.reshape(N // 16, 16, -1, 4, 2, 16).transpose(0, 2, 4, 3, 1, 5)
+        else:          # bytes 64s + 16q + j -> [g][s][q][r][j]
+            v = a.reshape(N // 16, 16, -1, 4, 16).transpose(0, 2, 3, 1, 4)
+    elif fmt == 1:     # scale 8s + 2q + b -> [g][s][q][r][b]
+        v = a.reshape(N // 16, 16, -1, 4, 2).transpose(0, 2, 3, 1, 4)
+    elif fmt == 2:     # scale 4s + q -> [g][s][q][r]
+        v = a.reshape(N // 16, 16, -1, 4).transpose(0, 2, 3, 1)
+    else:              # fp32 scale s -> [g][s][r]
+        v = a.reshape(N // 16, 16, -1).transpose(0, 2, 1)
+    return np.ascontiguousarray(v).view(np.uint8).ravel()
+
+
+def _documented_blob(fmt, H, F, canon):
+    out = np.zeros(B.moe_expert_bytes(fmt, H, F), np.uint8)
+    pos = 0
+    for key in ("codes_g", "codes_u", "codes_d", "scales_g", "scales_u", "scales_d"):
+        b = _frag_order(fmt, np.asarray(canon[key]), key.startswith("scales"))
+        out[pos:pos + b.size] = b
+        pos = (pos + b.size + 255) // 256 * 256
+    tau = [canon["tau_g"], canon["tau_u"], canon["tau_d"]] if fmt == 1 else [1.0, 1.0, 1.0]
+    out[pos:pos + 12] = np.asarray(tau, np.float32).view(np.uint8)
+    return out
 
 
 def test_pack_rejects_null():

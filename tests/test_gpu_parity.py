@@ -272,6 +272,26 @@ def test_cache_mode_bitwise_equals_resident_mode():
     assert 0 < hits < xs.shape[0] * k
 
 
+@pytest.mark.parametrize("fmt", [NV, MX])
+def test_decode_wide_experts_combine_fallback(fmt):
+    """Width 8192 with top-8: the k rows of h (k*F*2 bytes) exceed the fused
+    down+combine kernel's LDS, so down runs alone and the combine follows."""
+    H, E, F, k = 256, 8, 8192, 8
+    L = Layer(fmt, H, E, F, cfg=46, layer=0, w_std=0.02)
+    x = iid_tokens(0, 46, 2, H, [L.router], k)
+    pool, R = L.device()
+    idx, w, out = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, _x_dev(x), R)
+    y = torch.empty((2 * k, H), dtype=torch.float32, device="cuda")
+    out2 = torch.empty((2, H), dtype=torch.uint16, device="cuda")
+    B.moe_expert_ffn(fmt, pool, L.stride, H, F, E, _x_dev(x), idx, topk_w=w, y=y, out=out2)
+    torch.cuda.synchronize()
+    _check_route(x, L.router, k, idx, w)
+    ref = moe.moe_layer(fmt, x, L.router, L.experts, k)
+    assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
+    assert_rows_close(y.cpu().numpy(), ref["y"].reshape(-1, H), what="y")
+    assert torch.equal(out, out2)
+
+
 def test_determinism():
     fmt, H, E, F, k = NV, 2048, 256, 512, 8
     L = Layer(fmt, H, E, F, cfg=1, layer=5, w_std=0.02, eager=False)
@@ -346,6 +366,14 @@ def test_grouped_tiny_mxfp4():
 @pytest.mark.parametrize("fmt,T", [(NV, 512), (MX, 256), (F8, 256)])
 def test_grouped_35b_shape(fmt, T):
     _grouped_case(fmt, 2048, 256, 512, 8, T, cfg=41 + fmt)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX, F8])
+def test_grouped_many_rows_per_expert(fmt):
+    """About 128 rows per expert: several row tiles per expert (96-row FP4
+    tiles, 32-row FP8 tiles), odd subtile counts, and down workgroups that
+    sweep two column tiles (hidden 512 = 4 column tiles, width 1024 = 8 steps)."""
+    _grouped_case(fmt, 512, 16, 1024, 4, 512, cfg=45, sample=96)
 
 
 def test_grouped_ragged_tiles():
