@@ -40,6 +40,10 @@ def parse():
     p.add_argument("--prefill", default="prefill35b", choices=["prefill35b", "prefill753b", "none"],
                    help="prefill workload timed alongside the decode headline")
     p.add_argument("--prefill-reps", type=int, default=20)
+    p.add_argument("--cache", default="cache35b", choices=["cache35b", "none"],
+                   help="cache-constrained decode timed on the same layers (VRAM slot pools + pinned host pools)")
+    p.add_argument("--cache-warmup", type=int, default=64)
+    p.add_argument("--cache-steps", type=int, default=128)
     p.add_argument("--fmt", type=int, default=0, help="override weight format (1 NVFP4, 2 MXFP4, 3 FP8)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (testing only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -51,9 +55,9 @@ def parse():
     return p.parse_args()
 
 
-def build_stack(wl, fmt, n_layers, threads):
-    """Generate, quantize, pack and upload every layer; returns device pools and routers."""
-    import numpy as np
+def build_stack(wl, fmt, n_layers, threads, keep_host=False):
+    """Generate, quantize, pack and upload every layer; returns device pools, routers,
+    the blob stride and (keep_host) the pinned host copy of every layer."""
     import torch
 
     from block_scaled_fp4_gemv_amd import binding as B
@@ -61,19 +65,77 @@ def build_stack(wl, fmt, n_layers, threads):
 
     sy.set_threads(threads)
     stride = B.blob_stride(fmt, wl.H, wl.F)
-    pools, routers = [], []
-    host = np.empty(wl.E * stride, np.uint8)
+    pools, routers, hosts = [], [], []
+    host = torch.empty(wl.E * stride, dtype=torch.uint8).pin_memory()
     t0 = time.time()
     for l in range(n_layers):
-        batch = sy.experts(fmt, 0, wl.cfg_id, l, 0, wl.E, wl.H, wl.F, wl.w_std)
-        B.pack_layer(fmt, wl.H, wl.F, batch, host, stride)
+        batch = sy.experts(fmt, 0, wl.wcfg, l, 0, wl.E, wl.H, wl.F, wl.w_std)
+        if keep_host and l > 0:
+            host = torch.empty(wl.E * stride, dtype=torch.uint8).pin_memory()
+        B.pack_layer(fmt, wl.H, wl.F, batch, host.numpy(), stride, threads=threads)
         del batch
-        pools.append(torch.from_numpy(host).cuda())
-        routers.append(torch.from_numpy(sy.router(0, wl.cfg_id, l, wl.E, wl.H)).cuda())
+        pools.append(host.cuda())
+        if keep_host:
+            hosts.append(host)
+        routers.append(torch.from_numpy(sy.router(0, wl.wcfg, l, wl.E, wl.H)).cuda())
         if l % 4 == 3 or l == n_layers - 1:
             log(f"layer {l + 1}/{n_layers} generated ({time.time() - t0:.0f} s)")
     torch.cuda.synchronize()
-    return pools, routers, stride
+    return pools, routers, stride, hosts
+
+
+def cache_leg(name, fmt, hosts, routers, stride, warmup, steps):
+    """Cache-constrained decode: each layer keeps S of its E experts in a VRAM slot
+    pool; every step runs moe_cached_layer_forward per layer (router, LRU lookup,
+    host wait on the miss record, H2D fill of the misses on a side stream
+    overlapped with the hits, misses, combine)."""
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_gemv_amd import binding as B
+    from block_scaled_fp4_gemv_amd import synth as sy
+
+    wl = sy.WORKLOADS[name]
+    H, E, F, k, S = wl.H, wl.E, wl.F, wl.k, wl.slots
+    n_layers = len(hosts)
+    layers = [B.CachedLayer(routers[l], hosts[l], torch.zeros(S * stride, dtype=torch.uint8, device="cuda"),
+                            E, S, 1, k) for l in range(n_layers)]
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    xs = torch.from_numpy(sy.ar1_sequence(0, wl.cfg_id, warmup + steps, H)).cuda()
+    idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    pair_slot = torch.empty(k, dtype=torch.int32, device="cuda")
+    pair_order = torch.empty(k, dtype=torch.int32, device="cuda")
+    out = torch.empty((1, H), dtype=torch.uint16, device="cuda")
+    copy = torch.cuda.Stream()
+    eb = B.moe_expert_bytes(fmt, H, F)
+
+    def step(t):
+        hm = np.zeros(2, np.int64)
+        x = xs[t:t + 1]
+        for L in layers:
+            h, m = B.moe_cached_layer_forward(fmt, stride, H, F, E, k, L, x, idx, w, pair_slot, pair_order,
+                                              out, ws, copy_stream=copy)
+            hm += (h, m)
+        return hm
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    tot = np.zeros(2, np.int64)
+    t0 = time.perf_counter()
+    for t in range(warmup, warmup + steps):
+        tot += step(t)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    acc = steps * n_layers * k
+    return {"workload": f"{name}: {n_layers} layers, hidden {H}, {E} experts, top-{k}, width {F}, "
+                        f"{S} VRAM slots per layer, batch 1, pinned host pool",
+            "tokens_per_s": round(steps / dt, 2), "ms_per_step": round(dt / steps * 1e3, 3),
+            "warmup_steps": warmup, "timed_steps": steps, "hit_rate": round(float(tot[0]) / acc, 4),
+            "misses_per_token": round(float(tot[1]) / steps, 2),
+            "h2d_GBps": round(float(tot[1]) * eb / dt / 1e9, 2), "expert_blob_bytes": eb,
+            "timing": "host wall clock over the timed steps (the executor waits on each layer's lookup)"}
 
 
 def algorithmic_bytes(wl, fmt):
@@ -104,18 +166,28 @@ def prefill_leg(name, fmt_override, reps, threads):
     H, E, F, k, T = wl.H, wl.E, wl.F, wl.k, wl.T
     sy.set_threads(threads)
     stride = B.blob_stride(fmt, H, F)
-    host = np.empty(E * stride, np.uint8)
-    B.pack_layer(fmt, H, F, sy.experts(fmt, 0, wl.cfg_id, 0, 0, E, H, F, wl.w_std), host, stride)
-    pool = torch.from_numpy(host).cuda()
-    del host
-    R = torch.from_numpy(sy.router(0, wl.cfg_id, 0, E, H)).cuda()
+    # two layers used alternately, so that more than twice the 256 MB MALL is
+    # touched between reuses of a weight set
+    pools, Rs = [], []
+    for l in range(2):
+        host = np.empty(E * stride, np.uint8)
+        B.pack_layer(fmt, H, F, sy.experts(fmt, 0, wl.wcfg, l, 0, E, H, F, wl.w_std), host, stride,
+                     threads=threads)
+        pools.append(torch.from_numpy(host).cuda())
+        Rs.append(torch.from_numpy(sy.router(0, wl.wcfg, l, E, H)).cuda())
+        del host
     x = torch.from_numpy(sy.token_rows(0, wl.cfg_id, T, H)).cuda()
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     out = torch.empty((T, H), dtype=torch.uint16, device="cuda")
     ws = B.new_layer_workspace(fmt, T, H, F, k, E)
-    run = lambda: B.moe_layer_forward(fmt, pool, stride, H, F, E, k, x, R, topk_idx=idx, topk_w=w,  # noqa: E731
-                                      out=out, ws=ws)
+    rep = [0]
+
+    def run():
+        l = rep[0] % 2
+        rep[0] += 1
+        B.moe_layer_forward(fmt, pools[l], stride, H, F, E, k, x, Rs[l], topk_idx=idx, topk_w=w, out=out, ws=ws)
+
     for _ in range(3):
         run()
     torch.cuda.synchronize()
@@ -140,7 +212,7 @@ def prefill_leg(name, fmt_override, reps, threads):
             "tokens_per_s": round(T / t, 1), "layer_us": round(us, 2), "experts_used": used,
             "algorithmic_bytes": bytes_alg, "hbm_GBps": round(bytes_alg / t / 1e9, 1),
             "hbm_frac": round(hbm_frac, 4), "expert_mfma_tflops": round(mf, 2),
-            "mfma_instruction": "v_mfma_f32_32x32x16_bf16 (weights dequantized in registers)",
+            "mfma_instruction": "v_mfma_f32_16x16x32_bf16 (weights dequantized in registers)",
             "mfma_util_vs_bf16_peak": round(mf / MFMA_PEAK_TFLOPS["bf16"], 4),
             "mfma_util_vs_fp4_peak": round(mf / MFMA_PEAK_TFLOPS["fp4"], 4),
             "roofline_frac": round(max(hbm_frac, flops_mfma / (MFMA_PEAK_TFLOPS["bf16"] * 1e12) / t), 4),
@@ -183,11 +255,11 @@ def cpu_baseline(wl, fmt, xs, n_steps, n_layers):
 
         def __getitem__(self, e):
             if e not in self.c:
-                b = sy.experts(fmt, 0, wl.cfg_id, self.l, e, 1, wl.H, wl.F, wl.w_std)
+                b = sy.experts(fmt, 0, wl.wcfg, self.l, e, 1, wl.H, wl.F, wl.w_std)
                 self.c[e] = sy.expert_view(b, 0)
             return self.c[e]
 
-    layers = [(sy.router(0, wl.cfg_id, l, wl.E, wl.H), Lazy(l)) for l in range(n_layers)]
+    layers = [(sy.router(0, wl.wcfg, l, wl.E, wl.H), Lazy(l)) for l in range(n_layers)]
     # weights are generated outside the timed region (the GPU leg also starts resident)
     for t in range(n_steps):
         for R, ex in layers:
@@ -223,7 +295,8 @@ def main():
     B.lib()
     torch.cuda.init()
     log(f"workload {wl.name}: {n_layers} layers H={wl.H} E={wl.E} k={wl.k} F={wl.F} fmt={fmt}")
-    pools, routers, stride = build_stack(wl, fmt, n_layers, args.threads)
+    want_cache = args.cache != "none" and wl.name == "decode35b"
+    pools, routers, stride, hosts = build_stack(wl, fmt, n_layers, args.threads, keep_host=want_cache)
     H, E, F, k = wl.H, wl.E, wl.F, wl.k
 
     n_states = wl.steps
@@ -319,6 +392,12 @@ def main():
                      "bytes_per_launch": nb["layer_total"], "avg_launch_us": round(layer_us, 3),
                      "launch_timing": "timed graph replays / (steps x layers), HIP events"},
     }
+    if want_cache:
+        log(f"cache leg {args.cache} ...")
+        res["cache"] = cache_leg(args.cache, fmt, hosts, routers, stride, args.cache_warmup, args.cache_steps)
+        log(f"cache: {res['cache']['tokens_per_s']} tok/s, hit rate {res['cache']['hit_rate']}, "
+            f"{res['cache']['h2d_GBps']} GB/s H2D")
+        del hosts
     if args.prefill != "none":
         log(f"prefill leg {args.prefill} ...")
         del pools

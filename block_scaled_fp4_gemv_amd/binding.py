@@ -28,6 +28,11 @@ class moe_lru(ctypes.Structure):
                 ("expert_slot", _vp), ("slot_stamp", _vp), ("clock", _vp)]
 
 
+class moe_cached_layer(ctypes.Structure):
+    _fields_ = [("router", _vp), ("host_pool", _vp), ("slot_pool", _vp), ("lru", moe_lru),
+                ("miss_rec", _vp), ("lookup_done", _vp), ("slots_free", _vp), ("fill_done", _vp)]
+
+
 SIGNATURES = {
     "moe_status_str": (ctypes.c_char_p, [_i32]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -48,6 +53,11 @@ SIGNATURES = {
     "moe_layer_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_layer_forward": (_i32, [_i32, _vp, _sz, _i32, _i32, _i32, _i32, _u32, _vp, _i32, _vp, _vp, _vp,
                                  _vp, _vp, _sz, _vp]),
+    "moe_cached_layer_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "moe_cached_layer_forward": (_i32, [_i32, _sz, _i32, _i32, _i32, _i32, _u32,
+                                        ctypes.POINTER(moe_cached_layer), _vp, _i32, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _sz, _vp, _vp, ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_int32)]),
 }
 
 _lib = None
@@ -308,3 +318,42 @@ def moe_layer_forward(fmt, pool, stride, H, F, E, k, x, router, flags=0, topk_id
                                  _stream(stream))
     _check(st, "moe_layer_forward")
     return topk_idx, topk_w, out
+
+
+# ----------------------------------------------------------- cached layer
+
+def moe_cached_layer_workspace(fmt, T, H, F, k, E):
+    return int(lib().moe_cached_layer_workspace(fmt, T, H, F, k, E))
+
+
+class CachedLayer:
+    """One layer's VRAM expert cache for moe_cached_layer_forward: router (device),
+    host pool ([pinned] uint8 tensor of E blobs), slot pool (device, S blobs), LRU
+    state, a pinned miss record and three events (created here)."""
+
+    def __init__(self, router, host_pool, slot_pool, E, S, T, k):
+        import torch
+        self.router, self.host_pool, self.slot_pool = router, host_pool, slot_pool
+        self.lru = LRUState(E, S, router.device)
+        moe_lru_reset(self.lru)
+        self.miss_rec = torch.zeros(moe_miss_record_words(T, k, S), dtype=torch.int32).pin_memory()
+        self.lookup_done, self.slots_free, self.fill_done = (torch.cuda.Event() for _ in range(3))
+        for ev in (self.lookup_done, self.slots_free, self.fill_done):
+            ev.record()  # creates the underlying HIP event
+        torch.cuda.current_stream().synchronize()
+        self.c = moe_cached_layer(_ptr(router), _ptr(host_pool), _ptr(slot_pool), self.lru.c(),
+                                  _ptr(self.miss_rec), self.lookup_done.cuda_event, self.slots_free.cuda_event,
+                                  self.fill_done.cuda_event)
+
+
+def moe_cached_layer_forward(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w, pair_slot, pair_order, out,
+                             ws, flags=0, stream=None, copy_stream=None):
+    """Returns (n_hits, n_miss) of the step; raises MoeError on MOE_E_CAPACITY."""
+    T = x.shape[0]
+    hits, miss = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = lib().moe_cached_layer_forward(fmt, stride, H, F, E, k, flags, ctypes.byref(layer.c), _ptr(x), T,
+                                        _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
+                                        _ptr(out), _ptr(ws), ws.numel(), _stream(stream),
+                                        _stream(copy_stream), ctypes.byref(hits), ctypes.byref(miss))
+    _check(st, "moe_cached_layer_forward")
+    return hits.value, miss.value

@@ -384,3 +384,71 @@ int moe_combine(const float* y, const float* topk_w, int T, int H, int k, uint16
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------- cached layer executor
+
+size_t moe_cached_layer_workspace(int fmt, int T, int H, int F, int k, int E) {
+  const size_t ffn = moe_ffn_workspace(fmt, T, H, F, k, E), route = moe_route_workspace(T, H, E, k);
+  if (!ffn || !route) return 0;
+  return align256((size_t)T * k * H * 4) + align256(route) + ffn;
+}
+
+int moe_cached_layer_forward(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                             const moe_cached_layer* L, const uint16_t* x, int T, int32_t* topk_idx,
+                             float* topk_w, int32_t* pair_slot, int32_t* pair_order, uint16_t* out,
+                             void* ws, size_t ws_bytes, moe_stream_t stream, moe_stream_t copy_stream,
+                             int32_t* n_hits, int32_t* n_miss) {
+  g_err[0] = 0;
+  if (!L || !L->router || !L->host_pool || !L->slot_pool || !L->miss_rec || !L->lookup_done)
+    return fail(MOE_E_ARG, "incomplete moe_cached_layer");
+  const size_t need = moe_cached_layer_workspace(fmt, T, H, F, k, E);
+  if (!need) return fail(MOE_E_ARG, "bad shape or format");
+  if (!ws || !aligned(ws, 256) || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "cached layer workspace needs %zu bytes, 256-aligned", need);
+  if (T == 0) return MOE_OK;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  float* y = reinterpret_cast<float*>(p);
+  p += align256((size_t)T * k * H * 4);
+  const size_t route_bytes = moe_route_workspace(T, H, E, k);
+  void* route_ws = p;
+  p += align256(route_bytes);
+  void* ffn_ws = p;
+  const size_t ffn_bytes = moe_ffn_workspace(fmt, T, H, F, k, E);
+  int st = moe_route(x, L->router, T, H, E, k, route_flags, topk_idx, topk_w, nullptr, nullptr, route_ws,
+                     route_bytes, stream);
+  if (st) return st;
+  st = moe_cache_lookup(&L->lru, topk_idx, T, k, pair_slot, pair_order, L->miss_rec, stream);
+  if (st) return st;
+  hipEvent_t lk = static_cast<hipEvent_t>(L->lookup_done);
+  hipError_t e = hipEventRecord(lk, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipEventSynchronize(lk);
+  if (e != hipSuccess) return hip_fail(e, "lookup event");
+  const int32_t* rec = L->miss_rec;
+  if (n_hits) *n_hits = rec[3];
+  if (n_miss) *n_miss = rec[1];
+  if (rec[0] != MOE_OK) return fail(MOE_E_CAPACITY, "layer cache: %d misses exceed the evictable slots", rec[1]);
+  const size_t eb = moe_expert_bytes(fmt, H, F);
+  st = moe_cache_fill(rec, L->host_pool, L->slot_pool, eb, stride, L->slots_free, copy_stream, L->fill_done);
+  if (st) return st;
+  const int n_pairs = T * k, n_hit = rec[2];
+  if (n_hit > 0) {
+    st = moe_expert_ffn(fmt, L->slot_pool, stride, H, F, E, x, T, k, topk_idx, pair_slot, nullptr, nullptr,
+                        pair_order, n_hit, nullptr, y, nullptr, MOE_FFN_GEMV, ffn_ws, ffn_bytes, stream);
+    if (st) return st;
+  }
+  if (L->fill_done) {
+    e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(L->fill_done), 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(fill_done)");
+  }
+  if (n_hit < n_pairs) {
+    st = moe_expert_ffn(fmt, L->slot_pool, stride, H, F, E, x, T, k, topk_idx, pair_slot, nullptr, nullptr,
+                        pair_order + n_hit, n_pairs - n_hit, nullptr, y, nullptr, MOE_FFN_GEMV, ffn_ws,
+                        ffn_bytes, stream);
+    if (st) return st;
+  }
+  if (L->slots_free) {
+    e = hipEventRecord(static_cast<hipEvent_t>(L->slots_free), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(slots_free)");
+  }
+  return moe_combine(y, topk_w, T, H, k, out, stream);
+}

@@ -26,6 +26,11 @@ class Workload:
     x_kind: str = "iid"      # "iid" bf16 N(0,1) rows, or "ar1" decode states
     slots: int = 0           # VRAM slots per layer (0 = all experts resident)
     fmts: tuple = field(default_factory=tuple)
+    weights_cfg: int = -1    # seed group of the weights (-1 = cfg_id)
+
+    @property
+    def wcfg(self):
+        return self.cfg_id if self.weights_cfg < 0 else self.weights_cfg
 
     @property
     def label(self):
@@ -42,9 +47,10 @@ WORKLOADS = {
     # 35B-A3B-like prefill: 2048 tokens through one layer
     "prefill35b": Workload("prefill35b", 2, H=2048, E=256, k=8, F=512, layers=1, fmt=1, T=2048,
                            steps=1, w_std=0.02),
-    # cache-constrained decode: 64 of 256 experts per layer in VRAM
+    # cache-constrained decode: the decode35b layers (same weights), 64 of 256
+    # experts per layer in VRAM, the rest in pinned host memory; own AR(1) states
     "cache35b": Workload("cache35b", 3, H=2048, E=256, k=8, F=512, layers=40, fmt=1, T=1,
-                         steps=512, w_std=0.02, x_kind="ar1", slots=64),
+                         steps=512, w_std=0.02, x_kind="ar1", slots=64, weights_cfg=1),
     # 753B-class layer stack: decode and 4096-token prefill, three formats
     "decode753b": Workload("decode753b", 4, H=6144, E=256, k=8, F=2048, layers=8, fmt=1, T=1,
                            steps=128, w_std=0.015, x_kind="ar1", fmts=(1, 2, 3)),

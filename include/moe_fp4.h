@@ -255,6 +255,51 @@ int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, in
                       int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
                       moe_stream_t stream);
 
+/* ------------------------------------------- cached layer (host executor) */
+
+/* One layer's VRAM expert cache, caller-owned: the router, the pinned host
+ * pool holding all E blobs, the device slot pool of S blobs, the LRU state over
+ * it, a [pinned] miss record (moe_miss_record_words(T, k, S) words) and three
+ * events (created by the caller; slots_free may start unrecorded). */
+typedef struct moe_cached_layer {
+  const float* router;     /* float [E][H] */
+  const void* host_pool;   /* [pinned] E blobs at stride */
+  void* slot_pool;         /* S blobs at stride */
+  moe_lru lru;             /* LRU state over the S slots (lru.S = S) */
+  int32_t* miss_rec;       /* [pinned] miss record */
+  moe_event_t lookup_done; /* recorded after the lookup; the host waits on it */
+  moe_event_t slots_free;  /* recorded after the last kernel that reads the slots */
+  moe_event_t fill_done;   /* recorded on copy_stream after the fill */
+} moe_cached_layer;
+
+/* Workspace bytes for moe_cached_layer_forward (device, 256-byte aligned). */
+size_t moe_cached_layer_workspace(int fmt, int T, int H, int F, int k, int E);
+
+/* The layer with its experts served from the layer's VRAM slot cache, misses
+ * filled from pinned host memory on a side stream and overlapped with the
+ * hits (page "8GB 笔记本 39.3 tok/s、单卡跑 753B：FreeToken 把 frontier MoE 拉回
+ * 本地", section "设计核心"; page "753B...", section "按带宽动态分配参数存储").
+ * It calls the entry points above in this order:
+ *   moe_route (no permutation) -> moe_cache_lookup -> record lookup_done and
+ *   wait for it on the host -> moe_cache_fill on copy_stream (waits
+ *   slots_free, records fill_done) -> moe_expert_ffn on the pairs that hit
+ *   (GEMV path, pair_subset = the first n_hit_pairs of pair_order) -> `stream`
+ *   waits fill_done -> moe_expert_ffn on the remaining pairs -> slots_free
+ *   recorded on `stream` -> moe_combine.
+ * Every pair uses the same kernels as the all-resident path, so `out` equals
+ * moe_expert_ffn + moe_combine on a pool holding every expert, bit for bit.
+ *   x bf16 [T][H]; topk_idx int32 [T][k], topk_w float [T][k], pair_slot and
+ *   pair_order int32 [T*k] (outputs, device); out bf16 [T][H].
+ *   n_hits, n_miss: [host] optional, receive miss_rec[3] and miss_rec[1].
+ * Blocks the calling thread until this layer's lookup has run.  Returns
+ * MOE_E_CAPACITY (state unchanged, nothing computed after the lookup) when a
+ * step needs more victims than evictable slots. */
+int moe_cached_layer_forward(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                             const moe_cached_layer* layer, const uint16_t* x, int T,
+                             int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
+                             uint16_t* out, void* ws, size_t ws_bytes, moe_stream_t stream,
+                             moe_stream_t copy_stream, int32_t* n_hits, int32_t* n_miss);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,3 +165,23 @@ def test_cache_fill_refuses_capacity_record():
     assert L.moe_cache_fill(rec.ctypes.data, 0x1000, 0x1000, 256, 256, None, None, None) == B.MOE_E_CAPACITY
     rec_bad = np.array([0, 5, 0, 0, 2, 0, 0, 0, 0], np.int32)   # n_miss > n_max
     assert L.moe_cache_fill(rec_bad.ctypes.data, 0x1000, 0x1000, 256, 256, None, None, None) == B.MOE_E_ARG
+
+
+def test_cached_layer_argument_errors_before_any_hip_call():
+    L = B.lib()
+    fmt, H, F, E, k, T = 1, 2048, 512, 256, 8, 1
+    need = B.moe_cached_layer_workspace(fmt, T, H, F, k, E)
+    y = (T * k * H * 4 + 255) // 256 * 256
+    assert need == y + (B.moe_route_workspace(T, H, E, k) + 255) // 256 * 256 + \
+        B.lib().moe_ffn_workspace(fmt, T, H, F, k, E)
+    assert B.moe_cached_layer_workspace(fmt, T, 2000, F, k, E) == 0
+    fake = 0x1000  # never dereferenced: validation fails first
+    h = ctypes.c_int32(0)
+
+    def call(layer, ws_bytes):
+        return L.moe_cached_layer_forward(fmt, B.blob_stride(fmt, H, F), H, F, E, k, 0, layer, fake, T, fake,
+                                          fake, fake, fake, fake, 0x100000, ws_bytes, None, None,
+                                          ctypes.byref(h), ctypes.byref(h))
+    assert call(None, need) == B.MOE_E_ARG
+    layer = B.moe_cached_layer(fake, fake, fake, B.moe_lru(E, 64, fake, fake, fake, fake), fake, fake, None, None)
+    assert call(ctypes.byref(layer), need - 1) == B.MOE_E_WORKSPACE

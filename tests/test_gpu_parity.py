@@ -273,6 +273,68 @@ def test_cache_mode_bitwise_equals_resident_mode():
 
 
 @pytest.mark.parametrize("fmt", [NV, MX])
+def test_cached_layer_forward(fmt):
+    """The native cached-layer executor: 6 slots for 16 experts, top-2, 24 AR(1)
+    steps.  Each step's output equals the all-resident GEMV + combine bit for
+    bit; hits, misses and the slot table equal the oracle LRU; step 0 matches
+    the oracle layer."""
+    from oracle import lru as olru
+    H, E, F, k, S = 256, 16, 512, 2, 6
+    L = Layer(fmt, H, E, F, cfg=22, layer=0, w_std=0.02)
+    xs = ar1_states(0, 22, 24, H, [L.router], k)
+    pool_res, R = L.device()
+    host = torch.empty(E * L.stride, dtype=torch.uint8).pin_memory()
+    host.numpy()[:] = L.host_pool()
+    slots = torch.zeros(S * L.stride, dtype=torch.uint8, device="cuda")
+    cl = B.CachedLayer(R, host, slots, E, S, 1, k)
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    copy = torch.cuda.Stream()
+    ref_lru = olru.StampLRU(E, S)
+    for t in range(xs.shape[0]):
+        xd = _x_dev(xs[t:t + 1])
+        idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+        pair_slot = torch.empty(k, dtype=torch.int32, device="cuda")
+        pair_order = torch.empty(k, dtype=torch.int32, device="cuda")
+        out = torch.empty((1, H), dtype=torch.uint16, device="cuda")
+        hits, miss = B.moe_cached_layer_forward(fmt, L.stride, H, F, E, k, cl, xd, idx, w, pair_slot,
+                                                pair_order, out, ws, copy_stream=copy)
+        y_res = torch.empty((k, H), dtype=torch.float32, device="cuda")
+        B.moe_expert_ffn(fmt, pool_res, L.stride, H, F, E, xd, idx, y=y_res, flags=B.MOE_FFN_GEMV)
+        out_res = torch.empty_like(out)
+        B.moe_combine(y_res, w, out_res)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_res), f"step {t}"
+        r = ref_lru.step(idx.cpu().numpy().ravel())
+        assert (hits, miss) == (r["n_hits"], r["n_miss"]), f"step {t}"
+        assert np.array_equal(pair_slot.cpu().numpy(), r["pair_slot"]), f"step {t}"
+        if t == 0:
+            _check_route(xs[:1], L.router, k, idx, w)
+            ref = moe.moe_layer(fmt, xs[:1], L.router, L.experts, k)
+            assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
+
+
+def test_cached_layer_capacity_error():
+    """One slot cannot take two distinct misses: MOE_E_CAPACITY, state unchanged."""
+    fmt, H, E, F, k, S = MX, 256, 8, 512, 2, 1
+    L = Layer(fmt, H, E, F, cfg=0, layer=0, w_std=0.02)
+    x = iid_tokens(0, 0, 1, H, [L.router], k)
+    _, R = L.device()
+    host = torch.empty(E * L.stride, dtype=torch.uint8).pin_memory()
+    host.numpy()[:] = L.host_pool()
+    slots = torch.zeros(S * L.stride, dtype=torch.uint8, device="cuda")
+    cl = B.CachedLayer(R, host, slots, E, S, 1, k)
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    bufs = [torch.empty(s, dtype=d, device="cuda") for s, d in
+            (((1, k), torch.int32), ((1, k), torch.float32), (k, torch.int32), (k, torch.int32), ((1, H), torch.uint16))]
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_cached_layer_forward(fmt, L.stride, H, F, E, k, cl, _x_dev(x), *bufs, ws)
+    assert ei.value.status == B.MOE_E_CAPACITY
+    torch.cuda.synchronize()
+    assert int(cl.lru.clock.item()) == 0 and bool((cl.lru.slot_expert == -1).all())
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
 def test_decode_wide_experts_combine_fallback(fmt):
     """Width 8192 with top-8: the k rows of h (k*F*2 bytes) exceed the fused
     down+combine kernel's LDS, so down runs alone and the combine follows."""
