@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--cache-steps", type=int, default=128)
     p.add_argument("--fmt", type=int, default=0, help="override weight format (1 NVFP4, 2 MXFP4, 3 FP8)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (testing only)")
+    p.add_argument("--replicate-layers", action="store_true",
+                   help="generate layer 0's experts once and give every other layer its own device copy "
+                        "(distinct addresses, same bytes; routers stay per layer) - for the large stacks")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-steps", type=int, default=6)
     p.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
@@ -55,9 +58,10 @@ def parse():
     return p.parse_args()
 
 
-def build_stack(wl, fmt, n_layers, threads, keep_host=False):
+def build_stack(wl, fmt, n_layers, threads, keep_host=False, replicate=False):
     """Generate, quantize, pack and upload every layer; returns device pools, routers,
-    the blob stride and (keep_host) the pinned host copy of every layer."""
+    the blob stride and (keep_host) the pinned host copy of every layer.  With
+    replicate, layers after the first get a device copy of layer 0's experts."""
     import torch
 
     from block_scaled_fp4_gemv_amd import binding as B
@@ -69,6 +73,10 @@ def build_stack(wl, fmt, n_layers, threads, keep_host=False):
     host = torch.empty(wl.E * stride, dtype=torch.uint8).pin_memory()
     t0 = time.time()
     for l in range(n_layers):
+        if replicate and l > 0:
+            pools.append(pools[0].clone())
+            routers.append(torch.from_numpy(sy.router(0, wl.wcfg, l, wl.E, wl.H)).cuda())
+            continue
         batch = sy.experts(fmt, 0, wl.wcfg, l, 0, wl.E, wl.H, wl.F, wl.w_std)
         if keep_host and l > 0:
             host = torch.empty(wl.E * stride, dtype=torch.uint8).pin_memory()
@@ -296,7 +304,8 @@ def main():
     torch.cuda.init()
     log(f"workload {wl.name}: {n_layers} layers H={wl.H} E={wl.E} k={wl.k} F={wl.F} fmt={fmt}")
     want_cache = args.cache != "none" and wl.name == "decode35b"
-    pools, routers, stride, hosts = build_stack(wl, fmt, n_layers, args.threads, keep_host=want_cache)
+    pools, routers, stride, hosts = build_stack(wl, fmt, n_layers, args.threads, keep_host=want_cache,
+                                                replicate=args.replicate_layers)
     H, E, F, k = wl.H, wl.E, wl.F, wl.k
 
     n_states = wl.steps
@@ -375,7 +384,9 @@ def main():
         "dtype": {1: "nvfp4 weights, bf16 activations, fp32 accumulate",
                   2: "mxfp4 weights, bf16 activations, fp32 accumulate",
                   3: "fp8-e4m3 weights, bf16 activations, fp32 accumulate"}[fmt],
-        "data": "synthetic (seeded N(0,0.02) weights quantized to the block format; AR(1) bf16 states)",
+        "data": (f"synthetic (seeded N(0,{wl.w_std}) weights quantized to the block format; AR(1) bf16 states"
+                 + ("; layer 0's experts replicated to every layer's own device pool" if args.replicate_layers
+                    else "") + ")"),
         "config": {"workload": f"{wl.name}: {n_layers} stacked MoE layers, hidden {H}, {E} experts, "
                                f"top-{k}, expert width {F}, batch 1",
                    "layers": n_layers, "hidden": H, "experts": E, "top_k": k, "expert_width": F,
@@ -402,7 +413,7 @@ def main():
         log(f"prefill leg {args.prefill} ...")
         del pools
         torch.cuda.empty_cache()
-        res["prefill"] = prefill_leg(args.prefill, 0, args.prefill_reps, args.threads)
+        res["prefill"] = prefill_leg(args.prefill, args.fmt, args.prefill_reps, args.threads)
         log(f"prefill: {res['prefill']['layer_us']} us/layer, {res['prefill']['tokens_per_s']} tok/s")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
