@@ -54,6 +54,10 @@ SIGNATURES = {
     "moe_layer_forward": (_i32, [_i32, _vp, _sz, _i32, _i32, _i32, _i32, _u32, _vp, _i32, _vp, _vp, _vp,
                                  _vp, _vp, _sz, _vp]),
     "moe_cached_layer_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "moe_cache_fill_device": (_i32, [_vp, _vp, _vp, _sz, _sz, _vp, _vp, _vp, _vp]),
+    "moe_cached_layer_enqueue": (_i32, [_i32, _sz, _i32, _i32, _i32, _i32, _u32,
+                                        ctypes.POINTER(moe_cached_layer), _vp, _i32, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _sz, _vp]),
     "moe_cached_layer_forward": (_i32, [_i32, _sz, _i32, _i32, _i32, _i32, _u32,
                                         ctypes.POINTER(moe_cached_layer), _vp, _i32, _vp, _vp, _vp, _vp,
                                         _vp, _vp, _sz, _vp, _vp, ctypes.POINTER(ctypes.c_int32),
@@ -331,12 +335,14 @@ class CachedLayer:
     host pool ([pinned] uint8 tensor of E blobs), slot pool (device, S blobs), LRU
     state, a pinned miss record and three events (created here)."""
 
-    def __init__(self, router, host_pool, slot_pool, E, S, T, k):
+    def __init__(self, router, host_pool, slot_pool, E, S, T, k, rec_on_device=False):
         import torch
         self.router, self.host_pool, self.slot_pool = router, host_pool, slot_pool
         self.lru = LRUState(E, S, router.device)
         moe_lru_reset(self.lru)
-        self.miss_rec = torch.zeros(moe_miss_record_words(T, k, S), dtype=torch.int32).pin_memory()
+        n = moe_miss_record_words(T, k, S)
+        self.miss_rec = (torch.zeros(n, dtype=torch.int32, device=router.device) if rec_on_device
+                         else torch.zeros(n, dtype=torch.int32).pin_memory())
         self.lookup_done, self.slots_free, self.fill_done = (torch.cuda.Event() for _ in range(3))
         for ev in (self.lookup_done, self.slots_free, self.fill_done):
             ev.record()  # creates the underlying HIP event
@@ -357,3 +363,22 @@ def moe_cached_layer_forward(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w
                                         _stream(copy_stream), ctypes.byref(hits), ctypes.byref(miss))
     _check(st, "moe_cached_layer_forward")
     return hits.value, miss.value
+
+
+def moe_cache_fill_device(miss_rec, host_pool, slot_pool, expert_bytes, stride, record_ready=None,
+                          slots_free=None, copy_stream=None, fill_done=None):
+    ev = lambda e: None if e is None else e.cuda_event  # noqa: E731
+    st = lib().moe_cache_fill_device(_ptr(miss_rec), _ptr(host_pool), _ptr(slot_pool), expert_bytes, stride,
+                                     ev(record_ready), ev(slots_free), _stream(copy_stream), ev(fill_done))
+    _check(st, "moe_cache_fill_device")
+
+
+def moe_cached_layer_enqueue(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w, pair_slot, pair_order, out,
+                             ws, flags=0, stream=None):
+    """Enqueue one cached layer on one stream (no host wait; misses streamed from the
+    host pool); hits/misses are in layer.miss_rec once the stream has passed it."""
+    T = x.shape[0]
+    st = lib().moe_cached_layer_enqueue(fmt, stride, H, F, E, k, flags, ctypes.byref(layer.c), _ptr(x), T,
+                                        _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
+                                        _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "moe_cached_layer_enqueue")

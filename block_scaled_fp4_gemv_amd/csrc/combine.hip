@@ -9,7 +9,8 @@ namespace {
 
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const float* __restrict__ w, int H, int k,
-                                                 uint16_t* __restrict__ out) {
+                                                 uint16_t* __restrict__ out, const int32_t* __restrict__ rec) {
+  if (rec && rec[0] != MOE_OK) return;  // the pairs did not run (cache capacity error)
   const int t = blockIdx.y;
   const int n4 = blockIdx.x * blockDim.x + threadIdx.x;
   if (n4 * 4 >= H) return;
@@ -34,6 +35,14 @@ hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, u
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid((H / 4 + 255) / 256, T);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, y, w, H, k, out);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, y, w, H, k, out, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_rec(const float* y, const float* w, int T, int H, int k, uint16_t* out,
+                              const int32_t* rec, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((H / 4 + 255) / 256, T);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, y, w, H, k, out, rec);
   return hipGetLastError();
 }

@@ -44,6 +44,24 @@ struct Frag {
     }
   }
 
+  // Write the fragment back at the same place of another blob (cache fill of a
+  // streamed miss): every lane stores its codes, and the lanes holding a
+  // distinct scale store it.
+  __device__ __forceinline__ void store(uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, size_t f,
+                                        int lane) const {
+    if constexpr (kFP8) {
+      reinterpret_cast<uint4*>(codes + f * 2048)[lane] = c[0];
+      reinterpret_cast<uint4*>(codes + f * 2048 + 1024)[lane] = c[1];
+      if (lane < 16) reinterpret_cast<uint32_t*>(scales + f * 64)[lane] = sc;
+    } else {
+      reinterpret_cast<uint4*>(codes + f * 1024)[lane] = c[0];
+      if constexpr (FMT == MOE_FMT_NVFP4)
+        reinterpret_cast<uint16_t*>(scales + f * 128)[lane] = (uint16_t)sc;
+      else
+        scales[f * 64 + lane] = (uint8_t)sc;
+    }
+  }
+
   // The lane's 32 elements against xs (16 bf16 pairs of the same k).
   __device__ __forceinline__ float dot(const uint32_t* xs) const {
     if constexpr (FMT == MOE_FMT_NVFP4)
@@ -82,12 +100,35 @@ inline int gemv_batch(int S) {
   return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
 }
 
+// Pair handled by workgroup row blockIdx.y; -1 if this workgroup has nothing to
+// do.  With a miss record (subset_rec) the entries of pair_subset are split on
+// the device: mode 1 takes the first rec[2] (the hits), mode 2 the rest, mode 3
+// all of them and flags the rest as misses to stream from host memory, mode 4
+// all of them from their slots; nothing runs unless rec[0] == MOE_OK.
+__device__ __forceinline__ int pair_of_block(const int32_t* __restrict__ pair_subset,
+                                             const int32_t* __restrict__ subset_rec, int subset_mode,
+                                             bool& miss) {
+  const int i = blockIdx.y;
+  miss = false;
+  if (subset_rec) {
+    if (subset_rec[0] != MOE_OK) return -1;
+    const int nh = subset_rec[2];
+    if (subset_mode == 1 && i >= nh) return -1;
+    if (subset_mode == 2 && i < nh) return -1;
+    miss = subset_mode == 3 && i >= nh;  // mode 4: every entry, all from their slots
+    return pair_subset ? pair_subset[i] : i;
+  }
+  return pair_subset ? pair_subset[i] : i;
+}
+
 // Gate and up rows 16g.. of one pair: steps w, w+nw, ... of S, in batches of NB
 // with every load of a batch issued before its arithmetic.
+// With fill != NULL (a streamed miss) the fragments read from blob are also
+// written to the same places of fill.
 template <int FMT, int NB>
 __device__ __forceinline__ void gateup_partial(const uint8_t* __restrict__ blob, const BlobLayout& L,
                                                int S, int g, const uint16_t* xl, int w, int nw,
-                                               int lane, float& ag, float& au) {
+                                               int lane, float& ag, float& au, uint8_t* fill = nullptr) {
   const int q = lane >> 4;
   for (int s0 = w; s0 < S; s0 += NB * nw) {
     Frag<FMT> fg[NB], fu[NB];
@@ -98,6 +139,17 @@ __device__ __forceinline__ void gateup_partial(const uint8_t* __restrict__ blob,
         const size_t f = (size_t)g * S + s;
         fg[i].load(blob + L.cg, blob + L.sg, f, lane);
         fu[i].load(blob + L.cu, blob + L.su, f, lane);
+      }
+    }
+    if (fill) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int s = s0 + i * nw;
+        if (s < S) {
+          const size_t f = (size_t)g * S + s;
+          fg[i].store(fill + L.cg, fill + L.sg, f, lane);
+          fu[i].store(fill + L.cu, fill + L.su, f, lane);
+        }
       }
     }
 #pragma unroll
@@ -127,6 +179,13 @@ struct DownRows {
       if (s0 + i * nw < S) fd[i].load(codes, scales, (size_t)g * S + s0 + i * nw, lane);
   }
 
+  __device__ __forceinline__ void store(uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int S, int g,
+                                        int s0, int nw, int lane) const {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      if (s0 + i * nw < S) fd[i].store(codes, scales, (size_t)g * S + s0 + i * nw, lane);
+  }
+
   __device__ __forceinline__ float dot(const uint16_t* xrow, int S, int s0, int nw, int lane) const {
     float a = 0.0f;
 #pragma unroll
@@ -151,13 +210,16 @@ __global__ __launch_bounds__(512) void k_gateup_gemv(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F, int E, int k,
     unsigned flags, const uint16_t* __restrict__ x, const float* __restrict__ logits,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, const int32_t* __restrict__ pair_slot,
-    const int32_t* __restrict__ pair_subset, uint16_t* __restrict__ hbuf) {
+    const int32_t* __restrict__ pair_subset, const int32_t* __restrict__ subset_rec, int subset_mode,
+    const uint8_t* __restrict__ miss_src, uint16_t* __restrict__ hbuf) {
   __shared__ __attribute__((aligned(16))) uint16_t xl[kMaxDim];
   __shared__ float red[8][2][16];
   __shared__ int s_slot;
   __shared__ TopkScratch s_topk;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int q = TOPK ? (int)blockIdx.y : (pair_subset ? pair_subset[blockIdx.y] : (int)blockIdx.y);
+  bool miss = false;
+  const int q = TOPK ? (int)blockIdx.y : pair_of_block(pair_subset, subset_rec, subset_mode, miss);
+  if (q < 0) return;
   const int t = q / k, j = q % k, g = blockIdx.x;
   const uint4* xs4 = reinterpret_cast<const uint4*>(x + (size_t)t * H);
   for (int i = threadIdx.x; i < H / 8; i += blockDim.x) reinterpret_cast<uint4*>(xl)[i] = xs4[i];
@@ -178,9 +240,27 @@ __global__ __launch_bounds__(512) void k_gateup_gemv(
     if (threadIdx.x == 0) s_slot = pair_slot ? pair_slot[q] : topk_idx[q];
   }
   __syncthreads();
-  const uint8_t* blob = pool + (size_t)s_slot * stride;
+  // a streamed miss reads the expert's blob from host memory and fills its slot
+  const uint8_t* blob = miss ? miss_src + (size_t)topk_idx[q] * stride : pool + (size_t)s_slot * stride;
+  uint8_t* fill = miss ? const_cast<uint8_t*>(pool) + (size_t)s_slot * stride : nullptr;
+  if (fill && g == 0 && threadIdx.x < 3)
+    reinterpret_cast<float*>(fill + L.tau)[threadIdx.x] = reinterpret_cast<const float*>(blob + L.tau)[threadIdx.x];
   float ag = 0.0f, au = 0.0f;
-  gateup_partial<FMT, NB>(blob, L, H / kFragK, g, xl, w, nw, lane, ag, au);
+  gateup_partial<FMT, NB>(blob, L, H / kFragK, g, xl, w, nw, lane, ag, au, fill);
+  if (fill) {
+    // the workgroups of a streamed miss also bring its down matrix (codes and
+    // scales) into the slot, so the down kernel reads every pair from VRAM
+    const size_t cd = (size_t)H * F / (FMT == MOE_FMT_FP8_E4M3 ? 1 : 2);
+    const size_t sd = FMT == MOE_FMT_NVFP4 ? (size_t)H * F / 16 : FMT == MOE_FMT_MXFP4 ? (size_t)H * F / 32
+                                                                                     : (size_t)H * (F / 128) * 4;
+    const size_t nc = cd / 16, ns = sd / 16, step = (size_t)gridDim.x * blockDim.x;
+    const uint4* sc4 = reinterpret_cast<const uint4*>(blob + L.cd);
+    uint4* dc4 = reinterpret_cast<uint4*>(fill + L.cd);
+    for (size_t c = (size_t)g * blockDim.x + threadIdx.x; c < nc; c += step) dc4[c] = sc4[c];
+    const uint4* ss4 = reinterpret_cast<const uint4*>(blob + L.sd);
+    uint4* ds4 = reinterpret_cast<uint4*>(fill + L.sd);
+    for (size_t c = (size_t)g * blockDim.x + threadIdx.x; c < ns; c += step) ds4[c] = ss4[c];
+  }
   ag = row_lanes_sum(ag);
   au = row_lanes_sum(au);
   if (lane < 16) {
@@ -208,13 +288,17 @@ template <int FMT, int NB>
 __global__ __launch_bounds__(512) void k_down_gemv(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F, int k,
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ pair_slot,
-    const int32_t* __restrict__ pair_subset, const uint16_t* __restrict__ hbuf, float* __restrict__ y) {
+    const int32_t* __restrict__ pair_subset, const int32_t* __restrict__ subset_rec, int subset_mode,
+    const uint8_t* __restrict__ miss_src, const uint16_t* __restrict__ hbuf, float* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint16_t hl[kMaxDim];
   __shared__ float red[8][16];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int q = pair_subset ? pair_subset[blockIdx.y] : (int)blockIdx.y;
+  bool miss = false;
+  const int q = pair_of_block(pair_subset, subset_rec, subset_mode, miss);
+  if (q < 0) return;
   const int slot = pair_slot ? pair_slot[q] : topk_idx[q];
-  const uint8_t* blob = pool + (size_t)slot * stride;
+  const uint8_t* blob = miss ? miss_src + (size_t)topk_idx[q] * stride : pool + (size_t)slot * stride;
+  uint8_t* fill = miss ? const_cast<uint8_t*>(pool) + (size_t)slot * stride : nullptr;
   const int g = blockIdx.x;
   const int S = F / kFragK;
   DownRows<FMT, NB> d;
@@ -222,9 +306,11 @@ __global__ __launch_bounds__(512) void k_down_gemv(
   const uint4* h4 = reinterpret_cast<const uint4*>(hbuf + (size_t)q * F);
   for (int i = threadIdx.x; i < F / 8; i += blockDim.x) reinterpret_cast<uint4*>(hl)[i] = h4[i];
   __syncthreads();
+  if (fill) d.store(fill + L.cd, fill + L.sd, S, g, w, nw, lane);
   float a = d.dot(hl, S, w, nw, lane);
   for (int s0 = w + NB * nw; s0 < S; s0 += NB * nw) {
     d.load(blob + L.cd, blob + L.sd, S, g, s0, nw, lane);
+    if (fill) d.store(fill + L.cd, fill + L.sd, S, g, s0, nw, lane);
     a += d.dot(hl, S, s0, nw, lane);
   }
   a = row_lanes_sum(a);
@@ -247,8 +333,9 @@ __global__ __launch_bounds__(1024) void k_down_combine_gemv(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F, int k,
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ pair_slot,
     const uint16_t* __restrict__ hbuf, const float* __restrict__ topk_w, float* __restrict__ y,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, const int32_t* __restrict__ rec) {
   extern __shared__ __attribute__((aligned(16))) uint16_t hl_dyn[];
+  if (rec && rec[0] != MOE_OK) return;  // cache capacity error: the pairs did not run
   __shared__ float ys[16][16];
   const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
   const int t = blockIdx.y, q = t * k + j, g = blockIdx.x;
@@ -290,7 +377,7 @@ hipError_t launch_gateup_t(const FfnArgs& a, const float* logits, unsigned flags
   case NB:                                                                                             \
     hipLaunchKernelGGL((k_gateup_gemv<FMT, NB, TOPK, NV>), grid, block, 0, s, a.pool, a.stride, a.L, \
                        a.H, a.F, a.E, a.k, flags, a.x, logits, TOPK ? idx : const_cast<int32_t*>(a.topk_idx), \
-                       w, a.pair_slot, a.pair_subset, a.hbuf);                                         \
+                       w, a.pair_slot, a.pair_subset, a.subset_rec, a.subset_mode, a.miss_src, a.hbuf); \
     break;
   switch (gemv_batch(S)) {
     L(1) L(2) L(4) L(8)
@@ -319,15 +406,17 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
 #define LC(NB)                                                                                         \
   case NB:                                                                                             \
     hipLaunchKernelGGL((k_down_combine_gemv<FMT, NB>), grid, dim3(64 * a.k), lds, s, a.pool, a.stride, a.L, \
-                       a.H, a.F, a.k, a.topk_idx, a.pair_slot, a.hbuf, a.topk_w, a.y, a.out);         \
+                       a.H, a.F, a.k, a.topk_idx, a.pair_slot, a.hbuf, a.topk_w, a.y, a.out, a.subset_rec); \
     break;
 #define LD(NB)                                                                                         \
   case NB:                                                                                             \
     hipLaunchKernelGGL((k_down_gemv<FMT, NB>), grid, dim3(64 * nw), 0, s, a.pool, a.stride, a.L, a.H, \
-                       a.F, a.k, a.topk_idx, a.pair_slot, a.pair_subset, a.hbuf, y);                 \
+                       a.F, a.k, a.topk_idx, a.pair_slot, a.pair_subset, a.subset_rec, a.subset_mode, \
+                       a.miss_src, a.hbuf, y);                                                         \
     break;
   const size_t lds = (size_t)a.k * a.F * 2;
-  if (a.out && a.k <= 16 && lds <= 64 * 1024 && !a.pair_subset) {
+  // fused down + combine: all pairs of each token (a miss record only guards it, mode 4)
+  if (a.out && a.k <= 16 && lds <= 64 * 1024 && !a.pair_subset && (!a.subset_rec || a.subset_mode == 4)) {
     dim3 grid(a.H / kFragRows, a.T);
     switch (S <= 1 ? 1 : S <= 2 ? 2 : 4) {  // one wave per pair: batches of <= 4 steps
       LC(1) LC(2) LC(4)
@@ -346,7 +435,8 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
     if (a.out) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      return launch_combine(y, a.topk_w, a.T, a.H, a.k, a.out, s);
+      return a.subset_rec ? launch_combine_rec(y, a.topk_w, a.T, a.H, a.k, a.out, a.subset_rec, s)
+                          : launch_combine(y, a.topk_w, a.T, a.H, a.k, a.out, s);
     }
   }
 #undef LC
@@ -366,6 +456,27 @@ hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s) {
     default: e = launch_gateup<MOE_FMT_FP8_E4M3>(a, s); break;
   }
   if (e != hipSuccess) return e;
+  switch (a.fmt) {
+    case MOE_FMT_NVFP4: return launch_down<MOE_FMT_NVFP4>(a, s);
+    case MOE_FMT_MXFP4: return launch_down<MOE_FMT_MXFP4>(a, s);
+    default: return launch_down<MOE_FMT_FP8_E4M3>(a, s);
+  }
+}
+
+hipError_t launch_ffn_gemv_split(const FfnArgs& a0, int gateup_mode, int down_mode, hipStream_t s) {
+  FfnArgs a = a0;
+  a.subset_mode = gateup_mode;
+  if (a.n_pairs == 0) return hipSuccess;
+  if (a.H > kMaxDim || a.H % kFragK || a.F % kFragK) return hipErrorInvalidValue;
+  hipError_t e;
+  switch (a.fmt) {
+    case MOE_FMT_NVFP4: e = launch_gateup<MOE_FMT_NVFP4>(a, s); break;
+    case MOE_FMT_MXFP4: e = launch_gateup<MOE_FMT_MXFP4>(a, s); break;
+    default: e = launch_gateup<MOE_FMT_FP8_E4M3>(a, s); break;
+  }
+  if (e != hipSuccess) return e;
+  a.subset_mode = down_mode;
+  if (down_mode == 4 && a.out) a.pair_subset = nullptr;  // every pair from its slot, combine fused
   switch (a.fmt) {
     case MOE_FMT_NVFP4: return launch_down<MOE_FMT_NVFP4>(a, s);
     case MOE_FMT_MXFP4: return launch_down<MOE_FMT_MXFP4>(a, s);

@@ -14,6 +14,15 @@ struct FfnArgs {
   const int32_t* expert_off;
   const int32_t* pair_subset;
   int n_pairs;  // pairs to compute (n_subset, or T*k)
+  // Device-side split of pair_subset (GEMV path): with subset_rec (a miss
+  // record) the grid covers all n_pairs entries and mode 1 computes the first
+  // rec[2] of them (hits), mode 2 the rest, mode 3 all with the rest streamed
+  // from miss_src; nothing runs unless rec[0] == MOE_OK.
+  const int32_t* subset_rec;
+  int subset_mode;
+  // mode 3: host pool (pinned) the missed pairs stream their blob from; their
+  // slot in `pool` is filled on the way
+  const uint8_t* miss_src;
   const float* topk_w;
   float* y;        // [T*k][H] or NULL
   uint16_t* out;   // [T][H] or NULL
@@ -25,6 +34,8 @@ size_t grouped_tiles_bytes(int T, int k, int E);
 
 // GEMV path: gate/up + SwiGLU into hbuf, then down (+ combine when out != NULL).
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s);
+// The same with separate subset modes for the gate/up and the down kernel.
+hipError_t launch_ffn_gemv_split(const FfnArgs& a, int gateup_mode, int down_mode, hipStream_t s);
 // Decode layer: gate/up with the softmax/top-k of `logits` computed inside each
 // workgroup (writes topk_idx/topk_w), then down + combine.  T*k pairs, T <= 4.
 hipError_t launch_decode_layer(const FfnArgs& a, const float* logits, unsigned route_flags,
@@ -60,8 +71,20 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, unsigned flags,
 
 hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, uint16_t* out,
                           hipStream_t s);
+// The same, skipped on the device unless rec[0] == MOE_OK (rec: a miss record).
+hipError_t launch_combine_rec(const float* y, const float* w, int T, int H, int k, uint16_t* out,
+                              const int32_t* rec, hipStream_t s);
 
 hipError_t launch_lru_reset(const moe_lru& l, hipStream_t s);
+// The same step with the routed experts selected inside the kernel from the
+// router logits (softmax + top-k; T <= 4, k <= 16), writing topk_idx / topk_w.
+hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int T, int k, unsigned flags,
+                                  int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
+                                  int32_t* miss_rec, int n_max, hipStream_t s);
+// Copy the blobs named by a miss record (read on the device) from the host
+// pool (pinned, device-addressable) into their victim slots.
+hipError_t launch_cache_fill(const int32_t* miss_rec, const uint8_t* host_pool, uint8_t* slot_pool,
+                             size_t expert_bytes, size_t stride, hipStream_t s);
 hipError_t launch_lru_lookup(const moe_lru& l, const int32_t* topk_idx, int n_pairs,
                              int32_t* pair_slot, int32_t* pair_order, int32_t* miss_rec, int n_max,
                              hipStream_t s);

@@ -16,10 +16,11 @@
 //    final stamp is clock0 + (last access index of its expert) + 1.
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kMaxE = 1024, kMaxS = 1024;
 
 __device__ int block_exclusive_scan(int v, int* sh, int* total) {
@@ -44,11 +45,39 @@ __device__ int block_exclusive_scan(int v, int* sh, int* total) {
   return wbase + incl - v;
 }
 
+// NV > 0: the routed experts are first selected here from `logits` (T <= 4
+// tokens, one wave each: softmax + top-k, written to topk_idx / topk_w), which
+// saves a dependent kernel between the router and the lookup.
+constexpr int kMaxFusedPairs = (kThreads / 64) * 16;
+
+template <int NV>
 __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     int E, int S, int32_t* __restrict__ slot_expert, int32_t* __restrict__ expert_slot,
     int64_t* __restrict__ slot_stamp, int64_t* __restrict__ clock,
-    const int32_t* __restrict__ idx, int n, int32_t* __restrict__ pair_slot,
-    int32_t* __restrict__ pair_order, int32_t* __restrict__ rec, int n_max) {
+    const int32_t* __restrict__ idx_in, int n, int32_t* __restrict__ pair_slot,
+    int32_t* __restrict__ pair_order, int32_t* __restrict__ rec, int n_max,
+    const float* __restrict__ logits, int k, unsigned flags, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+  __shared__ int s_idx[kMaxFusedPairs];
+  const int32_t* idx = idx_in;
+  if constexpr (NV > 0) {
+    __shared__ TopkScratch s_topk[kThreads / 64];
+    const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63, T = n / k;
+    if (wv < T) {
+      float v[NV];
+      wave_load_logits<NV>(logits + (size_t)wv * E, E, v);
+      int e;
+      float wt;
+      wave_topk_regs<NV>(v, E, k, flags, e, wt, s_topk[wv]);
+      if (ln < k) {
+        s_idx[wv * k + ln] = e;
+        topk_idx[wv * k + ln] = e;
+        topk_w[wv * k + ln] = wt;
+      }
+    }
+    __syncthreads();
+    idx = s_idx;
+  }
   __shared__ int s_first[kMaxE];   // first access index of each expert (n = none)
   __shared__ int s_last[kMaxE];    // last access index
   __shared__ int s_eslot[kMaxE];   // expert -> slot (updated in place)
@@ -56,6 +85,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
   __shared__ int s_sexp[kMaxS];    // slot -> expert
   __shared__ long long s_stamp[kMaxS];
   __shared__ int s_cand_rank[kMaxS];
+  __shared__ unsigned long long s_key[kMaxS];
   __shared__ int s_victim[kMaxS];
   __shared__ int s_miss_exp[kMaxS];
   __shared__ int s_scan[kThreads / 64];
@@ -97,32 +127,36 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
   }
   if (tid == 0) s_nmiss = carry;
 
-  // candidate victims: slots whose expert is not requested this step
+  // candidate victims: slots whose expert is not requested this step.  Their
+  // order (empty slots first, then occupied by stamp, ties by index) becomes one
+  // 64-bit key per slot; a candidate's rank is the number of keys below its own.
+  if (tid == 0) s_ncand = 0;
   for (int s = tid; s < S; s += blockDim.x) {
     const int e = s_sexp[s];
     const bool cand = e < 0 || s_first[e] == n;
-    int rank = -1;
-    if (cand) {
-      rank = 0;
-      const int ke = e < 0 ? 0 : 1;
-      const long long ks = s_stamp[s];
-      for (int o = 0; o < S; ++o) {
-        const int eo = s_sexp[o];
-        if (!(eo < 0 || s_first[eo] == n)) continue;
-        const int koe = eo < 0 ? 0 : 1;
-        const long long kos = s_stamp[o];
-        if (koe < ke || (koe == ke && (kos < ks || (kos == ks && o < s)))) ++rank;
-      }
-    }
-    s_cand_rank[s] = rank;
+    s_key[s] = cand ? ((unsigned long long)(e >= 0) << 62) | (unsigned long long)s_stamp[s] : ~0ull;
   }
   __syncthreads();
-  int ncand_local = 0;
-  for (int s = tid; s < S; s += blockDim.x) ncand_local += s_cand_rank[s] >= 0;
-  {
-    int tot;
-    block_exclusive_scan(ncand_local, s_scan, &tot);
-    if (tid == 0) s_ncand = tot;
+  for (int s = tid; s < S; s += blockDim.x) {
+    const unsigned long long ks = s_key[s];
+    int rank = -1;
+    if (ks != ~0ull) {
+      rank = 0;
+      int o = 0;
+      for (; o + 8 <= S; o += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const unsigned long long ko = s_key[o + u];
+          rank += (ko < ks) || (ko == ks && o + u < s);
+        }
+      }
+      for (; o < S; ++o) {
+        const unsigned long long ko = s_key[o];
+        rank += (ko < ks) || (ko == ks && o < s);
+      }
+      atomicAdd(&s_ncand, 1);
+    }
+    s_cand_rank[s] = rank;
   }
   __syncthreads();
   const int n_miss = s_nmiss;
@@ -224,8 +258,59 @@ hipError_t launch_lru_reset(const moe_lru& l, hipStream_t s) {
 hipError_t launch_lru_lookup(const moe_lru& l, const int32_t* topk_idx, int n_pairs,
                              int32_t* pair_slot, int32_t* pair_order, int32_t* miss_rec, int n_max,
                              hipStream_t s) {
-  hipLaunchKernelGGL(k_lru_lookup, dim3(1), dim3(kThreads), 0, s, l.E, l.S, l.slot_expert,
+  hipLaunchKernelGGL(k_lru_lookup<0>, dim3(1), dim3(kThreads), 0, s, l.E, l.S, l.slot_expert,
                      l.expert_slot, l.slot_stamp, l.clock, topk_idx, n_pairs, pair_slot, pair_order,
-                     miss_rec, n_max);
+                     miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int T, int k, unsigned flags,
+                                  int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
+                                  int32_t* miss_rec, int n_max, hipStream_t s) {
+  if (T > kThreads / 64 || k > 16) return hipErrorInvalidValue;
+#define L(NV)                                                                                           \
+  hipLaunchKernelGGL(k_lru_lookup<NV>, dim3(1), dim3(kThreads), 0, s, l.E, l.S, l.slot_expert,          \
+                     l.expert_slot, l.slot_stamp, l.clock, nullptr, T * k, pair_slot, pair_order, miss_rec, \
+                     n_max, logits, k, flags, topk_idx, topk_w)
+  if (l.E <= 64) L(1);
+  else if (l.E <= 256) L(4);
+  else L(16);
+#undef L
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- device fill
+// The GPU cache fill without a host round trip: the miss record is read on the
+// device and each missed blob is copied from the pinned host pool (addressed
+// directly over PCIe) into its victim slot with 16-byte loads and stores, four
+// in flight per thread.  Blob sizes are multiples of 256 bytes.
+namespace {
+__global__ __launch_bounds__(256) void k_cache_fill(const int32_t* __restrict__ rec,
+                                                    const uint8_t* __restrict__ host,
+                                                    uint8_t* __restrict__ slots, size_t expert_bytes,
+                                                    size_t stride) {
+  if (rec[0] != MOE_OK) return;
+  const int n_max = rec[4], n_miss = min(rec[1], n_max);
+  const size_t chunks = expert_bytes / 16, step = (size_t)gridDim.x * blockDim.x;
+  for (int m = 0; m < n_miss; ++m) {
+    const uint4* src = reinterpret_cast<const uint4*>(host + (size_t)rec[5 + m] * stride);
+    uint4* dst = reinterpret_cast<uint4*>(slots + (size_t)rec[5 + n_max + m] * stride);
+    size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; c + 3 * step < chunks; c += 4 * step) {
+      const uint4 a = src[c], b = src[c + step], d = src[c + 2 * step], e = src[c + 3 * step];
+      dst[c] = a;
+      dst[c + step] = b;
+      dst[c + 2 * step] = d;
+      dst[c + 3 * step] = e;
+    }
+    for (; c < chunks; c += step) dst[c] = src[c];
+  }
+}
+}  // namespace
+
+hipError_t launch_cache_fill(const int32_t* miss_rec, const uint8_t* host_pool, uint8_t* slot_pool,
+                             size_t expert_bytes, size_t stride, hipStream_t s) {
+  hipLaunchKernelGGL(k_cache_fill, dim3(512), dim3(256), 0, s, miss_rec, host_pool, slot_pool, expert_bytes,
+                     stride);
   return hipGetLastError();
 }

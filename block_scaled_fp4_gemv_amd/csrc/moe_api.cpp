@@ -452,3 +452,89 @@ int moe_cached_layer_forward(int fmt, size_t stride, int H, int F, int E, int k,
   }
   return moe_combine(y, topk_w, T, H, k, out, stream);
 }
+
+int moe_cache_fill_device(const int32_t* miss_rec, const void* host_pool, void* slot_pool,
+                          size_t expert_bytes, size_t stride, moe_event_t record_ready,
+                          moe_event_t slots_free, moe_stream_t copy_stream, moe_event_t fill_done) {
+  g_err[0] = 0;
+  if (!miss_rec || !host_pool || !slot_pool) return fail(MOE_E_ARG, "NULL record or pool");
+  if (!expert_bytes || expert_bytes % 256 || stride < expert_bytes || stride % 256)
+    return fail(MOE_E_ARG, "bad expert_bytes %zu / stride %zu", expert_bytes, stride);
+  if (!aligned(host_pool, 16) || !aligned(slot_pool, 16)) return fail(MOE_E_ARG, "pools must be 16-byte aligned");
+  hipStream_t cs = static_cast<hipStream_t>(copy_stream);
+  hipError_t e;
+  for (moe_event_t ev : {record_ready, slots_free}) {
+    if (!ev) continue;
+    e = hipStreamWaitEvent(cs, static_cast<hipEvent_t>(ev), 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  e = launch_cache_fill(miss_rec, static_cast<const uint8_t*>(host_pool), static_cast<uint8_t*>(slot_pool),
+                        expert_bytes, stride, cs);
+  if (e != hipSuccess) return hip_fail(e, "cache fill kernel");
+  if (fill_done) {
+    e = hipEventRecord(static_cast<hipEvent_t>(fill_done), cs);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  return MOE_OK;
+}
+
+int moe_cached_layer_enqueue(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                             const moe_cached_layer* L, const uint16_t* x, int T, int32_t* topk_idx,
+                             float* topk_w, int32_t* pair_slot, int32_t* pair_order, uint16_t* out, void* ws,
+                             size_t ws_bytes, moe_stream_t stream) {
+  g_err[0] = 0;
+  if (!L || !L->router || !L->host_pool || !L->slot_pool || !L->miss_rec)
+    return fail(MOE_E_ARG, "incomplete moe_cached_layer");
+  int st = check_shape(fmt, H, F);
+  if (st) return st;
+  const size_t need = moe_cached_layer_workspace(fmt, T, H, F, k, E);
+  if (!need) return fail(MOE_E_ARG, "bad shape or format");
+  if (!ws || !aligned(ws, 256) || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "cached layer workspace needs %zu bytes, 256-aligned", need);
+  if (!pair_slot || !pair_order || !out || !topk_idx || !topk_w) return fail(MOE_E_ARG, "NULL output");
+  if (stride < moe_expert_bytes(fmt, H, F) || stride % 256) return fail(MOE_E_ARG, "bad stride %zu", stride);
+  if (!aligned(L->host_pool, 256) || !aligned(L->slot_pool, 256)) return fail(MOE_E_ARG, "pools must be 256-byte aligned");
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  float* y = reinterpret_cast<float*>(p);
+  p += align256((size_t)T * k * H * 4);
+  const size_t route_bytes = moe_route_workspace(T, H, E, k);
+  void* route_ws = p;
+  p += align256(route_bytes);
+  if (L->lru.E != E || L->lru.S < 1 || L->lru.S > 1024 || E > 1024)
+    return fail(MOE_E_ARG, "LRU state E=%d S=%d for E=%d", L->lru.E, L->lru.S, E);
+  if (T < 0 || k < 1 || k > E || k > 16) return fail(MOE_E_ARG, "T=%d k=%d E=%d", T, k, E);
+  if (T <= 4 && k <= 16) {
+    // router GEMV, then the lookup kernel selects the experts itself (one kernel fewer)
+    RouteArgs r{};
+    r.T = T; r.H = H; r.E = E; r.k = k;
+    route_ws_carve(r, route_ws);
+    if (!aligned(x, 16) || !aligned(L->router, 16)) return fail(MOE_E_ARG, "x and router must be 16-byte aligned");
+    hipError_t e = launch_router_logits(x, L->router, T, H, E, r.logits, s);
+    if (e == hipSuccess)
+      e = launch_lru_lookup_topk(L->lru, r.logits, T, k, route_flags, topk_idx, topk_w, pair_slot, pair_order,
+                                 L->miss_rec, T * k < L->lru.S ? T * k : L->lru.S, s);
+    if (e != hipSuccess) return hip_fail(e, "cached layer (route + lookup)");
+  } else {
+    st = moe_route(x, L->router, T, H, E, k, route_flags, topk_idx, topk_w, nullptr, nullptr, route_ws,
+                   route_bytes, stream);
+    if (st) return st;
+    st = moe_cache_lookup(&L->lru, topk_idx, T, k, pair_slot, pair_order, L->miss_rec, stream);
+    if (st) return st;
+  }
+  FfnArgs a{};
+  a.fmt = fmt; a.H = H; a.F = F; a.E = E; a.T = T; a.k = k;
+  a.pool = static_cast<const uint8_t*>(L->slot_pool); a.stride = stride; a.L = blob_layout(fmt, H, F);
+  a.x = x; a.topk_idx = topk_idx; a.pair_slot = pair_slot; a.pair_subset = pair_order;
+  a.n_pairs = T * k; a.subset_rec = L->miss_rec;
+  a.miss_src = static_cast<const uint8_t*>(L->host_pool); a.y = nullptr;
+  a.hbuf = reinterpret_cast<uint16_t*>(p);
+  a.ybuf = y;  // only if the fused down + combine does not fit
+  a.out = out; a.topk_w = topk_w;
+  // gate/up: mode 3 (misses streamed from the host pool into their slots, down
+  // matrix included); down: mode 4 (every pair from its slot) with the combine
+  hipError_t e = launch_ffn_gemv_split(a, 3, 4, s);
+  // (the combine is fused into the down kernel, or follows it guarded by the record)
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "cached layer (experts)");
+}

@@ -202,6 +202,19 @@ int moe_cache_fill(const int32_t* miss_rec, const void* host_pool, void* slot_po
                    size_t expert_bytes, size_t stride, moe_event_t slots_free,
                    moe_stream_t copy_stream, moe_event_t fill_done);
 
+/* The same GPU cache fill with the miss record read on the device instead of
+ * the host, so nothing waits on the host: copy_stream waits on record_ready
+ * (if not NULL; recorded after moe_cache_lookup) and on slots_free (if not
+ * NULL), then one kernel copies every missed blob from host_pool (pinned,
+ * addressed by the GPU over PCIe) into its victim slot, then fill_done is
+ * recorded (if not NULL).  Copies nothing when miss_rec[0] != MOE_OK.
+ *   miss_rec  device or [pinned] record written by moe_cache_lookup
+ *   host_pool [pinned] E blobs at `stride`; slot_pool device, S blobs at `stride`
+ * expert_bytes must be a multiple of 256 (moe_expert_bytes is). */
+int moe_cache_fill_device(const int32_t* miss_rec, const void* host_pool, void* slot_pool,
+                          size_t expert_bytes, size_t stride, moe_event_t record_ready,
+                          moe_event_t slots_free, moe_stream_t copy_stream, moe_event_t fill_done);
+
 /* ----------------------------------------------------------- expert FFN */
 
 /* Workspace bytes for moe_expert_ffn. */
@@ -299,6 +312,28 @@ int moe_cached_layer_forward(int fmt, size_t stride, int H, int F, int E, int k,
                              int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
                              uint16_t* out, void* ws, size_t ws_bytes, moe_stream_t stream,
                              moe_stream_t copy_stream, int32_t* n_hits, int32_t* n_miss);
+
+/* The cached layer without any host wait, on one stream:
+ *   moe_route -> moe_cache_lookup -> gate/up and down (GEMV) for every pair, the
+ *   pairs that hit (first miss_rec[2] entries of pair_order) reading their slot,
+ *   the missed pairs streaming their expert's blob straight from the pinned host
+ *   pool over PCIe and writing it into their victim slot on the way (the GPU
+ *   cache fill overlapped with the missed pairs' own compute) -> moe_combine.
+ * For T <= 4 the router GEMV is followed by the lookup kernel, which selects
+ * the experts itself (softmax + top-k), and down runs fused with the combine:
+ * the arithmetic of moe_layer_forward's decode path, so topk_idx, topk_w and
+ * `out` equal moe_layer_forward on an all-resident pool bit for bit (larger T:
+ * moe_route, and equal up to fp32 summation order).  The slots end up holding
+ * the same blobs as with moe_cache_fill.
+ * layer->miss_rec may be device memory; the events and copy streams of the
+ * layer are not used.  If the lookup reports MOE_E_CAPACITY (miss_rec[0]),
+ * nothing after the lookup writes anything and `out` keeps its contents: check
+ * miss_rec[0] after synchronising.  Stream-ordered, so a whole decode step of
+ * such layers can be captured in one graph. */
+int moe_cached_layer_enqueue(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                             const moe_cached_layer* layer, const uint16_t* x, int T,
+                             int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
+                             uint16_t* out, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

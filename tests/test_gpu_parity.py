@@ -314,6 +314,117 @@ def test_cached_layer_forward(fmt):
             assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
 
 
+@pytest.mark.parametrize("fmt", [NV, F8])
+def test_cached_layer_enqueue(fmt):
+    """The one-stream executor (device hit/miss split, misses streamed from the
+    pinned host pool and written into their slots), three steps enqueued back to
+    back between synchronisations: every step's routing and output equal the
+    all-resident moe_layer_forward bit for bit, the device miss record equals the
+    oracle LRU, and
+    after each step the occupied slots hold exactly the host blobs of their
+    experts."""
+    from oracle import lru as olru
+    H, E, F, k, S = 256, 16, 512, 2, 6
+    L = Layer(fmt, H, E, F, cfg=23, layer=0, w_std=0.02)
+    xs = ar1_states(0, 23, 24, H, [L.router], k)
+    pool_res, R = L.device()
+    hp = L.host_pool()
+    host = torch.empty(E * L.stride, dtype=torch.uint8).pin_memory()
+    host.numpy()[:] = hp
+    slots = torch.zeros(S * L.stride, dtype=torch.uint8, device="cuda")
+    cl = B.CachedLayer(R, host, slots, E, S, 1, k, rec_on_device=True)
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    ref_lru = olru.StampLRU(E, S)
+    eb = B.moe_expert_bytes(fmt, H, F)
+    n = xs.shape[0]
+    outs = [torch.empty((1, H), dtype=torch.uint16, device="cuda") for _ in range(n)]
+    idxs = [torch.empty((1, k), dtype=torch.int32, device="cuda") for _ in range(n)]
+    ws_ = [torch.empty((1, k), dtype=torch.float32, device="cuda") for _ in range(n)]
+    recs = []
+    pair_slot = torch.empty(k, dtype=torch.int32, device="cuda")
+    pair_order = torch.empty(k, dtype=torch.int32, device="cuda")
+    for t in range(n):
+        B.moe_cached_layer_enqueue(fmt, L.stride, H, F, E, k, cl, _x_dev(xs[t:t + 1]), idxs[t], ws_[t], pair_slot,
+                                   pair_order, outs[t], ws)
+        recs.append(cl.miss_rec.clone())
+        if t % 3 == 2 or t == n - 1:
+            torch.cuda.synchronize()
+            se = cl.lru.slot_expert.cpu().numpy()
+            for s_, e_ in enumerate(se):
+                if e_ >= 0:
+                    got = slots[s_ * L.stride:s_ * L.stride + eb].cpu().numpy()
+                    assert np.array_equal(got, hp[e_ * L.stride:e_ * L.stride + eb]), f"slot {s_}"
+    torch.cuda.synchronize()
+    for t in range(n):
+        # batch <= 4: the same router GEMV, in-kernel top-k, gate/up and fused
+        # down + combine arithmetic as the resident decode layer
+        idx_r, w_r, out_res = B.moe_layer_forward(fmt, pool_res, L.stride, H, F, E, k, _x_dev(xs[t:t + 1]), R)
+        torch.cuda.synchronize()
+        assert torch.equal(idxs[t], idx_r) and torch.equal(ws_[t], w_r), f"step {t}"
+        assert torch.equal(outs[t], out_res), f"step {t}"
+        r = ref_lru.step(idxs[t].cpu().numpy().ravel())
+        rec = recs[t].cpu().numpy()
+        assert rec[0] == 0 and (rec[3], rec[1]) == (r["n_hits"], r["n_miss"]), f"step {t}"
+    _check_route(xs[:1], L.router, k, idxs[0], ws_[0])
+    ref = moe.moe_layer(fmt, xs[:1], L.router, L.experts, k)
+    assert_rows_close(bf16_dev_to_f64(outs[0]), fm.bf16_to_f64(ref["out"]), what="out")
+
+
+def test_cached_layer_enqueue_capacity():
+    """Capacity error on the device path: the record says so, nothing after the
+    lookup writes (out keeps its sentinel), the LRU state is unchanged."""
+    fmt, H, E, F, k, S = MX, 256, 8, 512, 2, 1
+    L = Layer(fmt, H, E, F, cfg=0, layer=0, w_std=0.02)
+    x = iid_tokens(0, 0, 1, H, [L.router], k)
+    _, R = L.device()
+    host = torch.empty(E * L.stride, dtype=torch.uint8).pin_memory()
+    host.numpy()[:] = L.host_pool()
+    slots = torch.zeros(S * L.stride, dtype=torch.uint8, device="cuda")
+    cl = B.CachedLayer(R, host, slots, E, S, 1, k, rec_on_device=True)
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    out = torch.full((1, H), 0x1234, dtype=torch.uint16, device="cuda")
+    bufs = [torch.empty(s, dtype=d, device="cuda") for s, d in
+            (((1, k), torch.int32), ((1, k), torch.float32), (k, torch.int32), (k, torch.int32))]
+    B.moe_cached_layer_enqueue(fmt, L.stride, H, F, E, k, cl, _x_dev(x), *bufs, out, ws)
+    torch.cuda.synchronize()
+    assert int(cl.miss_rec[0].item()) == B.MOE_E_CAPACITY
+    assert bool((out == 0x1234).all())
+    assert int(cl.lru.clock.item()) == 0 and bool((slots == 0).all())
+
+
+def test_cache_fill_device_copies_the_missed_blobs():
+    """moe_cache_fill_device after a lookup: each missed expert's blob lands in
+    its victim slot byte for byte (record in device memory, side stream, events)."""
+    fmt, H, E, F, k, S = MX, 256, 16, 512, 2, 4
+    L = Layer(fmt, H, E, F, cfg=24, layer=0, w_std=0.02)
+    hp = L.host_pool()
+    host = torch.empty(E * L.stride, dtype=torch.uint8).pin_memory()
+    host.numpy()[:] = hp
+    slots = torch.zeros(S * L.stride, dtype=torch.uint8, device="cuda")
+    st = B.LRUState(E, S)
+    B.moe_lru_reset(st)
+    rec = torch.zeros(B.moe_miss_record_words(3, k, S), dtype=torch.int32, device="cuda")
+    idx = torch.tensor([[3, 9], [9, 14], [3, 0]], dtype=torch.int32, device="cuda")
+    pair_slot = torch.empty(6, dtype=torch.int32, device="cuda")
+    pair_order = torch.empty(6, dtype=torch.int32, device="cuda")
+    ready, done = torch.cuda.Event(), torch.cuda.Event()
+    copy = torch.cuda.Stream()
+    B.moe_cache_lookup(st, idx, pair_slot, pair_order, rec)
+    ready.record()
+    B.moe_cache_fill_device(rec, host, slots, B.moe_expert_bytes(fmt, H, F), L.stride, record_ready=ready,
+                            copy_stream=copy, fill_done=done)
+    torch.cuda.current_stream().wait_event(done)
+    torch.cuda.synchronize()
+    r = rec.cpu().numpy()
+    n_max = r[4]
+    assert r[0] == 0 and r[1] == 4 and list(r[5:9]) == [3, 9, 14, 0]
+    eb = B.moe_expert_bytes(fmt, H, F)
+    for m in range(r[1]):
+        e_, s_ = r[5 + m], r[5 + n_max + m]
+        assert np.array_equal(slots[s_ * L.stride:s_ * L.stride + eb].cpu().numpy(),
+                              hp[e_ * L.stride:e_ * L.stride + eb])
+
+
 def test_cached_layer_capacity_error():
     """One slot cannot take two distinct misses: MOE_E_CAPACITY, state unchanged."""
     fmt, H, E, F, k, S = MX, 256, 8, 512, 2, 1
