@@ -147,7 +147,11 @@ struct BFrag {
   __device__ __forceinline__ float step_scale() const { return __uint_as_float(s); }  // FP8
 };
 
+constexpr int kPatchLd = 68, kPatchFloats = 16 * kPatchLd;  // down epilogue patch per wave (16 x 64 fp32, padded)
+
 struct TileArgs {
+  uint8_t* epi;               // LDS: down epilogue patches
+  const int32_t* rows_perm;   // LDS: pair_perm of the tile's rows (down)
   const uint8_t* blob;
   BlobLayout L;
   int K, N, k_top, a_by_token, ct, npass, row_base, rows;
@@ -267,15 +271,34 @@ __device__ __forceinline__ void tile_epilogue(const TileArgs& t, const floatx4_t
             t.hout[(size_t)(t.row_base + row) * t.N + col] = f32_to_bf16_rne(silu_f32(gv) * uv);
           }
         }
-    } else {
-      const float td = FMT == MOE_FMT_NVFP4 ? tau[2] : 1.0f;
+    }
+  }
+  if constexpr (NMAT == 1) {
+    // y rows of the pairs: each 16-row subtile goes through this wave's LDS
+    // patch (16 rows x 64 columns) so that a store covers 16 B per lane and
+    // 256 contiguous bytes of a row per 16 lanes
+    const float td = FMT == MOE_FMT_NVFP4 ? tau[2] : 1.0f;
+    float* patch = reinterpret_cast<float*>(t.epi) + (threadIdx.x >> 6) * kPatchFloats;
+    const int col0 = g0 * kFragRows;
 #pragma unroll
-      for (int r = 0; r < NS; ++r)
+    for (int r = 0; r < NS; ++r) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = kFragRows * r + 4 * aq + v;
-          if (row < t.rows) t.yout[(size_t)t.pair_perm[t.row_base + row] * t.N + col] = acc[0][cg][r][v] * td;
-        }
+      for (int cg = 0; cg < kCG<NMAT>; ++cg)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) patch[(4 * aq + v) * kPatchLd + 16 * cg + am] = acc[0][cg][r][v] * td;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rl = 4 * j + (lane >> 4), row = kFragRows * r + rl, c4 = 4 * (lane & 15);
+        const float4 val = *reinterpret_cast<const float4*>(patch + rl * kPatchLd + c4);
+        if (row < t.rows)
+          *reinterpret_cast<float4*>(t.yout + (size_t)t.rows_perm[row] * t.N + col0 + c4) = val;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 }
@@ -372,7 +395,9 @@ __global__ __launch_bounds__(256, 2) void k_grouped(
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ tile_e,
     const int32_t* __restrict__ tile_m0, const int32_t* __restrict__ n_tiles, int n_sweeps, int npass,
     uint16_t* __restrict__ hout, float* __restrict__ yout) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2 * kTileRows<FMT> * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t As[2 * kTileRows<FMT> * ROWB +
+                                                   (NMAT == 1 ? NWAVE * kPatchFloats * 4 : 0)];
+  __shared__ int s_rows[NMAT == 1 ? kTileRows<FMT> : 1];
   // A workgroup takes one row tile and a sweep of npass consecutive column
   // tiles.  Workgroups are handed to the 8 XCDs round-robin by index; within
   // each run of 8 * n_sweeps indices, the sweeps of one row tile share an XCD
@@ -384,6 +409,10 @@ __global__ __launch_bounds__(256, 2) void k_grouped(
   const int e = tile_e[tile];
   t.row_base = expert_off[e] + tile_m0[tile];
   t.rows = min(kTileRows<FMT>, expert_off[e + 1] - t.row_base);
+  t.epi = As + 2 * kTileRows<FMT> * ROWB;
+  t.rows_perm = s_rows;
+  if constexpr (NMAT == 1)  // read before the first epilogue, after the pipeline's first barrier
+    for (int i = threadIdx.x; i < t.rows; i += blockDim.x) s_rows[i] = pair_perm[t.row_base + i];
   t.blob = pool + (size_t)e * stride;
   t.L = L;
   t.K = K;

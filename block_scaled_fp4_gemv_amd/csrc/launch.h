@@ -67,7 +67,7 @@ hipError_t launch_router_logits(const uint16_t* x, const float* R, int T, int H,
 hipError_t launch_router_gemm(const uint16_t* x, const float* R, int T, int H, int E, float* logits,
                               uint16_t* planes, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, unsigned flags, int32_t* idx,
-                       float* w, hipStream_t s);
+                       float* w, hipStream_t s, int nsplit = 1);
 
 hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, uint16_t* out,
                           hipStream_t s);

@@ -23,6 +23,7 @@ constexpr int kMaxE = 1024;
 // butterfly reduction.  Every expert uses the same sequence, so experts with
 // identical router rows produce identical logits.
 constexpr int kGemvMaxT = 4;
+constexpr int kRouterSplitK = 4;  // large-T router GEMM: K split 4 ways, partials summed by k_topk
 
 template <int NT, int NC>
 __global__ __launch_bounds__(64) void k_router_logits(const uint16_t* __restrict__ x,
@@ -101,6 +102,9 @@ __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict_
                                                      int E, float* __restrict__ logits) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[RBM * RLD];
   __shared__ __attribute__((aligned(16))) uint16_t rs[3][RBN * RLD];
+  // split K: workgroup z sums k in [z*H/Z, (z+1)*H/Z) into partial z of logits
+  const int kz = H / gridDim.z, k0 = blockIdx.z * kz;
+  logits += (size_t)blockIdx.z * T * E;
   const int tm = blockIdx.y * RBM, tn = blockIdx.x * RBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
@@ -123,8 +127,8 @@ __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict_
   rfloatx16_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  gload(0);
-  for (int kb = 0; kb < H; kb += RBK) {
+  gload(k0);
+  for (int kb = k0; kb < k0 + kz; kb += RBK) {
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict_
       for (int p = 0; p < 3; ++p) *reinterpret_cast<uint4*>(rs[p] + sr * RLD + sc + 8 * j) = ra[p][j];
     }
     __syncthreads();
-    if (kb + RBK < H) gload(kb + RBK);
+    if (kb + RBK < k0 + kz) gload(kb + RBK);
 #pragma unroll
     for (int i = 0; i < RBK / 16; ++i) {
       const rbf16x8_t a = *reinterpret_cast<const rbf16x8_t*>(xs + (32 * wm + (lane & 31)) * RLD + 16 * i + 8 * h);
@@ -154,15 +158,22 @@ __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict_
   }
 }
 
+// logits holds nsplit partial sums [nsplit][T][E]; they are added in order.
 template <int NV>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               unsigned flags, int32_t* __restrict__ topk_idx,
-                                              float* __restrict__ topk_w) {
+                                              float* __restrict__ topk_w, int nsplit) {
   __shared__ TopkScratch scr[4];
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (t >= T) return;
   float v[NV];
   wave_load_logits<NV>(logits + (size_t)t * E, E, v);
+  for (int z = 1; z < nsplit; ++z) {
+    float p[NV];
+    wave_load_logits<NV>(logits + ((size_t)z * T + t) * E, E, p);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] += p[i];
+  }
   int idx;
   float w;
   wave_topk_regs<NV>(v, E, k, flags, idx, w, scr[threadIdx.x >> 6]);
@@ -173,11 +184,11 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 }
 
 hipError_t topk_impl(const float* logits, int T, int E, int k, unsigned flags, int32_t* idx,
-                     float* w, hipStream_t s) {
+                     float* w, int nsplit, hipStream_t s) {
   dim3 grid((T + 3) / 4);
-  if (E <= 64) hipLaunchKernelGGL(k_topk<1>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w);
-  else if (E <= 256) hipLaunchKernelGGL(k_topk<4>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w);
-  else hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w);
+  if (E <= 64) hipLaunchKernelGGL(k_topk<1>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w, nsplit);
+  else if (E <= 256) hipLaunchKernelGGL(k_topk<4>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w, nsplit);
+  else hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w, nsplit);
   return hipGetLastError();
 }
 
@@ -197,40 +208,70 @@ __global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_cnt[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
+// One workgroup: expert e's column of chunk counts is split over tpe = 1024/E
+// threads (contiguous chunk ranges, up to 16 counts kept in registers), the
+// per-thread sums are combined in LDS, an exclusive scan over the expert totals
+// gives expert_off, and each thread rewrites its counts as running offsets.
 __global__ __launch_bounds__(1024) void k_perm_scan(int nchunk, int E, int32_t* __restrict__ chunk_cnt,
                                                     int32_t* __restrict__ expert_off) {
-  __shared__ int tot[kMaxE];
+  __shared__ int s_part[1024];
+  __shared__ int s_tot[kMaxE];
+  __shared__ int s_off[kMaxE];
   __shared__ int wsum[16];
-  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
-  int s = 0;
-  if (e < E) {
-#pragma unroll 16
-    for (int c = 0; c < nchunk; ++c) s += chunk_cnt[(size_t)c * E + e];
+  const int tid = threadIdx.x, tpe = blockDim.x / E;
+  const int e = tid / tpe, sub = tid % tpe;
+  const bool valid = e < E;
+  const int per = (nchunk + tpe - 1) / tpe, c0 = sub * per, c1 = min(nchunk, c0 + per);
+  int v[16];
+  int sum = 0;
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = c0 + i < c1 ? chunk_cnt[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += v[i];
+    for (int c = c0 + 16; c < c1; ++c) sum += chunk_cnt[(size_t)c * E + e];
   }
-  // exclusive scan of the per-expert totals over the block
-  int incl = s;
+  s_part[tid] = sum;
+  __syncthreads();
+  int before = 0;  // this thread's offset inside its expert
+  if (valid) {
+    for (int j = 0; j < sub; ++j) before += s_part[e * tpe + j];
+    if (sub == tpe - 1) s_tot[e] = before + sum;
+  }
+  __syncthreads();
+  // exclusive scan of the expert totals (experts on threads 0..E-1)
+  const int lane = tid & 63, wave = tid >> 6;
+  const int t = tid < E ? s_tot[tid] : 0;
+  int incl = t;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
+    const int n = __shfl_up(incl, o);
+    if (lane >= o) incl += n;
   }
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int base = 0;
   for (int w = 0; w < wave; ++w) base += wsum[w];
-  const int excl = base + incl - s;
-  if (e < E) {
-    expert_off[e] = excl;
-    tot[e] = excl;
-    int run = excl;
-#pragma unroll 16
-    for (int c = 0; c < nchunk; ++c) {
+  if (tid < E) {
+    s_off[tid] = base + incl - t;
+    expert_off[tid] = base + incl - t;
+    if (tid == E - 1) expert_off[E] = base + incl;
+  }
+  __syncthreads();
+  if (valid) {
+    int run = s_off[e] + before;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (c0 + i < c1) {
+        chunk_cnt[(size_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
+    for (int c = c0 + 16; c < c1; ++c) {
       const size_t i = (size_t)c * E + e;
-      const int v = chunk_cnt[i];
+      const int x = chunk_cnt[i];
       chunk_cnt[i] = run;
-      run += v;
+      run += x;
     }
-    if (e == E - 1) expert_off[E] = run;
   }
 }
 
@@ -283,27 +324,31 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* R, int T, int H, i
                               uint16_t* planes, hipStream_t s) {
   const size_t n = (size_t)E * H;
   hipLaunchKernelGGL(k_router_split, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, R, n, planes);
-  dim3 grid((E + RBN - 1) / RBN, (T + RBM - 1) / RBM);
+  dim3 grid((E + RBN - 1) / RBN, (T + RBM - 1) / RBM, kRouterSplitK);
   hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, x, planes, T, H, E, logits);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, unsigned flags, int32_t* idx,
-                       float* w, hipStream_t s) {
-  return topk_impl(logits, T, E, k, flags, idx, w, s);
+                       float* w, hipStream_t s, int nsplit) {
+  return topk_impl(logits, T, E, k, flags, idx, w, nsplit, s);
+}
+
+static size_t logits_bytes(int T, int E) {
+  return align256((size_t)T * E * 4 * (T > kGemvMaxT ? kRouterSplitK : 1));
 }
 
 size_t route_ws_bytes(int T, int H, int E, int k) {
   const size_t n = (size_t)T * k;
   const size_t nchunk = (n + kPermChunk - 1) / kPermChunk;
   const size_t planes = T > kGemvMaxT ? align256((size_t)3 * E * H * 2) : 0;
-  return align256((size_t)T * E * 4) + align256(nchunk * E * 4 + 4) + planes;
+  return logits_bytes(T, E) + align256(nchunk * E * 4 + 4) + planes;
 }
 
 void route_ws_carve(RouteArgs& a, void* ws) {
   uint8_t* p = static_cast<uint8_t*>(ws);
   a.logits = reinterpret_cast<float*>(p);
-  p += align256((size_t)a.T * a.E * 4);
+  p += logits_bytes(a.T, a.E);
   a.chunk_cnt = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)((a.T * a.k + kPermChunk - 1) / kPermChunk) * a.E * 4 + 4);
   a.planes = a.T > kGemvMaxT ? reinterpret_cast<uint16_t*>(p) : nullptr;
@@ -318,7 +363,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   hipError_t e = a.T <= kGemvMaxT ? launch_router_logits(a.x, a.router, a.T, a.H, a.E, a.logits, s)
                                   : launch_router_gemm(a.x, a.router, a.T, a.H, a.E, a.logits, a.planes, s);
   if (e != hipSuccess) return e;
-  e = launch_topk(a.logits, a.T, a.E, a.k, a.flags, a.topk_idx, a.topk_w, s);
+  e = launch_topk(a.logits, a.T, a.E, a.k, a.flags, a.topk_idx, a.topk_w, s,
+                  a.T <= kGemvMaxT ? 1 : kRouterSplitK);
   if (e != hipSuccess || !a.pair_perm) return e;
   const int n = a.T * a.k;
   const int nchunk = (n + kPermChunk - 1) / kPermChunk;
