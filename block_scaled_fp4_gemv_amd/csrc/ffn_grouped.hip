@@ -26,7 +26,7 @@
 //   FP8  : e4m3 -> bf16 exactly; the fp32 scale of the 128-element block is
 //          applied to each step's partial sums.
 // Activation tiles (rows x 128 k bf16) are double-buffered in LDS with the
-// 16-byte chunks of row r stored at chunk ^ (r & 7), which keeps both the
+// 16-byte chunks of row r stored at chunk ^ (r & 15), which keeps both the
 // staging writes and the MFMA operand reads free of bank conflicts; the next
 // step's activations and the step after next's weights are in flight while a
 // step computes, with one barrier per step.
@@ -356,32 +356,47 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
   // column tile, so it is staged again (from L2) on each pass.
   const int U = t.npass * S;
   const int gw = wave * kCG<NMAT>;  // this wave's first group inside a column tile
+  // Prefetches past the last step re-load the last step's data (cached, never
+  // used): every load is unconditional, so the compiler's wait counts stay
+  // exact and a wait for the activations never waits for a newer weight load.
+  const auto grp_of = [&](int v) { return (t.ct + min(v, U - 1) / S) * (kBN<NMAT> / kFragRows) + gw; };
+  const auto k_of = [&](int v) { return min(v, U - 1) % S; };
   uint8_t* buf0 = As;
   uint8_t* buf1 = As + RB * ROWB;
   a_load<NS>(av, arow, 0, sc);
-  b_load<FMT, NMAT>(wb0, codes, scales, t.ct * (kBN<NMAT> / kFragRows) + gw, S, 0, lane);
-  if (U > 1) b_load<FMT, NMAT>(wb1, codes, scales, (t.ct + 1 / S) * (kBN<NMAT> / kFragRows) + gw, S, 1 % S, lane);
-  for (int u = 0; u < U; u += 2) {
+  b_load<FMT, NMAT>(wb0, codes, scales, grp_of(0), S, 0, lane);
+  b_load<FMT, NMAT>(wb1, codes, scales, grp_of(1), S, k_of(1), lane);
+  // Down writes a column tile's results after its last k-step (an odd step:
+  // sweeps need S even), before the next weight prefetch is issued, so that
+  // later waits for activation loads never wait for those weights.  The
+  // scheduling barriers keep each prefetch after the step that frees its
+  // registers.
+  int u = 0;
+  for (; u + 1 < U; u += 2) {
     a_store<NS>(av, buf0, sr, sc);
-    if (u + 1 < U) a_load<NS>(av, arow, (u + 1) % S, sc);
+    a_load<NS>(av, arow, k_of(u + 1), sc);
     __syncthreads();
     tile_step<FMT, NMAT, NS>(acc, buf0, wb0, lane);
-    if (u + 2 < U)
-      b_load<FMT, NMAT>(wb0, codes, scales, (t.ct + (u + 2) / S) * (kBN<NMAT> / kFragRows) + gw, S, (u + 2) % S, lane);
-    if (u + 1 < U) {
-      a_store<NS>(av, buf1, sr, sc);
-      if (u + 2 < U) a_load<NS>(av, arow, (u + 2) % S, sc);
-      __syncthreads();
-      tile_step<FMT, NMAT, NS>(acc, buf1, wb1, lane);
-      if (u + 3 < U)
-        b_load<FMT, NMAT>(wb1, codes, scales, (t.ct + (u + 3) / S) * (kBN<NMAT> / kFragRows) + gw, S, (u + 3) % S, lane);
-      if constexpr (NMAT == 1) {  // sweeps (down only): S is even, a pass ends on the odd step
-        if ((u + 1) % S == S - 1) {
-          tile_epilogue<FMT, NMAT, NS>(t, acc, (t.ct + u / S) * (kBN<NMAT> / kFragRows) + gw, lane);
-          zero_acc<NMAT, NS>(acc);
-        }
+    __builtin_amdgcn_sched_barrier(0);
+    b_load<FMT, NMAT>(wb0, codes, scales, grp_of(u + 2), S, k_of(u + 2), lane);
+    a_store<NS>(av, buf1, sr, sc);
+    a_load<NS>(av, arow, k_of(u + 2), sc);
+    __syncthreads();
+    tile_step<FMT, NMAT, NS>(acc, buf1, wb1, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NMAT == 1) {
+      if ((u + 1) % S == S - 1) {
+        tile_epilogue<FMT, NMAT, NS>(t, acc, grp_of(u + 1), lane);
+        zero_acc<NMAT, NS>(acc);
       }
     }
+    b_load<FMT, NMAT>(wb1, codes, scales, grp_of(u + 3), S, k_of(u + 3), lane);
+  }
+  if (u < U) {  // odd step count: the last step (a pass end)
+    a_store<NS>(av, buf0, sr, sc);
+    __syncthreads();
+    tile_step<FMT, NMAT, NS>(acc, buf0, wb0, lane);
+    if constexpr (NMAT == 1) tile_epilogue<FMT, NMAT, NS>(t, acc, grp_of(u), lane);
   }
   if constexpr (NMAT == 2) tile_epilogue<FMT, NMAT, NS>(t, acc, t.ct * (kBN<NMAT> / kFragRows) + gw, lane);
 }
@@ -443,6 +458,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped(
 // a power of two that divides the column tile count.
 int sweep_len(int n_col_tiles, int S) {
   int n = 1;
+  if (S % 2) return n;  // a pass must end on an odd step
   while (n * 2 * S <= 16 && n_col_tiles % (n * 2) == 0) n *= 2;
   return n;
 }
@@ -480,7 +496,7 @@ hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
 }  // namespace
 
 size_t grouped_tiles_bytes(int T, int k, int E) {
-  // the FP4 formats use 128-row tiles and FP8 64-row tiles: size for the larger list
+  // the FP4 formats use 96-row tiles and FP8 32-row tiles: size for the longer list
   const int max_tiles = max_tiles_for<MOE_FMT_FP8_E4M3>(T * k, E);
   return align256((size_t)(2 * max_tiles + 1) * 4);
 }
