@@ -179,6 +179,16 @@ struct DownRows {
       if (s0 + i * nw < S) fd[i].load(codes, scales, (size_t)g * S + s0 + i * nw, lane);
   }
 
+  // Steps s0 .. s0+NB-1 (one wave per row group), with steps past the end
+  // re-loading the last one: the loads are unconditional, so a later wait for
+  // an older batch never waits for this one.
+  __device__ __forceinline__ void load_clamped(const uint8_t* __restrict__ codes,
+                                               const uint8_t* __restrict__ scales, int S, int g, int s0,
+                                               int lane) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) fd[i].load(codes, scales, (size_t)g * S + min(s0 + i, S - 1), lane);
+  }
+
   __device__ __forceinline__ void store(uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int S, int g,
                                         int s0, int nw, int lane) const {
 #pragma unroll
@@ -283,6 +293,115 @@ __global__ __launch_bounds__(512) void k_gateup_gemv(
   }
 }
 
+// Decode gate/up for layers with more (pair, 16-row group) units than the
+// chip holds workgroups at once.  A persistent workgroup owns `upw`
+// consecutive units of one token (units ordered by pair, then row group);
+// wave 0 computes the token's softmax/top-k once, then every wave streams its
+// k-steps of all those units through a ring of NB prefetched items (one item
+// = the gate and up fragments of one k-step): the next unit's weights are in
+// flight while the current unit is dotted, and no barrier runs inside the
+// stream.  Each unit's per-wave sums meet in LDS after the stream, in wave
+// order, so the results equal those of k_gateup_gemv bit for bit.
+constexpr int kStreamMaxUnits = 8;
+
+template <int FMT, int NB, int NV>
+__global__ __launch_bounds__(512) void k_gateup_topk_stream(
+    const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F, int E, int k, int T,
+    unsigned flags, const uint16_t* __restrict__ x, const float* __restrict__ logits,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int upw, uint16_t* __restrict__ hbuf) {
+  __shared__ __attribute__((aligned(16))) uint16_t xl[kMaxDim];
+  __shared__ float red[kStreamMaxUnits][8][2][16];
+  __shared__ int s_slot[16];
+  __shared__ TopkScratch s_topk;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int G = F / kFragRows, S = H / kFragK, per = (S + nw - 1) / nw;
+  const int u0 = blockIdx.x * upw, nu = min(upw, T * k * G - u0);
+  const int t = u0 / (k * G);  // upw divides k*G: all units of this workgroup belong to token t
+  const uint4* xs4 = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+  for (int i = threadIdx.x; i < H / 8; i += blockDim.x) reinterpret_cast<uint4*>(xl)[i] = xs4[i];
+  if (w == 0) {
+    float v[NV];
+    wave_load_logits<NV>(logits + (size_t)t * E, E, v);
+    int idx;
+    float wt;
+    wave_topk_regs<NV>(v, E, k, flags, idx, wt, s_topk);
+    if (lane < k) {
+      s_slot[lane] = idx;
+      if (u0 % (k * G) == 0) {
+        topk_idx[(size_t)t * k + lane] = idx;
+        topk_w[(size_t)t * k + lane] = wt;
+      }
+    }
+  }
+  __syncthreads();
+  const int n_items = nu * per;
+  // load cursor (unit, item within unit); items past the end re-load the last
+  // one, so every load is unconditional
+  int lu = 0, lj = 0;
+  const auto load_item = [&](Frag<FMT>& fg, Frag<FMT>& fu) {
+    const int cu = lu < nu ? lu : nu - 1, cj = lu < nu ? lj : per - 1;
+    const int u = u0 + cu, g = u % G, pj = (u / G) % k;
+    const uint8_t* blob = pool + (size_t)s_slot[pj] * stride;
+    const size_t f = (size_t)g * S + min(w + nw * cj, S - 1);
+    fg.load(blob + L.cg, blob + L.sg, f, lane);
+    fu.load(blob + L.cu, blob + L.su, f, lane);
+    if (++lj == per) {
+      lj = 0;
+      ++lu;
+    }
+  };
+  Frag<FMT> fg[NB], fu[NB];
+#pragma unroll
+  for (int r = 0; r < NB; ++r) load_item(fg[r], fu[r]);
+  float ag = 0.0f, au = 0.0f;
+  int cu = 0, cj = 0;  // compute cursor
+  for (int i0 = 0; i0 < n_items; i0 += NB) {
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      if (i0 + r < n_items) {
+        const int st = w + nw * cj;
+        if (st < S) {
+          uint32_t xs[16];
+          load_xslice(xl + kFragK * st + 32 * (lane >> 4), xs);
+          ag += fg[r].dot(xs);
+          au += fu[r].dot(xs);
+        }
+        if (cj == per - 1) {  // this wave's last step of unit cu
+          ag = row_lanes_sum(ag);
+          au = row_lanes_sum(au);
+          if (lane < 16) {
+            red[cu][w][0][lane] = ag;
+            red[cu][w][1][lane] = au;
+          }
+          ag = 0.0f;
+          au = 0.0f;
+          cj = 0;
+          ++cu;
+        } else {
+          ++cj;
+        }
+      }
+      load_item(fg[r], fu[r]);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 16 * nu) {
+    const int ul = threadIdx.x >> 4, row = threadIdx.x & 15;
+    const int u = u0 + ul, g = u % G, q = u / G;
+    float Gs = 0.0f, Us = 0.0f;
+    for (int i = 0; i < nw; ++i) {
+      Gs += red[ul][i][0][row];
+      Us += red[ul][i][1][row];
+    }
+    if constexpr (FMT == MOE_FMT_NVFP4) {
+      const float* tau = reinterpret_cast<const float*>(pool + (size_t)s_slot[q % k] * stride + L.tau);
+      Gs *= tau[0];
+      Us *= tau[1];
+    }
+    hbuf[(size_t)q * F + kFragRows * g + row] = f32_to_bf16_rne(silu_f32(Gs) * Us);
+  }
+}
+
 // y rows 16*blockIdx.x.. of pair blockIdx.y (or pair_subset entry).
 template <int FMT, int NB>
 __global__ __launch_bounds__(512) void k_down_gemv(
@@ -343,16 +462,25 @@ __global__ __launch_bounds__(1024) void k_down_combine_gemv(
   const uint8_t* blob = pool + (size_t)slot * stride;
   uint16_t* hl = hl_dyn + (size_t)j * F;
   const int S = F / kFragK;
-  DownRows<FMT, NB> d;
-  d.load(blob + L.cd, blob + L.sd, S, g, 0, 1, lane);
+  // batches of NB steps through two register sets: batch b+2 is requested as
+  // soon as batch b is consumed, so one batch is always in flight
+  const int nb = (S + NB - 1) / NB;
+  DownRows<FMT, NB> d0, d1;
+  d0.load_clamped(blob + L.cd, blob + L.sd, S, g, 0, lane);
+  if (nb > 1) d1.load_clamped(blob + L.cd, blob + L.sd, S, g, NB, lane);
   const uint4* h4 = reinterpret_cast<const uint4*>(hbuf + (size_t)q * F);
   for (int i = lane; i < F / 8; i += 64) reinterpret_cast<uint4*>(hl)[i] = h4[i];
   __syncthreads();
-  float a = d.dot(hl, S, 0, 1, lane);
-  for (int s0 = NB; s0 < S; s0 += NB) {
-    d.load(blob + L.cd, blob + L.sd, S, g, s0, 1, lane);
-    a += d.dot(hl, S, s0, 1, lane);
+  float a = 0.0f;
+  int b = 0;
+  for (; b + 2 < nb; b += 2) {
+    a += d0.dot(hl, S, b * NB, 1, lane);
+    d0.load_clamped(blob + L.cd, blob + L.sd, S, g, (b + 2) * NB, lane);
+    a += d1.dot(hl, S, (b + 1) * NB, 1, lane);
+    d1.load_clamped(blob + L.cd, blob + L.sd, S, g, (b + 3) * NB, lane);
   }
+  a += d0.dot(hl, S, b * NB, 1, lane);
+  if (b + 1 < nb) a += d1.dot(hl, S, (b + 1) * NB, 1, lane);
   a = row_lanes_sum(a);
   if (lane < 16) {
     if constexpr (FMT == MOE_FMT_NVFP4) a *= reinterpret_cast<const float*>(blob + L.tau)[2];
@@ -392,12 +520,47 @@ hipError_t launch_gateup(const FfnArgs& a, hipStream_t s) {
   return launch_gateup_t<FMT, false, 1>(a, nullptr, 0, nullptr, nullptr, s);
 }
 
+// Workgroups of k_gateup_topk_stream<FMT, NB, NV> the current device holds at once.
+template <int FMT, int NB, int NV>
+int stream_capacity(int block) {
+  static int cap = 0;  // per process: one device model
+  if (cap == 0) {
+    int dev = 0, n_cu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&k_gateup_topk_stream<FMT, NB, NV>), block, 0) != hipSuccess)
+      return 0;
+    cap = n_cu * per_cu;
+  }
+  return cap;
+}
+
+// Decode gate/up with in-block top-k: one unit (pair, 16-row group) per
+// workgroup when the chip holds them all at once, else the streaming kernel
+// with `upw` units per workgroup (a power of two <= 8, so it divides k*G).
+template <int FMT, int NV>
+hipError_t launch_gateup_topk_nv(const FfnArgs& a, const float* logits, unsigned flags, int32_t* idx, float* w,
+                                 hipStream_t s) {
+  constexpr int NB = 2;  // ring depth: the fastest of 1, 2, 3, 4 and 8 measured at hidden 6144
+  const int S = a.H / kFragK, nw = gemv_waves(S), G = a.F / kFragRows;
+  const int n_units = a.T * a.k * G;
+  const int cap = stream_capacity<FMT, NB, NV>(64 * nw);
+  const int old_cap = 256;  // k_gateup_gemv with one 8-wave workgroup per compute unit
+  if (n_units <= old_cap || cap <= 0) return launch_gateup_t<FMT, true, NV>(a, logits, flags, idx, w, s);
+  int upw = 1;
+  while (upw < kStreamMaxUnits && (n_units + upw - 1) / upw > cap) upw *= 2;
+  hipLaunchKernelGGL((k_gateup_topk_stream<FMT, NB, NV>), dim3((n_units + upw - 1) / upw), dim3(64 * nw), 0, s,
+                     a.pool, a.stride, a.L, a.H, a.F, a.E, a.k, a.T, flags, a.x, logits, idx, w, upw, a.hbuf);
+  return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t launch_gateup_topk(const FfnArgs& a, const float* logits, unsigned flags, int32_t* idx, float* w,
                               hipStream_t s) {
-  if (a.E <= 64) return launch_gateup_t<FMT, true, 1>(a, logits, flags, idx, w, s);
-  if (a.E <= 256) return launch_gateup_t<FMT, true, 4>(a, logits, flags, idx, w, s);
-  return launch_gateup_t<FMT, true, 16>(a, logits, flags, idx, w, s);
+  if (a.E <= 64) return launch_gateup_topk_nv<FMT, 1>(a, logits, flags, idx, w, s);
+  if (a.E <= 256) return launch_gateup_topk_nv<FMT, 4>(a, logits, flags, idx, w, s);
+  return launch_gateup_topk_nv<FMT, 16>(a, logits, flags, idx, w, s);
 }
 
 template <int FMT>

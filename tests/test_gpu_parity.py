@@ -87,9 +87,12 @@ def test_decode_35b_shape(fmt):
             assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
 
 
-def test_decode_753b_shape_sampled():
-    """hidden 6144, 256 experts, top-8, width 2048 (one layer, one token, NVFP4)."""
-    fmt, H, E, F, k = NV, 6144, 256, 2048, 8
+@pytest.mark.parametrize("fmt", [NV, F8])
+def test_decode_753b_shape_sampled(fmt):
+    """hidden 6144, 256 experts, top-8, width 2048 (one layer, one token): the
+    expert FFN against the oracle, and moe_layer_forward (whose gate/up streams
+    several row groups per workgroup at this size) equal to it bit for bit."""
+    H, E, F, k = 6144, 256, 2048, 8
     L = Layer(fmt, H, E, F, cfg=4, layer=0, w_std=0.015, eager=False)
     x = ar1_states(0, 4, 1, H, [L.router], k)
     oidx, _, _ = moe.route(x, L.router, k)
@@ -104,6 +107,10 @@ def test_decode_753b_shape_sampled():
     ref = moe.moe_layer(fmt, x, L.router, L.experts, k)
     assert_rows_close(y.cpu().numpy(), ref["y"].reshape(k, H), what="y")
     assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
+    idx2, w2, out2 = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, xd, R)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx) and torch.equal(w2, w)
+    assert torch.equal(out2, out)
 
 
 # ----------------------------------------------------------------- routing
