@@ -142,7 +142,9 @@ __device__ __forceinline__ float group_sum(float v) {
   }
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), with the hardware reciprocal (about 1 ulp) in
+// place of a full-precision division
+__device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // ---------------------------------------------------------------- chunk dot products
 // One 16-byte code chunk against the matching x slice (bf16 pairs in registers).

@@ -8,9 +8,11 @@
 //
 // Pairs arrive sorted by expert (pair_perm / expert_off).  A device-built tile
 // list holds one (expert, first row) entry per 96 rows of each expert (32 for
-// FP8, whose per-step partial sums need more registers).  A workgroup (4 waves) owns one tile x 128 output columns per matrix:
-// wave w takes the two 16-row weight fragments of columns [32w, 32w+32) and all
-// rows of the tile (up to six 16-row subtiles, v_mfma_f32_16x16x32_bf16), so
+// FP8, whose per-step partial sums need more registers).  A workgroup of NW
+// waves (8 for the FP4 formats, 4 for FP8) owns one tile x NW*32 output columns
+// per matrix for gate/up (NW*64 for down): wave w takes the weight fragments
+// of its 32 (64) columns and all rows of the tile (up to six 16-row subtiles,
+// v_mfma_f32_16x16x32_bf16), so
 // each dequantized weight operand feeds one MFMA per subtile and an expert's
 // weights are fetched and dequantized once per column tile whenever it has at
 // most 96 rows.  The subtile count is a template parameter chosen per tile,
@@ -41,15 +43,15 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int NWAVE = 4;     // waves per workgroup
 constexpr int BK = kFragK;   // k per step
 // 16-column weight groups per wave: each activation operand read from LDS
 // feeds NMAT * CG MFMAs; down (one matrix) takes four groups so that LDS reads
 // stay at half the MFMA rate, gate/up two (its two matrices double the reuse).
 template <int NMAT>
 constexpr int kCG = NMAT == 2 ? 2 : 4;
-template <int NMAT>
-constexpr int kBN = NWAVE * kCG<NMAT> * kFragRows;  // output columns per matrix per column tile
+// output columns per matrix per column tile of a workgroup of NW waves
+template <int NMAT, int NW>
+constexpr int kBN = NW * kCG<NMAT> * kFragRows;
 constexpr int ROWB = BK * 2;                 // LDS bytes per activation row per step
 
 template <int FMT>
@@ -148,6 +150,7 @@ struct BFrag {
 };
 
 constexpr int kPatchLd = 68, kPatchFloats = 16 * kPatchLd;  // down epilogue patch per wave (16 x 64 fp32, padded)
+constexpr int kHPatchLd = 40, kHPatchHalfs = 16 * kHPatchLd;  // gate/up epilogue patch per wave (16 x 32 bf16, padded)
 
 struct TileArgs {
   uint8_t* epi;               // LDS: down epilogue patches
@@ -161,20 +164,24 @@ struct TileArgs {
   float* yout;
 };
 
-// Activation staging: thread -> rows tid/16 + 16j (j < NS), 16-byte chunk tid%16.
+// Activation staging by the 64*NW threads: thread -> rows tid/16 + 4*NW*j
+// (j < NP), 16-byte chunk tid%16, NP passes covering the tile's 16*NS rows.
 // Row r's chunk c sits at slot c ^ (r & 15): sixteen lanes writing one row, or
 // reading one chunk of sixteen consecutive rows, touch sixteen distinct slots.
-template <int NS>
-__device__ __forceinline__ void a_load(u32x4_t (&av)[NS], const uint16_t* const (&arow)[NS], int s, int sc) {
+template <int NS, int NW>
+constexpr int kStagePasses = (4 * NS + NW - 1) / NW;
+
+template <int NP>
+__device__ __forceinline__ void a_load(u32x4_t (&av)[NP], const uint16_t* const (&arow)[NP], int s, int sc) {
 #pragma unroll
-  for (int j = 0; j < NS; ++j) av[j] = reinterpret_cast<const u32x4_t*>(arow[j] + s * BK)[sc];
+  for (int j = 0; j < NP; ++j) av[j] = reinterpret_cast<const u32x4_t*>(arow[j] + s * BK)[sc];
 }
 
-template <int NS>
-__device__ __forceinline__ void a_store(const u32x4_t (&av)[NS], uint8_t* __restrict__ buf, int sr, int sc) {
+template <int NP, int NW>
+__device__ __forceinline__ void a_store(const u32x4_t (&av)[NP], uint8_t* __restrict__ buf, int sr, int sc) {
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int r = sr + kFragRows * j;
+  for (int j = 0; j < NP; ++j) {
+    const int r = sr + 4 * NW * j;
     *reinterpret_cast<u32x4_t*>(buf + r * ROWB + ((sc ^ (r & 15)) << 4)) = av[j];
   }
 }
@@ -256,21 +263,31 @@ __device__ __forceinline__ void tile_epilogue(const TileArgs& t, const floatx4_t
                                               int lane) {
   const int am = lane & 15, aq = lane >> 4;
   const float* tau = reinterpret_cast<const float*>(t.blob + t.L.tau);
+  if constexpr (NMAT == 2) {
+    // h = bf16(silu(g) * u): each 16-row subtile (this wave's 32 columns) goes
+    // through the wave's LDS patch so that a store covers 16 B per lane and the
+    // 64 contiguous bytes of a row per 4 lanes
+    const float tg = FMT == MOE_FMT_NVFP4 ? tau[0] : 1.0f, tu = FMT == MOE_FMT_NVFP4 ? tau[1] : 1.0f;
+    uint16_t* patch = reinterpret_cast<uint16_t*>(t.epi) + (threadIdx.x >> 6) * kHPatchHalfs;
+    const int col0 = g0 * kFragRows;
 #pragma unroll
-  for (int cg = 0; cg < kCG<NMAT>; ++cg) {
-    const int col = (g0 + cg) * kFragRows + am;
-    if constexpr (NMAT == 2) {
-      const float tg = FMT == MOE_FMT_NVFP4 ? tau[0] : 1.0f, tu = FMT == MOE_FMT_NVFP4 ? tau[1] : 1.0f;
+    for (int r = 0; r < NS; ++r) {
 #pragma unroll
-      for (int r = 0; r < NS; ++r)
+      for (int cg = 0; cg < kCG<NMAT>; ++cg)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int row = kFragRows * r + 4 * aq + v;
-          if (row < t.rows) {
-            const float gv = acc[0][cg][r][v] * tg, uv = acc[1][cg][r][v] * tu;
-            t.hout[(size_t)(t.row_base + row) * t.N + col] = f32_to_bf16_rne(silu_f32(gv) * uv);
-          }
+          const float gv = acc[0][cg][r][v] * tg, uv = acc[1][cg][r][v] * tu;
+          patch[(4 * aq + v) * kHPatchLd + 16 * cg + am] = f32_to_bf16_rne(silu_f32(gv) * uv);
         }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int rl = lane >> 2, c8 = 8 * (lane & 3), row = kFragRows * r + rl;
+      const uint4 val = *reinterpret_cast<const uint4*>(patch + rl * kHPatchLd + c8);
+      if (row < t.rows) *reinterpret_cast<uint4*>(t.hout + (size_t)(t.row_base + row) * t.N + col0 + c8) = val;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
   if constexpr (NMAT == 1) {
@@ -313,9 +330,10 @@ __device__ __forceinline__ void zero_acc(floatx4_t (&acc)[NMAT][kCG<NMAT>][NS]) 
       for (int r = 0; r < NS; ++r) acc[m][cg][r] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-// One tile with NS 16-row subtiles (rows <= 16*NS).
-template <int FMT, int NMAT, int NS>
+// One tile with NS 16-row subtiles (rows <= 16*NS), NW waves.
+template <int FMT, int NMAT, int NS, int NW>
 __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restrict__ As) {
+  constexpr int NP = kStagePasses<NS, NW>;
   constexpr int RB = kTileRows<FMT>;       // LDS rows per buffer
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = t.K / BK;
@@ -330,15 +348,16 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
     scales[NMAT - 1] = t.blob + t.L.su;
   }
 
-  // activation staging rows (rows past the end repeat the last row; never stored)
+  // activation staging rows (rows past the end repeat the last row; they land
+  // in buffer rows no subtile reads)
   const int sr = tid >> 4, sc = tid & 15;
-  const uint16_t* arow[NS];
+  const uint16_t* arow[NP];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int p = t.row_base + min(sr + kFragRows * j, t.rows - 1);
+  for (int j = 0; j < NP; ++j) {
+    const int p = t.row_base + min(sr + 4 * NW * j, t.rows - 1);
     arow[j] = t.a_by_token ? t.a_src + (size_t)(t.pair_perm[p] / t.k_top) * t.K : t.a_src + (size_t)p * t.K;
   }
-  u32x4_t av[NS];
+  u32x4_t av[NP];
   BFrag<FMT> wb0[NMAT][kCG<NMAT>], wb1[NMAT][kCG<NMAT>];
   floatx4_t acc[NMAT][kCG<NMAT>][NS];
 #pragma unroll
@@ -359,11 +378,11 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
   // Prefetches past the last step re-load the last step's data (cached, never
   // used): every load is unconditional, so the compiler's wait counts stay
   // exact and a wait for the activations never waits for a newer weight load.
-  const auto grp_of = [&](int v) { return (t.ct + min(v, U - 1) / S) * (kBN<NMAT> / kFragRows) + gw; };
+  const auto grp_of = [&](int v) { return (t.ct + min(v, U - 1) / S) * (kBN<NMAT, NW> / kFragRows) + gw; };
   const auto k_of = [&](int v) { return min(v, U - 1) % S; };
   uint8_t* buf0 = As;
   uint8_t* buf1 = As + RB * ROWB;
-  a_load<NS>(av, arow, 0, sc);
+  a_load<NP>(av, arow, 0, sc);
   b_load<FMT, NMAT>(wb0, codes, scales, grp_of(0), S, 0, lane);
   b_load<FMT, NMAT>(wb1, codes, scales, grp_of(1), S, k_of(1), lane);
   // Down writes a column tile's results after its last k-step (an odd step:
@@ -373,14 +392,14 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
   // registers.
   int u = 0;
   for (; u + 1 < U; u += 2) {
-    a_store<NS>(av, buf0, sr, sc);
-    a_load<NS>(av, arow, k_of(u + 1), sc);
+    a_store<NP, NW>(av, buf0, sr, sc);
+    a_load<NP>(av, arow, k_of(u + 1), sc);
     __syncthreads();
     tile_step<FMT, NMAT, NS>(acc, buf0, wb0, lane);
     __builtin_amdgcn_sched_barrier(0);
     b_load<FMT, NMAT>(wb0, codes, scales, grp_of(u + 2), S, k_of(u + 2), lane);
-    a_store<NS>(av, buf1, sr, sc);
-    a_load<NS>(av, arow, k_of(u + 2), sc);
+    a_store<NP, NW>(av, buf1, sr, sc);
+    a_load<NP>(av, arow, k_of(u + 2), sc);
     __syncthreads();
     tile_step<FMT, NMAT, NS>(acc, buf1, wb1, lane);
     __builtin_amdgcn_sched_barrier(0);
@@ -393,25 +412,25 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
     b_load<FMT, NMAT>(wb1, codes, scales, grp_of(u + 3), S, k_of(u + 3), lane);
   }
   if (u < U) {  // odd step count: the last step (a pass end)
-    a_store<NS>(av, buf0, sr, sc);
+    a_store<NP, NW>(av, buf0, sr, sc);
     __syncthreads();
     tile_step<FMT, NMAT, NS>(acc, buf0, wb0, lane);
     if constexpr (NMAT == 1) tile_epilogue<FMT, NMAT, NS>(t, acc, grp_of(u), lane);
   }
-  if constexpr (NMAT == 2) tile_epilogue<FMT, NMAT, NS>(t, acc, t.ct * (kBN<NMAT> / kFragRows) + gw, lane);
+  if constexpr (NMAT == 2) tile_epilogue<FMT, NMAT, NS>(t, acc, t.ct * (kBN<NMAT, NW> / kFragRows) + gw, lane);
 }
 
 // NMAT = 2: gate/up with SwiGLU into hout (expert-sorted rows, width N).
 // NMAT = 1: down into y rows of the original pairs.
-template <int FMT, int NMAT>
-__global__ __launch_bounds__(256, 2) void k_grouped(
+template <int FMT, int NMAT, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_grouped(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int K, int N, int k_top,
     const uint16_t* __restrict__ a_src, int a_by_token, const int32_t* __restrict__ pair_perm,
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ tile_e,
     const int32_t* __restrict__ tile_m0, const int32_t* __restrict__ n_tiles, int n_sweeps, int npass,
     uint16_t* __restrict__ hout, float* __restrict__ yout) {
   __shared__ __attribute__((aligned(16))) uint8_t As[2 * kTileRows<FMT> * ROWB +
-                                                   (NMAT == 1 ? NWAVE * kPatchFloats * 4 : 0)];
+                                                   (NMAT == 1 ? NW * kPatchFloats * 4 : NW * kHPatchHalfs * 2)];
   __shared__ int s_rows[NMAT == 1 ? kTileRows<FMT> : 1];
   // A workgroup takes one row tile and a sweep of npass consecutive column
   // tiles.  Workgroups are handed to the 8 XCDs round-robin by index; within
@@ -441,14 +460,14 @@ __global__ __launch_bounds__(256, 2) void k_grouped(
   t.hout = hout;
   t.yout = yout;
   switch ((t.rows + kFragRows - 1) / kFragRows) {
-    case 1: grouped_tile<FMT, NMAT, 1>(t, As); break;
-    case 2: grouped_tile<FMT, NMAT, 2>(t, As); break;
-    case 3: grouped_tile<FMT, NMAT, 3>(t, As); break;
-    case 4: grouped_tile<FMT, NMAT, 4>(t, As); break;
+    case 1: grouped_tile<FMT, NMAT, 1, NW>(t, As); break;
+    case 2: grouped_tile<FMT, NMAT, 2, NW>(t, As); break;
+    case 3: grouped_tile<FMT, NMAT, 3, NW>(t, As); break;
+    case 4: grouped_tile<FMT, NMAT, 4, NW>(t, As); break;
     default:
       if constexpr (kSubMax<FMT> >= 6) {
-        if (t.rows > 5 * kFragRows) grouped_tile<FMT, NMAT, 6>(t, As);
-        else grouped_tile<FMT, NMAT, 5>(t, As);
+        if (t.rows > 5 * kFragRows) grouped_tile<FMT, NMAT, 6, NW>(t, As);
+        else grouped_tile<FMT, NMAT, 5, NW>(t, As);
       }
       break;
   }
@@ -469,25 +488,39 @@ int max_tiles_for(int n_pairs, int E) {
   return ((n_pairs + RB - 1) / RB + E + 7) / 8 * 8;
 }
 
+// One grouped kernel: NMAT = 2 gate/up (A = x rows by token, K = H, N = F,
+// h rows in expert order), NMAT = 1 down (A = h rows in expert order, K = F,
+// N = H, y rows of the pairs).  FP4 formats: eight waves (twice the columns
+// per staged activation tile, so half the activation reads) when N allows;
+// else four.
+template <int FMT, int NMAT>
+void launch_grouped_k(const FfnArgs& a, int max_tiles, const int32_t* tile_e, const int32_t* tile_m0,
+                      const int32_t* n_tiles, float* y, hipStream_t s) {
+  const int K = NMAT == 2 ? a.H : a.F, N = NMAT == 2 ? a.F : a.H;
+  const uint16_t* a_src = NMAT == 2 ? a.x : a.hbuf;
+#define GK(NW)                                                                                                \
+  {                                                                                                           \
+    const int nct = N / kBN<NMAT, NW>;                                                                        \
+    const int np = NMAT == 2 ? 1 : sweep_len(nct, K / BK); /* gate/up keeps its epilogue out of the loop */   \
+    hipLaunchKernelGGL((k_grouped<FMT, NMAT, NW>), dim3(max_tiles * (nct / np)), dim3(64 * NW), 0, s, a.pool, \
+                       a.stride, a.L, K, N, a.k, a_src, NMAT == 2 ? 1 : 0, a.pair_perm, a.expert_off, tile_e,  \
+                       tile_m0, n_tiles, nct / np, np, NMAT == 2 ? a.hbuf : nullptr, NMAT == 2 ? nullptr : y); \
+  }
+  if (FMT != MOE_FMT_FP8_E4M3 && N % kBN<NMAT, 8> == 0) GK(8) else GK(4)  // FP8: 32-row tiles, two workgroups per CU
+#undef GK
+}
+
 template <int FMT>
 hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
   const int n_pairs = a.T * a.k;
   const int max_tiles = max_tiles_for<FMT>(n_pairs, a.E);
   int32_t *tile_e = tiles, *tile_m0 = tiles + max_tiles, *n_tiles = tiles + 2 * max_tiles;
-  if (a.F % kBN<2> || a.H % kBN<1> || a.H % BK || a.F % BK) return hipErrorInvalidValue;
+  if (a.F % kBN<2, 4> || a.H % kBN<1, 4> || a.H % BK || a.F % BK) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E, kTileRows<FMT>, tile_e,
                      tile_m0, n_tiles);
-  // gate/up: A = x rows by token, K = H, N = F, h rows in expert order (hbuf)
-  const int nct_gu = a.F / kBN<2>, np_gu = 1;  // gate/up keeps its epilogue out of the loop
-  hipLaunchKernelGGL((k_grouped<FMT, 2>), dim3(max_tiles * (nct_gu / np_gu)), dim3(256), 0, s, a.pool,
-                     a.stride, a.L, a.H, a.F, a.k, a.x, 1, a.pair_perm, a.expert_off, tile_e, tile_m0,
-                     n_tiles, nct_gu / np_gu, np_gu, a.hbuf, nullptr);
-  // down: A = h rows in expert order, K = F, N = H, y rows of the pairs
   float* y = a.y ? a.y : a.ybuf;
-  const int nct_d = a.H / kBN<1>, np_d = sweep_len(nct_d, a.F / BK);
-  hipLaunchKernelGGL((k_grouped<FMT, 1>), dim3(max_tiles * (nct_d / np_d)), dim3(256), 0, s, a.pool, a.stride,
-                     a.L, a.F, a.H, a.k, a.hbuf, 0, a.pair_perm, a.expert_off, tile_e, tile_m0,
-                     n_tiles, nct_d / np_d, np_d, nullptr, y);
+  launch_grouped_k<FMT, 2>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
+  launch_grouped_k<FMT, 1>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.out) return e;
   return launch_combine(y, a.topk_w, a.T, a.H, a.k, a.out, s);
