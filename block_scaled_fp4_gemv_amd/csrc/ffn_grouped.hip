@@ -516,8 +516,9 @@ hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
   const int max_tiles = max_tiles_for<FMT>(n_pairs, a.E);
   int32_t *tile_e = tiles, *tile_m0 = tiles + max_tiles, *n_tiles = tiles + 2 * max_tiles;
   if (a.F % kBN<2, 4> || a.H % kBN<1, 4> || a.H % BK || a.F % BK) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E, kTileRows<FMT>, tile_e,
-                     tile_m0, n_tiles);
+  if (!a.tiles_ready)  // else the permutation kernel wrote the list (grouped_tile_rows / grouped_max_tiles)
+    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E, kTileRows<FMT>, tile_e,
+                       tile_m0, n_tiles);
   float* y = a.y ? a.y : a.ybuf;
   launch_grouped_k<FMT, 2>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
   launch_grouped_k<FMT, 1>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
@@ -532,6 +533,15 @@ size_t grouped_tiles_bytes(int T, int k, int E) {
   // the FP4 formats use 96-row tiles and FP8 32-row tiles: size for the longer list
   const int max_tiles = max_tiles_for<MOE_FMT_FP8_E4M3>(T * k, E);
   return align256((size_t)(2 * max_tiles + 1) * 4);
+}
+
+int grouped_tile_rows(int fmt) {
+  return fmt == MOE_FMT_FP8_E4M3 ? kTileRows<MOE_FMT_FP8_E4M3> : kTileRows<MOE_FMT_NVFP4>;
+}
+
+int grouped_max_tiles(int fmt, int n_pairs, int E) {
+  return fmt == MOE_FMT_FP8_E4M3 ? max_tiles_for<MOE_FMT_FP8_E4M3>(n_pairs, E)
+                                 : max_tiles_for<MOE_FMT_NVFP4>(n_pairs, E);
 }
 
 hipError_t launch_ffn_grouped(const FfnArgs& a, hipStream_t s) {

@@ -29,8 +29,13 @@ struct FfnArgs {
   uint16_t* hbuf;  // workspace [T*k][F] bf16
   float* ybuf;     // workspace [T*k][H] fp32 (grouped path with fused combine)
   int32_t* tiles;  // workspace: grouped-path tile list (grouped_tiles_bytes)
+  int tiles_ready;  // the tile list was written with the permutation
 };
 size_t grouped_tiles_bytes(int T, int k, int E);
+// Tile list geometry of the grouped path for a format: rows per tile and the
+// list capacity (for the permutation kernel to write it).
+int grouped_tile_rows(int fmt);
+int grouped_max_tiles(int fmt, int n_pairs, int E);
 
 // GEMV path: gate/up + SwiGLU into hbuf, then down (+ combine when out != NULL).
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s);
@@ -52,9 +57,12 @@ struct RouteArgs {
   float* topk_w;
   int32_t* pair_perm;
   int32_t* expert_off;
+  // optional grouped-path tile list built with the permutation (tile_rows > 0):
+  // tiles = [tile_e (max_tiles) | tile_m0 (max_tiles) | n_tiles]
+  int32_t* tiles;
+  int tile_rows, max_tiles;
   // workspace carve-up
   float* logits;       // [T][E]
-  int32_t* chunk_cnt;  // [n_chunks][E]
   uint16_t* planes;    // [3][E][H] bf16 split of the router (T > 4)
 };
 size_t route_ws_bytes(int T, int H, int E, int k);

@@ -364,11 +364,17 @@ int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, in
   }
   r.pair_perm = perm;
   r.expert_off = off;
+  const bool grouped = (long long)T * k >= 2LL * E;
+  if (grouped) {  // the permutation kernel also writes the grouped path's tile list
+    r.tiles = a.tiles;
+    r.tile_rows = grouped_tile_rows(fmt);
+    r.max_tiles = grouped_max_tiles(fmt, T * k, E);
+    a.tiles_ready = 1;
+  }
   e = launch_route(r, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer_forward(route)");
   a.pair_perm = perm;
   a.expert_off = off;
-  const bool grouped = (long long)T * k >= 2LL * E;
   e = grouped ? launch_ffn_grouped(a, s) : launch_ffn_gemv(a, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_layer_forward(ffn)");
 }

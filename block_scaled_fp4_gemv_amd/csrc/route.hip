@@ -14,7 +14,6 @@
 
 namespace {
 
-constexpr int kPermChunk = 256;  // pairs per permutation block
 constexpr int kMaxE = 1024;
 
 // ------------------------------------------------------- small-T router (decode)
@@ -193,56 +192,21 @@ hipError_t topk_impl(const float* logits, int T, int E, int k, unsigned flags, i
 }
 
 // ------------------------------------------------------------ permutation
-// Stable counting sort of the pairs by expert, in three kernels (no device-wide
-// fences): per-chunk expert counts, one block turning them into expert_off and
-// per-chunk base offsets, then a scatter that ranks each pair among the earlier
-// pairs of its chunk with the same expert.
-__global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ idx, int n, int E,
-                                                    int32_t* __restrict__ chunk_cnt) {
-  __shared__ int cnt[kMaxE];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
-  __syncthreads();
-  const int q = blockIdx.x * kPermChunk + threadIdx.x;
-  if (q < n) atomicAdd(&cnt[idx[q]], 1);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_cnt[(size_t)blockIdx.x * E + e] = cnt[e];
-}
+// Stable counting sort of the pairs by expert in one kernel: workgroup e
+// histograms all pair experts in LDS (every workgroup the same histogram),
+// takes its expert's offset from the exclusive scan, then writes the pairs of
+// expert e in ascending pair order.  Wave w owns the w-th quarter of the pairs
+// and walks it 64 pairs at a time (one coalesced load per lane); a ballot
+// ranks the matches inside a 64-pair chunk and the waves' match counts, scanned
+// once, order the quarters.  With tile_rows > 0 it also writes the grouped
+// path's tile list (one entry per tile_rows pairs of each expert, in expert
+// order).
+constexpr int kPermThreads = 256, kPermWaves = kPermThreads / 64, kPermUnroll = 64;
 
-// One workgroup: expert e's column of chunk counts is split over tpe = 1024/E
-// threads (contiguous chunk ranges, up to 16 counts kept in registers), the
-// per-thread sums are combined in LDS, an exclusive scan over the expert totals
-// gives expert_off, and each thread rewrites its counts as running offsets.
-__global__ __launch_bounds__(1024) void k_perm_scan(int nchunk, int E, int32_t* __restrict__ chunk_cnt,
-                                                    int32_t* __restrict__ expert_off) {
-  __shared__ int s_part[1024];
-  __shared__ int s_tot[kMaxE];
-  __shared__ int s_off[kMaxE];
-  __shared__ int wsum[16];
-  const int tid = threadIdx.x, tpe = blockDim.x / E;
-  const int e = tid / tpe, sub = tid % tpe;
-  const bool valid = e < E;
-  const int per = (nchunk + tpe - 1) / tpe, c0 = sub * per, c1 = min(nchunk, c0 + per);
-  int v[16];
-  int sum = 0;
-  if (valid) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = c0 + i < c1 ? chunk_cnt[(size_t)(c0 + i) * E + e] : 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sum += v[i];
-    for (int c = c0 + 16; c < c1; ++c) sum += chunk_cnt[(size_t)c * E + e];
-  }
-  s_part[tid] = sum;
-  __syncthreads();
-  int before = 0;  // this thread's offset inside its expert
-  if (valid) {
-    for (int j = 0; j < sub; ++j) before += s_part[e * tpe + j];
-    if (sub == tpe - 1) s_tot[e] = before + sum;
-  }
-  __syncthreads();
-  // exclusive scan of the expert totals (experts on threads 0..E-1)
-  const int lane = tid & 63, wave = tid >> 6;
-  const int t = tid < E ? s_tot[tid] : 0;
-  int incl = t;
+// Exclusive scan over the 256 threads' values; *total = the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int n = __shfl_up(incl, o);
@@ -250,53 +214,105 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int nchunk, int E, int32_t* 
   }
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
-  if (tid < E) {
-    s_off[tid] = base + incl - t;
-    expert_off[tid] = base + incl - t;
-    if (tid == E - 1) expert_off[E] = base + incl;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kPermWaves; ++w) {
+    base += w < wave ? wsum[w] : 0;
+    tot += wsum[w];
   }
   __syncthreads();
-  if (valid) {
-    int run = s_off[e] + before;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (c0 + i < c1) {
-        chunk_cnt[(size_t)(c0 + i) * E + e] = run;
-        run += v[i];
-      }
-    for (int c = c0 + 16; c < c1; ++c) {
-      const size_t i = (size_t)c * E + e;
-      const int x = chunk_cnt[i];
-      chunk_cnt[i] = run;
-      run += x;
-    }
-  }
+  *total = tot;
+  return base + incl - v;
 }
 
-__global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ idx, int n, int E,
-                                                      const int32_t* __restrict__ chunk_base,
-                                                      int32_t* __restrict__ pair_perm) {
-  __shared__ int wcnt[4][kMaxE];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 4 * E; i += blockDim.x) wcnt[i / E][i % E] = 0;
+// ONE: every wave's quarter fits one batch of kPermUnroll chunks (n <=
+// 4 * 64 * kPermUnroll); its pair experts stay in registers between the passes.
+template <bool ONE>
+__global__ __launch_bounds__(kPermThreads) void k_perm_experts(const int32_t* __restrict__ idx, int n, int E,
+                                                              int32_t* __restrict__ pair_perm,
+                                                              int32_t* __restrict__ expert_off, int tile_rows,
+                                                              int32_t* __restrict__ tile_e,
+                                                              int32_t* __restrict__ tile_m0,
+                                                              int32_t* __restrict__ n_tiles) {
+  __shared__ int hist[kMaxE];
+  __shared__ int wsum[kPermWaves];
+  __shared__ int s_wcnt[kPermWaves];
+  __shared__ int s_off, s_tbase;
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int j = tid; j < E; j += kPermThreads) hist[j] = 0;
   __syncthreads();
-  const int q = blockIdx.x * kPermChunk + threadIdx.x;
-  const bool valid = q < n;
-  const int e = valid ? idx[q] : 0;
-  uint64_t same = __ballot(valid);
-  for (int b = 0; (1 << b) < E; ++b) {
-    const uint64_t m = __ballot(valid && ((e >> b) & 1));
-    same &= ((e >> b) & 1) ? m : ~m;
+  // this wave's quarter [b0, b1), in chunks of 64 pairs: the histogram of all
+  // pairs' experts and this wave's matches of e
+  const int qn = (n + kPermWaves - 1) / kPermWaves, b0 = min(n, wave * qn), b1 = min(n, b0 + qn);
+  int wcnt = 0;
+  int v[kPermUnroll];
+  for (int c = b0; c < b1; c += 64 * kPermUnroll) {
+#pragma unroll
+    for (int u = 0; u < kPermUnroll; ++u) {
+      const int q = c + 64 * u + lane;
+      v[u] = q < b1 ? idx[q] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPermUnroll; ++u) {
+      if (v[u] >= 0) atomicAdd(&hist[v[u]], 1);
+      wcnt += __popcll(__ballot(v[u] == e));
+    }
+    if (ONE) break;
   }
-  const int rank = __popcll(same & ((1ull << lane) - 1ull));
-  if (valid && rank == 0) wcnt[wave][e] = __popcll(same);
+  if (lane == 0) s_wcnt[wave] = wcnt;
   __syncthreads();
-  if (valid) {
-    int base = chunk_base[(size_t)blockIdx.x * E + e] + rank;
-    for (int w = 0; w < wave; ++w) base += wcnt[w][e];
-    pair_perm[base] = q;
+  // offsets of expert e (pairs and tiles): sums over the experts before it, the
+  // experts split into contiguous runs of ceil(E / 256) per thread
+  const int epr = (E + kPermThreads - 1) / kPermThreads, j0 = tid * epr, j1 = min(E, j0 + epr);
+  int cnt = 0, tl = 0;
+  for (int j = j0; j < j1; ++j) {
+    cnt += hist[j];
+    if (tile_rows > 0) tl += (hist[j] + tile_rows - 1) / tile_rows;
+  }
+  int total, tiles_total;
+  const int cnt_before = block_excl_scan(cnt, wsum, &total);
+  const int tl_before = block_excl_scan(tl, wsum, &tiles_total);
+  if (e >= j0 && e < j1) {  // the thread whose run holds e adds the experts of its run before e
+    int o = cnt_before, tb = tl_before;
+    for (int j = j0; j < e; ++j) {
+      o += hist[j];
+      if (tile_rows > 0) tb += (hist[j] + tile_rows - 1) / tile_rows;
+    }
+    s_off = o;
+    s_tbase = tb;
+  }
+  __syncthreads();
+  const int off = s_off, ce = hist[e];
+  int w = off;
+  for (int i = 0; i < wave; ++i) w += s_wcnt[i];
+  for (int c = b0; c < b1; c += 64 * kPermUnroll) {
+    if (!ONE) {
+#pragma unroll
+      for (int u = 0; u < kPermUnroll; ++u) {
+        const int q = c + 64 * u + lane;
+        v[u] = q < b1 ? idx[q] : -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPermUnroll; ++u) {
+      const uint64_t m = __ballot(v[u] == e);
+      if (v[u] == e) pair_perm[w + __popcll(m & lt)] = c + 64 * u + lane;
+      w += __popcll(m);
+    }
+    if (ONE) break;
+  }
+  if (tid == 0) {
+    expert_off[e] = off;
+    if (e == E - 1) expert_off[E] = off + ce;
+    if (tile_rows > 0 && e == 0) *n_tiles = tiles_total;
+  }
+  if (tile_rows > 0) {
+    const int nt = (ce + tile_rows - 1) / tile_rows, tb = s_tbase;
+    for (int j = tid; j < nt; j += kPermThreads) {
+      tile_e[tb + j] = e;
+      tile_m0[tb + j] = j * tile_rows;
+    }
   }
 }
 
@@ -339,18 +355,15 @@ static size_t logits_bytes(int T, int E) {
 }
 
 size_t route_ws_bytes(int T, int H, int E, int k) {
-  const size_t n = (size_t)T * k;
-  const size_t nchunk = (n + kPermChunk - 1) / kPermChunk;
+  (void)k;
   const size_t planes = T > kGemvMaxT ? align256((size_t)3 * E * H * 2) : 0;
-  return logits_bytes(T, E) + align256(nchunk * E * 4 + 4) + planes;
+  return logits_bytes(T, E) + planes;
 }
 
 void route_ws_carve(RouteArgs& a, void* ws) {
   uint8_t* p = static_cast<uint8_t*>(ws);
   a.logits = reinterpret_cast<float*>(p);
   p += logits_bytes(a.T, a.E);
-  a.chunk_cnt = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)((a.T * a.k + kPermChunk - 1) / kPermChunk) * a.E * 4 + 4);
   a.planes = a.T > kGemvMaxT ? reinterpret_cast<uint16_t*>(p) : nullptr;
 }
 
@@ -367,11 +380,14 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
                   a.T <= kGemvMaxT ? 1 : kRouterSplitK);
   if (e != hipSuccess || !a.pair_perm) return e;
   const int n = a.T * a.k;
-  const int nchunk = (n + kPermChunk - 1) / kPermChunk;
-  hipLaunchKernelGGL(k_perm_count, dim3(nchunk), dim3(kPermChunk), 0, s, a.topk_idx, n, a.E,
-                     a.chunk_cnt);
-  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, nchunk, a.E, a.chunk_cnt, a.expert_off);
-  hipLaunchKernelGGL(k_perm_scatter, dim3(nchunk), dim3(kPermChunk), 0, s, a.topk_idx, n, a.E,
-                     a.chunk_cnt, a.pair_perm);
+  int32_t* te = a.tile_rows > 0 ? a.tiles : nullptr;
+  if (n <= kPermWaves * 64 * kPermUnroll)
+    hipLaunchKernelGGL(k_perm_experts<true>, dim3(a.E), dim3(kPermThreads), 0, s, a.topk_idx, n, a.E, a.pair_perm,
+                       a.expert_off, a.tile_rows, te, te ? te + a.max_tiles : nullptr,
+                       te ? te + 2 * a.max_tiles : nullptr);
+  else
+    hipLaunchKernelGGL(k_perm_experts<false>, dim3(a.E), dim3(kPermThreads), 0, s, a.topk_idx, n, a.E, a.pair_perm,
+                       a.expert_off, a.tile_rows, te, te ? te + a.max_tiles : nullptr,
+                       te ? te + 2 * a.max_tiles : nullptr);
   return hipGetLastError();
 }

@@ -115,9 +115,11 @@ def test_decode_753b_shape_sampled(fmt):
 
 # ----------------------------------------------------------------- routing
 
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 64, 300])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 64, 300, 2100])
 @pytest.mark.parametrize("renorm", [False, True])
 def test_route_token_counts(T, renorm):
+    """Routing and the stable expert permutation; 2100 tokens (16800 pairs) take
+    the permutation kernel's multi-batch path."""
     H, E, k = 2048, 256, 8
     R = sy.router(0, 11, 0, E, H)
     x = iid_tokens(0, 11, T, H, [R], k)
