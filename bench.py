@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--cache-steps", type=int, default=128)
     p.add_argument("--cache-host-sync", action="store_true",
                    help="time the host-waiting executor (moe_cached_layer_forward) instead")
+    p.add_argument("--prefill-stream-reps", type=int, default=3,
+                   help="streamed-prefill leg passes (0 = skip; runs with the cache leg's host pools)")
     p.add_argument("--fmt", type=int, default=0, help="override weight format (1 NVFP4, 2 MXFP4, 3 FP8)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (testing only)")
     p.add_argument("--replicate-layers", action="store_true",
@@ -262,6 +264,71 @@ def prefill_leg(name, fmt_override, reps, threads):
             "router_fp32_gflop": round(flops_router / 1e9, 2)}
 
 
+def prefill_stream_leg(fmt, hosts, pools, routers, stride, reps):
+    """Prefill with the experts in pinned host memory (moe_prefill_streamed): the
+    2048-token prefill35b input through every layer of the stack, each layer's E
+    blobs copied over PCIe into one of two VRAM pools while the previous layer
+    computes.  Also timed alone: the same copies without compute, and the same
+    layers computed from resident pools (pools)."""
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_gemv_amd import binding as B
+    from block_scaled_fp4_gemv_amd import synth as sy
+
+    wl = sy.WORKLOADS["prefill35b"]
+    H, E, F, k, T = wl.H, wl.E, wl.F, wl.k, wl.T
+    L = len(hosts)
+    x = torch.from_numpy(sy.token_rows(0, wl.cfg_id, T, H)).cuda()
+    outs = [torch.empty((T, H), dtype=torch.uint16, device="cuda") for _ in range(L)]
+    idx = torch.empty((L, T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, T, k), dtype=torch.float32, device="cuda")
+    ps = B.PrefillStream(E, stride)
+    ws = torch.empty(B.moe_prefill_streamed_workspace(fmt, T, H, F, k, E), dtype=torch.uint8, device="cuda")
+    main = torch.cuda.current_stream()
+
+    def streamed():
+        B.moe_prefill_streamed(fmt, stride, H, F, E, k, hosts, routers, x, outs, idx, w, ps, ws)
+
+    def compute_only():
+        for l in range(L):
+            B.moe_layer_forward(fmt, pools[l], stride, H, F, E, k, x, routers[l], topk_idx=idx[l], topk_w=w[l],
+                                out=outs[l], ws=ws)
+
+    def copy_only():
+        for l in range(L):
+            ps.pools[l % 2].copy_(hosts[l], non_blocking=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(main)
+            fn()
+            b.record(main)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return float(np.median(ms))
+
+    t_stream = timed(streamed)
+    t_copy = timed(copy_only)
+    t_comp = timed(compute_only)
+    nbytes = L * E * stride
+    hidden = (t_copy + t_comp - t_stream) / t_comp if t_comp > 0 else 0.0
+    fmt_name = {1: "nvfp4", 2: "mxfp4", 3: "fp8"}[fmt]
+    return {"workload": f"prefill35b input ({T} tokens) through {L} layers of the decode35b stack, {fmt_name}, "
+                        f"every layer's {E} experts streamed from pinned host memory",
+            "executor": "moe_prefill_streamed (two VRAM pools, copy stream + events)",
+            "ms_per_prefill": round(t_stream, 3), "tokens_per_s": round(T / (t_stream * 1e-3), 1),
+            "h2d_bytes": nbytes, "h2d_GBps": round(nbytes / (t_stream * 1e-3) / 1e9, 2),
+            "copy_only_ms": round(t_copy, 3), "copy_only_GBps": round(nbytes / (t_copy * 1e-3) / 1e9, 2),
+            "compute_only_ms": round(t_comp, 3),
+            "compute_hidden_frac": round(min(1.0, max(0.0, hidden)), 4),
+            "timing": f"HIP events on the compute stream, median of {reps} passes after one warm-up pass"}
+
+
 def measured_traffic(n_layers_run, n_layers_default):
     """HBM bytes per decode layer from the committed FETCH_SIZE/WRITE_SIZE runs, if the
     kernel sources are unchanged since they were taken (else None)."""
@@ -444,6 +511,12 @@ def main():
                                  host_sync=args.cache_host_sync)
         log(f"cache: {res['cache']['tokens_per_s']} tok/s, hit rate {res['cache']['hit_rate']}, "
             f"{res['cache']['h2d_GBps']} GB/s H2D")
+        if args.prefill_stream_reps > 0:
+            log("streamed-prefill leg ...")
+            res["prefill_stream"] = prefill_stream_leg(fmt, hosts, pools, routers, stride, args.prefill_stream_reps)
+            log(f"streamed prefill: {res['prefill_stream']['ms_per_prefill']} ms per prefill, "
+                f"{res['prefill_stream']['h2d_GBps']} GB/s H2D, compute hidden "
+                f"{res['prefill_stream']['compute_hidden_frac']}")
         del hosts
     if args.prefill != "none":
         log(f"prefill leg {args.prefill} ...")

@@ -62,6 +62,10 @@ SIGNATURES = {
                                         ctypes.POINTER(moe_cached_layer), _vp, _i32, _vp, _vp, _vp, _vp,
                                         _vp, _vp, _sz, _vp, _vp, ctypes.POINTER(ctypes.c_int32),
                                         ctypes.POINTER(ctypes.c_int32)]),
+    "moe_prefill_streamed_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "moe_prefill_streamed": (_i32, [_i32, _sz, _i32, _i32, _i32, _i32, _u32, _i32, ctypes.POINTER(_vp),
+                                    ctypes.POINTER(_vp), _vp, _i32, ctypes.POINTER(_vp), _vp, _vp,
+                                    ctypes.POINTER(_vp), _vp, _sz, _vp, _vp, ctypes.POINTER(_vp)]),
 }
 
 _lib = None
@@ -382,3 +386,36 @@ def moe_cached_layer_enqueue(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w
                                         _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
                                         _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_cached_layer_enqueue")
+
+
+# ------------------------------------------------- prefill with streamed experts
+
+class PrefillStream:
+    """Two VRAM pools of E blobs, a copy stream and the four events of
+    moe_prefill_streamed (created here)."""
+
+    def __init__(self, E, stride, device="cuda"):
+        import torch
+        self.pools = [torch.empty(E * stride, dtype=torch.uint8, device=device) for _ in range(2)]
+        self.copy_stream = torch.cuda.Stream(device=device)
+        self.events = [torch.cuda.Event() for _ in range(4)]
+        for ev in self.events:
+            ev.record()  # creates the underlying HIP event
+        torch.cuda.current_stream().synchronize()
+
+
+def moe_prefill_streamed_workspace(fmt, T, H, F, k, E):
+    return int(lib().moe_prefill_streamed_workspace(fmt, T, H, F, k, E))
+
+
+def moe_prefill_streamed(fmt, stride, H, F, E, k, host_pools, routers, x, outs, topk_idx, topk_w, ps, ws,
+                         flags=0, stream=None):
+    """Enqueue a prefill of x through len(host_pools) layers streamed from pinned host
+    memory (ps: PrefillStream).  outs: list of bf16 [T][H]; topk_idx/topk_w: [L][T][k]."""
+    L, T = len(host_pools), x.shape[0]
+    arr = lambda xs: (_vp * max(1, len(xs)))(*[_ptr(t) for t in xs])  # noqa: E731
+    evs = (_vp * 4)(*[e.cuda_event for e in ps.events])
+    st = lib().moe_prefill_streamed(fmt, stride, H, F, E, k, flags, L, arr(host_pools), arr(routers), _ptr(x), T,
+                                    arr(outs), _ptr(topk_idx), _ptr(topk_w), arr(ps.pools), _ptr(ws), ws.numel(),
+                                    _stream(stream), _stream(ps.copy_stream), evs)
+    _check(st, "moe_prefill_streamed")

@@ -379,6 +379,65 @@ int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, in
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_layer_forward(ffn)");
 }
 
+size_t moe_prefill_streamed_workspace(int fmt, int T, int H, int F, int k, int E) {
+  return moe_layer_workspace(fmt, T, H, F, k, E);
+}
+
+int moe_prefill_streamed(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                         int n_layers, const void* const* host_pools, const float* const* routers,
+                         const uint16_t* x, int T, uint16_t* const* outs, int32_t* topk_idx,
+                         float* topk_w, void* const* pools, void* ws, size_t ws_bytes,
+                         moe_stream_t stream, moe_stream_t copy_stream, const moe_event_t* events) {
+  g_err[0] = 0;
+  int st = check_shape(fmt, H, F);
+  if (st) return st;
+  st = check_route_dims(T, H, E, k);
+  if (st) return st;
+  if (n_layers < 0) return fail(MOE_E_ARG, "n_layers %d", n_layers);
+  if (n_layers == 0 || T == 0) return MOE_OK;
+  if (!host_pools || !routers || !outs || !pools || !events || !topk_idx || !topk_w)
+    return fail(MOE_E_ARG, "NULL array argument");
+  if (!pools[0] || !pools[1] || pools[0] == pools[1]) return fail(MOE_E_ARG, "need two distinct pools");
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return fail(MOE_E_ARG, "event %d is NULL", i);
+  if (!copy_stream || copy_stream == stream) return fail(MOE_E_ARG, "copy_stream must be a second stream");
+  for (int l = 0; l < n_layers; ++l)
+    if (!host_pools[l] || !routers[l] || !outs[l]) return fail(MOE_E_ARG, "layer %d: NULL pointer", l);
+  const size_t need = moe_prefill_streamed_workspace(fmt, T, H, F, k, E);
+  if (!need) return fail(MOE_E_ARG, "bad shape or format");
+  if (!ws || !aligned(ws, 256) || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "prefill workspace needs %zu bytes, 256-aligned", need);
+  hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(copy_stream);
+  hipEvent_t ev[4];
+  for (int i = 0; i < 4; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
+  const size_t bytes = (size_t)E * stride;
+  // copy of layer l into pool l % 2, after the pool's previous reader (layer l-2)
+  auto copy_layer = [&](int l) -> hipError_t {
+    const int p = l & 1;
+    hipError_t e = hipSuccess;
+    if (l >= 2) e = hipStreamWaitEvent(cs, ev[2 + p], 0);
+    if (e == hipSuccess) e = hipMemcpyAsync(pools[p], host_pools[l], bytes, hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess) e = hipEventRecord(ev[p], cs);
+    return e;
+  };
+  hipError_t e = copy_layer(0);
+  if (e == hipSuccess && n_layers > 1) e = copy_layer(1);
+  if (e != hipSuccess) return hip_fail(e, "moe_prefill_streamed(copy)");
+  const size_t tk = (size_t)T * k;
+  for (int l = 0; l < n_layers; ++l) {
+    const int p = l & 1;
+    e = hipStreamWaitEvent(s, ev[p], 0);
+    if (e != hipSuccess) return hip_fail(e, "moe_prefill_streamed(wait copy)");
+    st = moe_layer_forward(fmt, pools[p], stride, H, F, E, k, route_flags, x, T, routers[l], topk_idx + l * tk,
+                           topk_w + l * tk, outs[l], ws, ws_bytes, stream);
+    if (st) return st;
+    e = hipEventRecord(ev[2 + p], s);
+    if (e == hipSuccess && l + 2 < n_layers) e = copy_layer(l + 2);
+    if (e != hipSuccess) return hip_fail(e, "moe_prefill_streamed(layer)");
+  }
+  return MOE_OK;
+}
+
 int moe_combine(const float* y, const float* topk_w, int T, int H, int k, uint16_t* out,
                 moe_stream_t stream) {
   g_err[0] = 0;

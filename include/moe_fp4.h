@@ -335,6 +335,41 @@ int moe_cached_layer_enqueue(int fmt, size_t stride, int H, int F, int E, int k,
                              int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
                              uint16_t* out, void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* ------------------------------------------- prefill with streamed experts */
+
+/* Workspace bytes for moe_prefill_streamed (device, 256-byte aligned): one
+ * moe_layer_forward workspace, shared by the layers in turn. */
+size_t moe_prefill_streamed_workspace(int fmt, int T, int H, int F, int k, int E);
+
+/* A prefill of T tokens through n_layers MoE layers whose experts live in
+ * pinned host memory, double-buffered over PCIe (page "8GB 笔记本 39.3 tok/s、
+ * 单卡跑 753B：FreeToken 把 frontier MoE 拉回本地", section "设计核心", the
+ * first execution principle: while the GPU computes one layer's experts, the
+ * next layer's experts stream in from host memory).  Two VRAM pools
+ * alternate; for layer l (pool p = l % 2):
+ *   copy_stream: wait events[2+p] (layer l-2, the pool's last reader, has
+ *     finished) -> one hipMemcpyAsync of the layer's E blobs host_pools[l] ->
+ *     pools[p] -> record events[p];
+ *   stream: wait events[p] -> moe_layer_forward(pools[p], routers[l], x) into
+ *     outs[l], topk_idx + l*T*k, topk_w + l*T*k -> record events[2+p].
+ * The copies of layers 0 and 1 are enqueued first and the copy of layer l+2
+ * right after the compute of layer l, so the copy of layer l+1 runs under the
+ * compute of layer l.  Each layer receives the same x (the layers are not
+ * chained).  Every layer runs moe_layer_forward's kernels, so its outputs
+ * equal moe_layer_forward on a resident pool bit for bit.
+ *   host_pools [host] array of n_layers [pinned] pointers, E*stride bytes each
+ *   routers    [host] array of n_layers device pointers, float [E][H]
+ *   outs       [host] array of n_layers device pointers, bf16 [T][H]
+ *   topk_idx, topk_w: device, [n_layers][T][k]
+ *   pools      [host] array of 2 device pointers, E*stride bytes each
+ *   events     [host] array of 4 events: copy_done[2], compute_done[2]
+ * Enqueues only (no host wait); stream != copy_stream. */
+int moe_prefill_streamed(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                         int n_layers, const void* const* host_pools, const float* const* routers,
+                         const uint16_t* x, int T, uint16_t* const* outs, int32_t* topk_idx,
+                         float* topk_w, void* const* pools, void* ws, size_t ws_bytes,
+                         moe_stream_t stream, moe_stream_t copy_stream, const moe_event_t* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -185,3 +185,25 @@ def test_cached_layer_argument_errors_before_any_hip_call():
     assert call(None, need) == B.MOE_E_ARG
     layer = B.moe_cached_layer(fake, fake, fake, B.moe_lru(E, 64, fake, fake, fake, fake), fake, fake, None, None)
     assert call(ctypes.byref(layer), need - 1) == B.MOE_E_WORKSPACE
+
+
+def test_prefill_streamed_argument_errors_before_any_hip_call():
+    L = B.lib()
+    fmt, H, F, E, k, T, n = 2, 2048, 512, 256, 8, 64, 3
+    need = B.moe_prefill_streamed_workspace(fmt, T, H, F, k, E)
+    assert need == B.lib().moe_layer_workspace(fmt, T, H, F, k, E) > 0
+    fake = 0x1000  # never dereferenced: validation fails first
+    vp = ctypes.c_void_p
+    arr = lambda m, v=fake: (vp * m)(*([v] * m))  # noqa: E731
+    pools = (vp * 2)(fake, fake + 0x100000)
+    stride = B.blob_stride(fmt, H, F)
+
+    def call(events, ws_bytes, s=0x11, cs=0x22, pools=pools, layers=n):
+        return L.moe_prefill_streamed(fmt, stride, H, F, E, k, 0, layers, arr(n), arr(n), fake, T, arr(n), fake,
+                                      fake, pools, 0x100000, ws_bytes, s, cs, events)
+    assert call(arr(4), need - 1) == B.MOE_E_WORKSPACE
+    assert call(arr(4, None), need) == B.MOE_E_ARG            # NULL events
+    assert call(arr(4), need, cs=0x11) == B.MOE_E_ARG          # copy stream == stream
+    assert call(arr(4), need, pools=(vp * 2)(fake, fake)) == B.MOE_E_ARG
+    assert call(arr(4), need, layers=-1) == B.MOE_E_ARG
+    assert call(arr(4), need, layers=0) == B.MOE_OK            # nothing to do

@@ -281,6 +281,63 @@ def test_cache_mode_bitwise_equals_resident_mode():
     assert 0 < hits < xs.shape[0] * k
 
 
+@pytest.mark.parametrize("fmt,T", [(NV, 96), (MX, 3), (F8, 64)])
+def test_prefill_streamed(fmt, T):
+    """Five layers streamed double-buffered from pinned host memory through two
+    VRAM pools: every layer's routing and output equal moe_layer_forward on a
+    resident pool bit for bit, on two calls in a row (the pools and events
+    reused); layer 0 matches the oracle."""
+    H, E, F, k, n_layers = 256, 16, 512, 4, 5
+    layers = [Layer(fmt, H, E, F, cfg=23, layer=l, w_std=0.02) for l in range(n_layers)]
+    x = iid_tokens(0, 23, T, H, [L.router for L in layers], k)
+    xd = _x_dev(x)
+    stride = layers[0].stride
+    hosts, routers, res = [], [], []
+    for L in layers:
+        h = torch.empty(E * stride, dtype=torch.uint8).pin_memory()
+        h.numpy()[:] = L.host_pool()
+        hosts.append(h)
+        pool, R = L.device()
+        routers.append(R)
+        res.append(B.moe_layer_forward(fmt, pool, stride, H, F, E, k, xd, R))
+    ps = B.PrefillStream(E, stride)
+    ws = torch.empty(B.moe_prefill_streamed_workspace(fmt, T, H, F, k, E), dtype=torch.uint8, device="cuda")
+    for call in range(2):
+        outs = [torch.full((T, H), 0xFFFF, dtype=torch.uint16, device="cuda") for _ in range(n_layers)]
+        idx = torch.empty((n_layers, T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((n_layers, T, k), dtype=torch.float32, device="cuda")
+        B.moe_prefill_streamed(fmt, stride, H, F, E, k, hosts, routers, xd, outs, idx, w, ps, ws)
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            ridx, rw, rout = res[l]
+            assert torch.equal(idx[l], ridx) and torch.equal(w[l], rw), f"call {call} layer {l}"
+            assert torch.equal(outs[l], rout), f"call {call} layer {l}"
+    ref = moe.moe_layer(fmt, x, layers[0].router, layers[0].experts, k)
+    assert_rows_close(bf16_dev_to_f64(outs[0]), fm.bf16_to_f64(ref["out"]), what="out")
+
+
+def test_prefill_streamed_argument_errors():
+    H, E, F, k = 256, 8, 512, 2
+    L = Layer(MX, H, E, F, cfg=0, layer=0, w_std=0.02)
+    stride = L.stride
+    pool, R = L.device()
+    h = torch.empty(E * stride, dtype=torch.uint8).pin_memory()
+    x = _x_dev(iid_tokens(0, 0, 8, H, [L.router], k))
+    ps = B.PrefillStream(E, stride)
+    ws = torch.empty(B.moe_prefill_streamed_workspace(MX, 8, H, F, k, E), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((8, H), dtype=torch.uint16, device="cuda")]
+    idx = torch.empty((1, 8, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, 8, k), dtype=torch.float32, device="cuda")
+    with pytest.raises(B.MoeError):       # the copy stream must differ from the compute stream
+        B.moe_prefill_streamed(MX, stride, H, F, E, k, [h], [R], x, outs, idx, w, ps, ws,
+                               stream=ps.copy_stream)
+    with pytest.raises(B.MoeError):       # workspace too small
+        B.moe_prefill_streamed(MX, stride, H, F, E, k, [h], [R], x, outs, idx, w, ps, ws[:256])
+    ps.pools[1] = ps.pools[0]
+    with pytest.raises(B.MoeError):       # the two pools must differ
+        B.moe_prefill_streamed(MX, stride, H, F, E, k, [h], [R], x, outs, idx, w, ps, ws)
+
+
 @pytest.mark.parametrize("fmt", [NV, MX])
 def test_cached_layer_forward(fmt):
     """The native cached-layer executor: 6 slots for 16 experts, top-2, 24 AR(1)
