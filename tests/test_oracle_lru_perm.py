@@ -101,3 +101,20 @@ def test_permutation_properties(T, k, E):
         seg = perm[off[e]:off[e + 1]]
         assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)    # stable
     assert np.array_equal(perm, np.argsort(flat, kind="stable"))      # library sort
+
+
+def test_prefetch_study_replays_the_oracle_lru():
+    """The runner-up prefetch study (tests/prefetch_study.py) with m = 0 replays
+    the oracle LRU exactly: the same misses at every step of every layer."""
+    import prefetch_study as ps
+    from block_scaled_fp4_gemv_amd import synth as sy
+    wl = sy.WORKLOADS["cache35b"]
+    r = ps.rankings(24, n_layers=3)
+    d = ps.simulate(r, wl.k, wl.slots, 0, warm=0)
+    for layer in range(3):
+        ref = lru.StampLRU(wl.E, wl.slots)
+        for t in range(24):
+            assert ref.step(r[layer, t, :wl.k])["n_miss"] == d["per_step_miss"][layer, t]
+    assert d["prefetched_per_token"] == 0
+    d4 = ps.simulate(r, wl.k, wl.slots, 4, warm=0)
+    assert d4["prefetched_per_token"] > 0 and 0.0 <= d4["prefetch_accuracy"] <= 1.0
