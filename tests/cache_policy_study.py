@@ -1,5 +1,7 @@
-"""Runner-up prefetch on the cache-constrained decode trace, evaluated on the CPU.
+"""Cache policies on the cache-constrained decode trace, evaluated on the CPU:
+runner-up prefetch, a CPU / GPU miss split, and one LRU across all layers.
 
+Prefetch:
 For every layer of the cache35b stack (64 of 256 experts per layer in VRAM,
 top-8, AR(1) decode states) the oracle's routing gives each step's expert
 ranking.  The study replays the per-layer LRU of the cache (the oracle's
@@ -13,7 +15,15 @@ the prefetch accuracy (share of prefetched experts that the same layer routes
 to at the next step).  m = 0 is the plain predictor (a layer's top-k at step t
 for step t+1), which names only resident experts and prefetches nothing.
 
-    python tests/prefetch_study.py [steps]
+Miss split: of a step's n misses the first round(q*n) are computed by the CPU
+from the host pool and stay out of the cache (no slot, no stamp); the rest are
+filled into the cache by the GPU.  It reports the GPU fills and the CPU expert
+evaluations per token.
+
+Global LRU: one pool of S*L slots shared by the L layers (keys (layer, expert),
+the layers of a step looked up in order) against the per-layer pools.
+
+    python tests/cache_policy_study.py [steps]
 """
 import os
 import sys
@@ -86,6 +96,66 @@ def simulate(ranks, k, S, m, warm):
                 per_step_miss=per_step_miss)
 
 
+def simulate_split(ranks, k, S, q, warm):
+    """(GPU fills, CPU expert evaluations) per token with the first round(q*n)
+    misses of each step computed on the CPU and left out of the cache."""
+    L, steps, _ = ranks.shape
+    gpu = cpu = 0
+    for layer in range(L):
+        slot_of, stamp, clock = {}, {}, 0
+        for t in range(steps):
+            top = [int(e) for e in ranks[layer, t, :k]]
+            req = set(top)
+            miss = []
+            for e in top:
+                if e not in slot_of and e not in miss:
+                    miss.append(e)
+            n_cpu = int(np.floor(q * len(miss) + 0.5))
+            for e in miss[n_cpu:]:
+                if len(slot_of) < S:
+                    slot_of[e] = len(slot_of)
+                else:
+                    v = min((x for x in slot_of if x not in req), key=lambda x: stamp[x])
+                    slot_of[e] = slot_of.pop(v)
+                    stamp.pop(v)
+            for e in top:
+                clock += 1
+                if e in slot_of:
+                    stamp[e] = clock
+            if t >= warm:
+                gpu += len(miss) - n_cpu
+                cpu += n_cpu
+    n = steps - warm
+    return gpu / n, cpu / n
+
+
+def simulate_global(ranks, k, total, warm):
+    """Misses per token with one LRU of `total` slots over (layer, expert) keys."""
+    L, steps, _ = ranks.shape
+    slot_of, stamp, clock, misses = {}, {}, 0, 0
+    for t in range(steps):
+        for layer in range(L):
+            top = [(layer, int(e)) for e in ranks[layer, t, :k]]
+            req = set(top)
+            miss = []
+            for e in top:
+                if e not in slot_of and e not in miss:
+                    miss.append(e)
+            for e in miss:
+                if len(slot_of) < total:
+                    slot_of[e] = len(slot_of)
+                else:
+                    v = min((x for x in slot_of if x not in req), key=lambda x: stamp[x])
+                    slot_of[e] = slot_of.pop(v)
+                    stamp.pop(v)
+            for e in top:
+                clock += 1
+                stamp[e] = clock
+            if t >= warm:
+                misses += len(miss)
+    return misses / (steps - warm)
+
+
 def main():
     steps = int(sys.argv[1]) if len(sys.argv) > 1 else 192
     wl = sy.WORKLOADS["cache35b"]
@@ -93,7 +163,12 @@ def main():
     for m in (0, 1, 2, 4, 8):
         d = simulate(r, wl.k, wl.slots, m, warm=64)
         d.pop("per_step_miss")
-        print({kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in d.items()})
+        print("prefetch", {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in d.items()})
+    for q in (0.0, 0.25, 0.5, 0.75, 1.0):
+        g, c = simulate_split(r, wl.k, wl.slots, q, warm=64)
+        print(f"split q={q:.2f}: GPU fills {g:.2f} per token, CPU expert evaluations {c:.2f} per token")
+    print(f"global LRU ({wl.slots * wl.layers} slots): "
+          f"{simulate_global(r, wl.k, wl.slots * wl.layers, warm=64):.2f} misses per token")
 
 
 if __name__ == "__main__":

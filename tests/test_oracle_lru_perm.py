@@ -103,10 +103,11 @@ def test_permutation_properties(T, k, E):
     assert np.array_equal(perm, np.argsort(flat, kind="stable"))      # library sort
 
 
-def test_prefetch_study_replays_the_oracle_lru():
-    """The runner-up prefetch study (tests/prefetch_study.py) with m = 0 replays
-    the oracle LRU exactly: the same misses at every step of every layer."""
-    import prefetch_study as ps
+def test_cache_policy_study_replays_the_oracle_lru():
+    """The cache policy study (tests/cache_policy_study.py) replays the oracle LRU
+    exactly when no policy is applied: prefetch m = 0, split q = 0 and a global
+    pool of one layer all give the oracle's misses."""
+    import cache_policy_study as ps
     from block_scaled_fp4_gemv_amd import synth as sy
     wl = sy.WORKLOADS["cache35b"]
     r = ps.rankings(24, n_layers=3)
@@ -118,3 +119,7 @@ def test_prefetch_study_replays_the_oracle_lru():
     assert d["prefetched_per_token"] == 0
     d4 = ps.simulate(r, wl.k, wl.slots, 4, warm=0)
     assert d4["prefetched_per_token"] > 0 and 0.0 <= d4["prefetch_accuracy"] <= 1.0
+    g, c = ps.simulate_split(r, wl.k, wl.slots, 0.0, warm=0)
+    assert c == 0 and g * 24 == d["per_step_miss"].sum()
+    one = ps.simulate_global(r[:1], wl.k, wl.slots, warm=0)
+    assert one * 24 == d["per_step_miss"][0].sum()
