@@ -129,6 +129,14 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
+__device__ __forceinline__ float wave_min(float v) {
+  v = fminf(v, dpp_f32<kDppXor1>(v));
+  v = fminf(v, dpp_f32<kDppXor2>(v));
+  v = fminf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fminf(v, dpp_f32<kDppMirror>(v));
+  return fminf(fminf(readlane_f32(v, 0), readlane_f32(v, 16)), fminf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+
 // Sum over aligned groups of W lanes (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {

@@ -213,10 +213,15 @@ struct DownRows {
 
 // Gate/up + SwiGLU for rows 16*blockIdx.x.. of pair blockIdx.y (or pair_subset
 // entry).  TOPK: the pair's expert comes from the softmax/top-k of `logits`,
-// which wave 0 of every workgroup computes (identical everywhere); column
-// group 0 of the token's first pair writes topk_idx / topk_w.
+// which one extra wave of every workgroup computes (identical everywhere);
+// column group 0 of the token's first pair writes topk_idx / topk_w.  When the
+// selection alone fixes the top-k set (no candidate beyond k), workgroup row j
+// takes the set's j-th expert in index order and the other waves start its
+// weight loads at once; the extra wave ranks the set meanwhile, and the h row
+// goes to the expert's rank position, so hbuf and topk_idx agree as when
+// ranked first.
 template <int FMT, int NB, bool TOPK, int NV>
-__global__ __launch_bounds__(512) void k_gateup_gemv(
+__global__ __launch_bounds__(TOPK ? 576 : 512) void k_gateup_gemv(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F, int E, int k,
     unsigned flags, const uint16_t* __restrict__ x, const float* __restrict__ logits,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, const int32_t* __restrict__ pair_slot,
@@ -224,30 +229,57 @@ __global__ __launch_bounds__(512) void k_gateup_gemv(
     const uint8_t* __restrict__ miss_src, uint16_t* __restrict__ hbuf) {
   __shared__ __attribute__((aligned(16))) uint16_t xl[kMaxDim];
   __shared__ float red[8][2][16];
-  __shared__ int s_slot;
+  __shared__ int s_slot, s_row;
   __shared__ TopkScratch s_topk;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  // nw waves take the K steps; with TOPK wave nw runs the top-k
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x >> 6) - (TOPK ? 1 : 0);
   bool miss = false;
   const int q = TOPK ? (int)blockIdx.y : pair_of_block(pair_subset, subset_rec, subset_mode, miss);
   if (q < 0) return;
   const int t = q / k, j = q % k, g = blockIdx.x;
   const uint4* xs4 = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+  // the logits are requested before the x staging waits on its loads, so the
+  // two loads are in flight together
+  float v[NV];
+  if constexpr (TOPK)
+    if (w == nw) wave_load_logits<NV>(logits + (size_t)t * E, E, v);
   for (int i = threadIdx.x; i < H / 8; i += blockDim.x) reinterpret_cast<uint4*>(xl)[i] = xs4[i];
+  TopkSel<NV> sel;
+  bool set_first = false;  // top-k wave: the set is known, its order comes later
+  // order the selection, publish the outputs and the h row of expert `mine`
+  const auto order = [&](int mine) {
+    int idx;
+    float wt;
+    wave_topk_order<NV>(v, E, k, flags, sel, idx, wt, s_topk);
+    const uint64_t at = __ballot(lane < k && idx == mine);
+    if (lane == 0) s_row = t * k + __builtin_ctzll(at);
+    if (g == 0 && j == 0 && lane < k) {
+      topk_idx[(size_t)t * k + lane] = idx;
+      topk_w[(size_t)t * k + lane] = wt;
+    }
+  };
   if constexpr (TOPK) {
-    if (w == 0) {
-      float v[NV];
-      wave_load_logits<NV>(logits + (size_t)t * E, E, v);
-      int idx;
-      float wt;
-      wave_topk_regs<NV>(v, E, k, flags, idx, wt, s_topk);
-      if (lane == j) s_slot = idx;
-      if (g == 0 && j == 0 && lane < k) {
-        topk_idx[(size_t)t * k + lane] = idx;
-        topk_w[(size_t)t * k + lane] = wt;
+    if (w == nw) {
+      set_first = wave_topk_select<NV>(v, E, k, sel);
+      if (set_first) {
+        if (lane == 0) s_slot = topk_candidate<NV>(sel, j);
+      } else {
+        int idx;
+        float wt;
+        wave_topk_order<NV>(v, E, k, flags, sel, idx, wt, s_topk);
+        if (lane == j) s_slot = idx;
+        if (lane == 0) s_row = q;
+        if (g == 0 && j == 0 && lane < k) {
+          topk_idx[(size_t)t * k + lane] = idx;
+          topk_w[(size_t)t * k + lane] = wt;
+        }
       }
     }
   } else {
-    if (threadIdx.x == 0) s_slot = pair_slot ? pair_slot[q] : topk_idx[q];
+    if (threadIdx.x == 0) {
+      s_slot = pair_slot ? pair_slot[q] : topk_idx[q];
+      s_row = q;
+    }
   }
   __syncthreads();
   // a streamed miss reads the expert's blob from host memory and fills its slot
@@ -256,7 +288,12 @@ __global__ __launch_bounds__(512) void k_gateup_gemv(
   if (fill && g == 0 && threadIdx.x < 3)
     reinterpret_cast<float*>(fill + L.tau)[threadIdx.x] = reinterpret_cast<const float*>(blob + L.tau)[threadIdx.x];
   float ag = 0.0f, au = 0.0f;
-  gateup_partial<FMT, NB>(blob, L, H / kFragK, g, xl, w, nw, lane, ag, au, fill);
+  if (w < nw) {
+    gateup_partial<FMT, NB>(blob, L, H / kFragK, g, xl, w, nw, lane, ag, au, fill);
+  } else {
+    if constexpr (TOPK)
+      if (set_first) order(topk_candidate<NV>(sel, j));
+  }
   if (fill) {
     // the workgroups of a streamed miss also bring its down matrix (codes and
     // scales) into the slot, so the down kernel reads every pair from VRAM
@@ -273,7 +310,7 @@ __global__ __launch_bounds__(512) void k_gateup_gemv(
   }
   ag = row_lanes_sum(ag);
   au = row_lanes_sum(au);
-  if (lane < 16) {
+  if (w < nw && lane < 16) {
     red[w][0][lane] = ag;
     red[w][1][lane] = au;
   }
@@ -289,7 +326,7 @@ __global__ __launch_bounds__(512) void k_gateup_gemv(
       G *= tau[0];
       U *= tau[1];
     }
-    hbuf[(size_t)q * F + kFragRows * g + threadIdx.x] = f32_to_bf16_rne(silu_f32(G) * U);
+    hbuf[(size_t)s_row * F + kFragRows * g + threadIdx.x] = f32_to_bf16_rne(silu_f32(G) * U);
   }
 }
 
@@ -318,10 +355,10 @@ __global__ __launch_bounds__(512) void k_gateup_topk_stream(
   const int u0 = blockIdx.x * upw, nu = min(upw, T * k * G - u0);
   const int t = u0 / (k * G);  // upw divides k*G: all units of this workgroup belong to token t
   const uint4* xs4 = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+  float v[NV];
+  if (w == 0) wave_load_logits<NV>(logits + (size_t)t * E, E, v);
   for (int i = threadIdx.x; i < H / 8; i += blockDim.x) reinterpret_cast<uint4*>(xl)[i] = xs4[i];
   if (w == 0) {
-    float v[NV];
-    wave_load_logits<NV>(logits + (size_t)t * E, E, v);
     int idx;
     float wt;
     wave_topk_regs<NV>(v, E, k, flags, idx, wt, s_topk);
@@ -500,15 +537,17 @@ template <int FMT, bool TOPK, int NV>
 hipError_t launch_gateup_t(const FfnArgs& a, const float* logits, unsigned flags, int32_t* idx, float* w,
                            hipStream_t s) {
   const int S = a.H / kFragK, nw = gemv_waves(S);
-  dim3 grid(a.F / kFragRows, TOPK ? a.T * a.k : a.n_pairs), block(64 * nw);
-#define L(NB)                                                                                          \
-  case NB:                                                                                             \
+  dim3 grid(a.F / kFragRows, TOPK ? a.T * a.k : a.n_pairs), block(64 * (nw + (TOPK ? 1 : 0)));
+  // the top-k wave lowers the register budget: FP8 batches of 8 would spill
+  constexpr int kNB8 = TOPK && FMT == MOE_FMT_FP8_E4M3 ? 4 : 8;
+#define L(CASE, NB)                                                                                    \
+  case CASE:                                                                                           \
     hipLaunchKernelGGL((k_gateup_gemv<FMT, NB, TOPK, NV>), grid, block, 0, s, a.pool, a.stride, a.L, \
                        a.H, a.F, a.E, a.k, flags, a.x, logits, TOPK ? idx : const_cast<int32_t*>(a.topk_idx), \
                        w, a.pair_slot, a.pair_subset, a.subset_rec, a.subset_mode, a.miss_src, a.hbuf); \
     break;
   switch (gemv_batch(S)) {
-    L(1) L(2) L(4) L(8)
+    L(1, 1) L(2, 2) L(4, 4) L(8, kNB8)
     default: return hipErrorInvalidValue;
   }
 #undef L

@@ -146,80 +146,116 @@ __device__ __forceinline__ void wave_topk_radix(const float (&v)[NV], int E, int
 
 // Scratch (LDS, private to one wave) for wave_topk_regs.
 struct TopkScratch {
-  uint32_t hist[256];
   uint32_t cz[64];   // candidate logits (fp32 bits)
   uint32_t ce[64];   // candidate experts
   uint32_t list[32]; // radix fallback scratch
 };
 
-// Lane l holds logits of experts l, l+64, ..., l+64*(NV-1) (E <= 64*NV; values
-// beyond E are ignored), k <= 16.  On return lane r < k holds the rank-r expert
-// (logit desc, index asc) and its softmax weight over all E experts.
-//
-// Selection: each logit falls in bin floor((zmax - z) * 16) (clamped to 255); a
-// 256-bin LDS histogram and one wave scan give the bin B holding the k-th
-// largest logit; the experts in bins <= B (at least k, usually a few more) are
-// ranked exactly against each other.  More than 64 candidates (many equal
-// logits) fall back to an exact radix select over all keys.
+// Selection state of one token's top-k on one wave (uniform except bin).
 template <int NV>
-__device__ __forceinline__ void wave_topk_regs(const float (&v)[NV], int E, int k, unsigned flags,
-                                               int& my_idx, float& my_w, TopkScratch& sc) {
+struct TopkSel {
+  float zmax, inv_se;  // max logit; 1 / sum of exp(z - zmax) over all E
+  int B, m;            // threshold bin; experts in bins <= B (the candidates)
+  uint64_t mask[NV];   // candidates: bit l of mask[i] is expert l + 64 i
+  int bin[NV];         // per lane: bin of experts lane + 64 i (256 beyond E)
+};
+
+// Lane l holds logits of experts l, l+64, ..., l+64*(NV-1) (E <= 64*NV; values
+// beyond E are ignored), 1 <= k <= min(E, 16).
+//
+// The logit range [zmin, zmax] is cut into 256 equal bins counted from the top,
+// bin = floor((zmax - z) * 255 / (zmax - zmin)), which never decreases as z
+// decreases, so the k best experts lie in the bins up to the one holding the
+// k-th best; that bin B is found by an 8-step bisection over bin numbers with
+// ballot counts.  Returns true when the candidates (bins <= B) are exactly k:
+// they are then the top-k set, known before its order.
+template <int NV>
+__device__ __forceinline__ bool wave_topk_select(const float (&v)[NV], int E, int k, TopkSel<NV>& s) {
   const int lane = threadIdx.x & 63;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-  float zmax = -INFINITY;
+  float zmax = -INFINITY, zmin = INFINITY;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
-    if (lane + 64 * i < E) zmax = fmaxf(zmax, v[i]);
+    if (lane + 64 * i < E) {
+      zmax = fmaxf(zmax, v[i]);
+      zmin = fminf(zmin, v[i]);
+    }
   zmax = wave_max(zmax);
+  zmin = wave_min(zmin);
+  const float span = zmax - zmin;
+  const float scale = span > 0.0f ? 255.0f / span : 0.0f;  // an infinite span gives 0: one bin
   float se = 0.0f;
-  int bin[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const bool ok = lane + 64 * i < E;
     se += ok ? __expf(v[i] - zmax) : 0.0f;
-    const float d = (zmax - v[i]) * 16.0f;
-    bin[i] = ok ? (d < 255.0f ? (int)d : 255) : 256;
+    const float d = (zmax - v[i]) * scale;
+    s.bin[i] = ok ? (d < 255.0f ? (int)d : 255) : 256;
   }
-  const float inv_se = 1.0f / wave_sum(se);
-  *reinterpret_cast<uint4*>(&sc.hist[lane * 4]) = make_uint4(0u, 0u, 0u, 0u);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+  s.zmax = zmax;
+  s.inv_se = 1.0f / wave_sum(se);
+  // B = the largest bin number with fewer than k experts in lower bins
+  int B = 0;
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
-    if (bin[i] < 256) atomicAdd(&sc.hist[bin[i]], 1u);
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  // lane l owns bins 4l .. 4l+3; exclusive prefix of the lane totals from bit-plane ballots
-  const uint4 hq = *reinterpret_cast<const uint4*>(&sc.hist[lane * 4]);
-  const int c0 = hq.x, c1 = c0 + hq.y, c2 = c1 + hq.z, c3 = c2 + hq.w;
-  int before = 0;
+  for (int bit = 7; bit >= 0; --bit) {
+    const int t = B + (1 << bit);
+    int cnt = 0;
 #pragma unroll
-  for (int bit = 0; bit < 9; ++bit) before += __popcll(__ballot((c3 >> bit) & 1) & lt_mask) << bit;
-  const uint64_t reach = __ballot(before + c3 >= k);
-  const int ln = __builtin_ctzll(reach);
-  const int b0 = __builtin_amdgcn_readlane(before, ln), b1 = __builtin_amdgcn_readlane(c0, ln),
-            b2 = __builtin_amdgcn_readlane(c1, ln), b3 = __builtin_amdgcn_readlane(c2, ln),
-            b4 = __builtin_amdgcn_readlane(c3, ln);
-  // cumulative counts through bins 4ln .. 4ln+3 are b0+b1 .. b0+b4
-  const int jb = b0 + b1 >= k ? 0 : b0 + b2 >= k ? 1 : b0 + b3 >= k ? 2 : 3;
-  const int B = 4 * ln + jb;
-  const int m = b0 + (jb == 0 ? b1 : jb == 1 ? b2 : jb == 2 ? b3 : b4);  // experts in bins <= B
+    for (int i = 0; i < NV; ++i) cnt += __popcll(__ballot(s.bin[i] < t));
+    if (cnt < k) B = t;
+  }
+  int m = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    s.mask[i] = __ballot(s.bin[i] <= B);
+    m += __popcll(s.mask[i]);
+  }
+  s.B = B;
+  s.m = m;
+  return m == k;
+}
+
+// The j-th candidate in ascending expert order (j < m; uniform).
+template <int NV>
+__device__ __forceinline__ int topk_candidate(const TopkSel<NV>& s, int j) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    uint64_t mk = s.mask[i];
+    const int n = __popcll(mk);
+    if (j < n) {
+      for (; j > 0; --j) mk &= mk - 1;
+      return 64 * i + __builtin_ctzll(mk);
+    }
+    j -= n;
+  }
+  return -1;
+}
+
+// Order the selection: on return lane r < k holds the rank-r expert (logit
+// desc, index asc) and its softmax weight over all E experts.  The candidates
+// are compacted into lanes through LDS and ranked exactly against each other;
+// more than 64 candidates (many equal or clustered logits) fall back to an
+// exact radix select over all keys.
+template <int NV>
+__device__ __forceinline__ void wave_topk_order(const float (&v)[NV], int E, int k, unsigned flags,
+                                                const TopkSel<NV>& s, int& my_idx, float& my_w,
+                                                TopkScratch& sc) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const int m = s.m;
   if (m > 64) {  // degenerate: many logits in one bin
     wave_topk_radix<NV>(v, E, k, flags, my_idx, my_w, sc.list);
     return;
   }
-  // compact the candidates (bins <= B) into lanes 0 .. m-1 through LDS
+  // compact the candidates into lanes 0 .. m-1 through LDS
   int pos_base = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const bool c = bin[i] <= B;
-    const uint64_t cm = __ballot(c);
-    if (c) {
-      const int pos = pos_base + __popcll(cm & lt_mask);
+    if (s.bin[i] <= s.B) {
+      const int pos = pos_base + __popcll(s.mask[i] & lt_mask);
       sc.cz[pos] = __float_as_uint(v[i]);
       sc.ce[pos] = (uint32_t)(lane + 64 * i);
     }
-    pos_base += __popcll(cm);
+    pos_base += __popcll(s.mask[i]);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -235,7 +271,7 @@ __device__ __forceinline__ void wave_topk_regs(const float (&v)[NV], int E, int 
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
   if (lane < m && rank < k) {
-    sc.cz[rank] = __float_as_uint(__expf(z - zmax) * inv_se);
+    sc.cz[rank] = __float_as_uint(__expf(z - s.zmax) * s.inv_se);
     sc.ce[rank] = (uint32_t)e;
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -251,6 +287,15 @@ __device__ __forceinline__ void wave_topk_regs(const float (&v)[NV], int E, int 
     my_w /= tot;
   }
   __builtin_amdgcn_wave_barrier();
+}
+
+// Softmax + top-k: selection, then order (lane r < k: rank-r expert and weight).
+template <int NV>
+__device__ __forceinline__ void wave_topk_regs(const float (&v)[NV], int E, int k, unsigned flags,
+                                               int& my_idx, float& my_w, TopkScratch& sc) {
+  TopkSel<NV> s;
+  wave_topk_select<NV>(v, E, k, s);
+  wave_topk_order<NV>(v, E, k, flags, s, my_idx, my_w, sc);
 }
 
 template <int NV>

@@ -147,6 +147,53 @@ def test_route_ties_go_to_lower_index():
             assert row.index(4) < row.index(11) and row.index(2) < row.index(13)
 
 
+def _logit_shapes(E, rng):
+    z = {
+        "tiny_spread": rng.normal(0.0, 1e-3, E),
+        "wide_spread": rng.normal(0.0, 100.0, E),
+        "one_outlier": np.r_[1e4, rng.normal(0.0, 1.0, E - 1)],
+        "all_equal": np.full(E, 0.5),
+        "three_levels": rng.integers(0, 3, E).astype(np.float64),
+        "far_negative": -np.abs(rng.normal(0.0, 1.0, E)) - 50.0,
+    }
+    tied = rng.normal(0.0, 1.0, E)
+    tied[rng.choice(E, 20, replace=False)] = 5.0   # 20 equal best logits: ties by index
+    z["tied_top"] = tied
+    return {n: v.astype(np.float32) for n, v in z.items()}
+
+
+@pytest.mark.parametrize("E", [64, 256, 384])
+def test_topk_logit_shapes(E):
+    """Softmax/top-k on chosen logit vectors: token t is one-hot at column t, so
+    its logits are exactly router column t.  Tiny and wide spreads, an outlier,
+    ties and few distinct values take both the binned and the radix selection;
+    the route of 7 tokens (router GEMM), of each token alone (router GEMV) and
+    the decode layer's in-block selection all match the oracle."""
+    H, k, F = 256, 8, 256
+    rng = np.random.default_rng(7)
+    shapes = _logit_shapes(E, rng)
+    names = sorted(shapes)
+    T = len(names)
+    R = np.zeros((E, H), np.float32)
+    x = np.zeros((T, H), np.uint16)
+    for t, n in enumerate(names):
+        R[:, t] = shapes[n]
+        x[t, t] = 0x3F80                     # bf16 1.0
+    Rd = torch.from_numpy(R).cuda()
+    idx, w, _, _ = B.moe_route(_x_dev(x), Rd, k, want_perm=False)
+    _check_route(x, R, k, idx, w)
+    L = Layer(MX, H, E, F, cfg=0, layer=0, w_std=0.02)
+    pool, _ = L.device()
+    for t, n in enumerate(names):
+        xt = _x_dev(x[t:t + 1])
+        idx1, w1, _, _ = B.moe_route(xt, Rd, k, want_perm=False)
+        oidx, ow = _check_route(x[t:t + 1], R, k, idx1, w1)
+        idx2, w2, _ = B.moe_layer_forward(MX, pool, L.stride, H, F, E, k, xt, Rd)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx2.cpu().numpy(), oidx), n
+        assert np.allclose(w2.cpu().numpy(), ow, rtol=1e-3, atol=1e-7), n
+
+
 def test_permutation_skewed_and_empty_experts():
     H, E, k, T = 256, 64, 8, 500
     R = sy.router(0, 13, 0, E, H)
