@@ -287,6 +287,12 @@ __global__ __launch_bounds__(TOPK ? 576 : 512) void k_gateup_gemv(
   uint8_t* fill = miss ? const_cast<uint8_t*>(pool) + (size_t)s_slot * stride : nullptr;
   if (fill && g == 0 && threadIdx.x < 3)
     reinterpret_cast<float*>(fill + L.tau)[threadIdx.x] = reinterpret_cast<const float*>(blob + L.tau)[threadIdx.x];
+  // NVFP4 tensor scales, requested with the weights so the epilogue does not wait for them
+  float tau_g = 1.0f, tau_u = 1.0f;
+  if constexpr (FMT == MOE_FMT_NVFP4) {
+    tau_g = reinterpret_cast<const float*>(blob + L.tau)[0];
+    tau_u = reinterpret_cast<const float*>(blob + L.tau)[1];
+  }
   float ag = 0.0f, au = 0.0f;
   if (w < nw) {
     gateup_partial<FMT, NB>(blob, L, H / kFragK, g, xl, w, nw, lane, ag, au, fill);
@@ -322,9 +328,8 @@ __global__ __launch_bounds__(TOPK ? 576 : 512) void k_gateup_gemv(
       U += red[i][1][threadIdx.x];
     }
     if constexpr (FMT == MOE_FMT_NVFP4) {
-      const float* tau = reinterpret_cast<const float*>(blob + L.tau);
-      G *= tau[0];
-      U *= tau[1];
+      G *= tau_g;
+      U *= tau_u;
     }
     hbuf[(size_t)s_row * F + kFragRows * g + threadIdx.x] = f32_to_bf16_rne(silu_f32(G) * U);
   }
@@ -371,6 +376,15 @@ __global__ __launch_bounds__(512) void k_gateup_topk_stream(
     }
   }
   __syncthreads();
+  // NVFP4 tensor scales of the unit this thread finishes, requested before the stream
+  float tau_g = 1.0f, tau_u = 1.0f;
+  if constexpr (FMT == MOE_FMT_NVFP4) {
+    if (threadIdx.x < 16 * nu) {
+      const float* tp = reinterpret_cast<const float*>(pool + (size_t)s_slot[((u0 + (threadIdx.x >> 4)) / G) % k] * stride + L.tau);
+      tau_g = tp[0];
+      tau_u = tp[1];
+    }
+  }
   const int n_items = nu * per;
   // load cursor (unit, item within unit); items past the end re-load the last
   // one, so every load is unconditional
@@ -431,9 +445,8 @@ __global__ __launch_bounds__(512) void k_gateup_topk_stream(
       Us += red[ul][i][1][row];
     }
     if constexpr (FMT == MOE_FMT_NVFP4) {
-      const float* tau = reinterpret_cast<const float*>(pool + (size_t)s_slot[q % k] * stride + L.tau);
-      Gs *= tau[0];
-      Us *= tau[1];
+      Gs *= tau_g;
+      Us *= tau_u;
     }
     hbuf[(size_t)q * F + kFragRows * g + row] = f32_to_bf16_rne(silu_f32(Gs) * Us);
   }
@@ -459,6 +472,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
   const int S = F / kFragK;
   DownRows<FMT, NB> d;
   d.load(blob + L.cd, blob + L.sd, S, g, w, nw, lane);
+  const float tau_d = FMT == MOE_FMT_NVFP4 ? reinterpret_cast<const float*>(blob + L.tau)[2] : 1.0f;
   const uint4* h4 = reinterpret_cast<const uint4*>(hbuf + (size_t)q * F);
   for (int i = threadIdx.x; i < F / 8; i += blockDim.x) reinterpret_cast<uint4*>(hl)[i] = h4[i];
   __syncthreads();
@@ -475,7 +489,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
   if (threadIdx.x < 16) {
     float v = 0.0f;
     for (int i = 0; i < nw; ++i) v += red[i][threadIdx.x];
-    if constexpr (FMT == MOE_FMT_NVFP4) v *= reinterpret_cast<const float*>(blob + L.tau)[2];
+    if constexpr (FMT == MOE_FMT_NVFP4) v *= tau_d;
     y[(size_t)q * H + kFragRows * g + threadIdx.x] = v;
   }
 }
@@ -492,11 +506,15 @@ __global__ __launch_bounds__(1024) void k_down_combine_gemv(
     uint16_t* __restrict__ out, const int32_t* __restrict__ rec) {
   extern __shared__ __attribute__((aligned(16))) uint16_t hl_dyn[];
   if (rec && rec[0] != MOE_OK) return;  // cache capacity error: the pairs did not run
-  __shared__ float ys[16][16];
+  __shared__ float ys[16][16], ws[16];
   const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
   const int t = blockIdx.y, q = t * k + j, g = blockIdx.x;
   const int slot = pair_slot ? pair_slot[q] : topk_idx[q];
   const uint8_t* blob = pool + (size_t)slot * stride;
+  // the pair's mixing weight and NVFP4 down scale, requested with the weights
+  // so that the combine does not wait for them
+  const float wq = topk_w[q];
+  const float tau_d = FMT == MOE_FMT_NVFP4 ? reinterpret_cast<const float*>(blob + L.tau)[2] : 1.0f;
   uint16_t* hl = hl_dyn + (size_t)j * F;
   const int S = F / kFragK;
   // batches of NB steps through two register sets: batch b+2 is requested as
@@ -507,6 +525,7 @@ __global__ __launch_bounds__(1024) void k_down_combine_gemv(
   if (nb > 1) d1.load_clamped(blob + L.cd, blob + L.sd, S, g, NB, lane);
   const uint4* h4 = reinterpret_cast<const uint4*>(hbuf + (size_t)q * F);
   for (int i = lane; i < F / 8; i += 64) reinterpret_cast<uint4*>(hl)[i] = h4[i];
+  if (lane == 0) ws[j] = wq;
   __syncthreads();
   float a = 0.0f;
   int b = 0;
@@ -520,15 +539,14 @@ __global__ __launch_bounds__(1024) void k_down_combine_gemv(
   if (b + 1 < nb) a += d1.dot(hl, S, (b + 1) * NB, 1, lane);
   a = row_lanes_sum(a);
   if (lane < 16) {
-    if constexpr (FMT == MOE_FMT_NVFP4) a *= reinterpret_cast<const float*>(blob + L.tau)[2];
+    if constexpr (FMT == MOE_FMT_NVFP4) a *= tau_d;
     ys[j][lane] = a;
     if (y) y[(size_t)q * H + kFragRows * g + lane] = a;
   }
   __syncthreads();
   if (threadIdx.x < 16) {
-    const float* wt = topk_w + (size_t)t * k;
     float acc = 0.0f;
-    for (int jj = 0; jj < k; ++jj) acc = fmaf(wt[jj], ys[jj][threadIdx.x], acc);
+    for (int jj = 0; jj < k; ++jj) acc = fmaf(ws[jj], ys[jj][threadIdx.x], acc);
     out[(size_t)t * H + kFragRows * g + threadIdx.x] = f32_to_bf16_rne(acc);
   }
 }

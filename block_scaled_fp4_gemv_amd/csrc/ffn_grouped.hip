@@ -258,11 +258,11 @@ __device__ __forceinline__ void tile_step(floatx4_t (&acc)[NMAT][kCG<NMAT>][NS],
 
 // Results of one column tile: lane holds column 16*g + lane%16 of each of its
 // groups, rows 16r + 4(lane/16) + v of the tile.
+// tau: the expert's NVFP4 tensor scales (gate, up, down), read when the tile starts.
 template <int FMT, int NMAT, int NS>
 __device__ __forceinline__ void tile_epilogue(const TileArgs& t, const floatx4_t (&acc)[NMAT][kCG<NMAT>][NS], int g0,
-                                              int lane) {
+                                              const float (&tau)[3], int lane) {
   const int am = lane & 15, aq = lane >> 4;
-  const float* tau = reinterpret_cast<const float*>(t.blob + t.L.tau);
   if constexpr (NMAT == 2) {
     // h = bf16(silu(g) * u): each 16-row subtile (this wave's 32 columns) goes
     // through the wave's LDS patch so that a store covers 16 B per lane and the
@@ -347,6 +347,14 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
     codes[NMAT - 1] = t.blob + t.L.cu;
     scales[NMAT - 1] = t.blob + t.L.su;
   }
+  // NVFP4 tensor scales, requested now so that the epilogue does not wait for them
+  float tau[3] = {1.0f, 1.0f, 1.0f};
+  if constexpr (FMT == MOE_FMT_NVFP4) {
+    const float* tp = reinterpret_cast<const float*>(t.blob + t.L.tau);
+    tau[0] = tp[0];
+    tau[1] = tp[1];
+    tau[2] = tp[2];
+  }
 
   // activation staging rows (rows past the end repeat the last row; they land
   // in buffer rows no subtile reads)
@@ -405,7 +413,7 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NMAT == 1) {
       if ((u + 1) % S == S - 1) {
-        tile_epilogue<FMT, NMAT, NS>(t, acc, grp_of(u + 1), lane);
+        tile_epilogue<FMT, NMAT, NS>(t, acc, grp_of(u + 1), tau, lane);
         zero_acc<NMAT, NS>(acc);
       }
     }
@@ -415,9 +423,9 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
     a_store<NP, NW>(av, buf0, sr, sc);
     __syncthreads();
     tile_step<FMT, NMAT, NS>(acc, buf0, wb0, lane);
-    if constexpr (NMAT == 1) tile_epilogue<FMT, NMAT, NS>(t, acc, grp_of(u), lane);
+    if constexpr (NMAT == 1) tile_epilogue<FMT, NMAT, NS>(t, acc, grp_of(u), tau, lane);
   }
-  if constexpr (NMAT == 2) tile_epilogue<FMT, NMAT, NS>(t, acc, t.ct * (kBN<NMAT, NW> / kFragRows) + gw, lane);
+  if constexpr (NMAT == 2) tile_epilogue<FMT, NMAT, NS>(t, acc, t.ct * (kBN<NMAT, NW> / kFragRows) + gw, tau, lane);
 }
 
 // NMAT = 2: gate/up with SwiGLU into hout (expert-sorted rows, width N).
