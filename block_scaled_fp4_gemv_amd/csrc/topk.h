@@ -154,7 +154,7 @@ struct TopkScratch {
 // Selection state of one token's top-k on one wave (uniform except bin).
 template <int NV>
 struct TopkSel {
-  float zmax, inv_se;  // max logit; 1 / sum of exp(z - zmax) over all E
+  float zmax;          // max logit
   int B, m;            // threshold bin; experts in bins <= B (the candidates)
   uint64_t mask[NV];   // candidates: bit l of mask[i] is expert l + 64 i
   int bin[NV];         // per lane: bin of experts lane + 64 i (256 beyond E)
@@ -183,16 +183,13 @@ __device__ __forceinline__ bool wave_topk_select(const float (&v)[NV], int E, in
   zmin = wave_min(zmin);
   const float span = zmax - zmin;
   const float scale = span > 0.0f ? 255.0f / span : 0.0f;  // an infinite span gives 0: one bin
-  float se = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const bool ok = lane + 64 * i < E;
-    se += ok ? __expf(v[i] - zmax) : 0.0f;
     const float d = (zmax - v[i]) * scale;
     s.bin[i] = ok ? (d < 255.0f ? (int)d : 255) : 256;
   }
   s.zmax = zmax;
-  s.inv_se = 1.0f / wave_sum(se);
   // B = the largest bin number with fewer than k experts in lower bins
   int B = 0;
 #pragma unroll
@@ -246,6 +243,11 @@ __device__ __forceinline__ void wave_topk_order(const float (&v)[NV], int E, int
     wave_topk_radix<NV>(v, E, k, flags, my_idx, my_w, sc.list);
     return;
   }
+  float se = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (lane + 64 * i < E) se += __expf(v[i] - s.zmax);
+  const float inv_se = 1.0f / wave_sum(se);
   // compact the candidates into lanes 0 .. m-1 through LDS
   int pos_base = 0;
 #pragma unroll
@@ -271,7 +273,7 @@ __device__ __forceinline__ void wave_topk_order(const float (&v)[NV], int E, int
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
   if (lane < m && rank < k) {
-    sc.cz[rank] = __float_as_uint(__expf(z - s.zmax) * s.inv_se);
+    sc.cz[rank] = __float_as_uint(__expf(z - s.zmax) * inv_se);
     sc.ce[rank] = (uint32_t)e;
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
