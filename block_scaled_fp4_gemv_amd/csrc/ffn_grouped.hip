@@ -7,9 +7,9 @@
 // here in registers, straight into MFMA operands.
 //
 // Pairs arrive sorted by expert (pair_perm / expert_off).  A device-built tile
-// list holds one (expert, first row) entry per 96 rows of each expert (32 for
+// list holds one (expert, first row) entry per 96 rows of each expert (64 for
 // FP8, whose per-step partial sums need more registers).  A workgroup of NW
-// waves (8 for the FP4 formats, 4 for FP8) owns one tile x NW*32 output columns
+// waves (8 when the output width allows, else 4) owns one tile x NW*32 output columns
 // per matrix for gate/up (NW*64 for down): wave w takes the weight fragments
 // of its 32 (64) columns and all rows of the tile (up to six 16-row subtiles,
 // v_mfma_f32_16x16x32_bf16), so
@@ -55,7 +55,7 @@ constexpr int kBN = NW * kCG<NMAT> * kFragRows;
 constexpr int ROWB = BK * 2;                 // LDS bytes per activation row per step
 
 template <int FMT>
-constexpr int kSubMax = FMT == MOE_FMT_FP8_E4M3 ? 2 : 6;  // 16-row subtiles per tile
+constexpr int kSubMax = FMT == MOE_FMT_FP8_E4M3 ? 4 : 6;  // 16-row subtiles per tile
 template <int FMT>
 constexpr int kTileRows = kFragRows * kSubMax<FMT>;
 
@@ -431,7 +431,7 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
 // NMAT = 2: gate/up with SwiGLU into hout (expert-sorted rows, width N).
 // NMAT = 1: down into y rows of the original pairs.
 template <int FMT, int NMAT, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void k_grouped(
+__global__ __launch_bounds__(64 * NW, NW == 4 && FMT != MOE_FMT_FP8_E4M3 ? 2 : 1) void k_grouped(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int K, int N, int k_top,
     const uint16_t* __restrict__ a_src, int a_by_token, const int32_t* __restrict__ pair_perm,
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ tile_e,
@@ -514,7 +514,7 @@ void launch_grouped_k(const FfnArgs& a, int max_tiles, const int32_t* tile_e, co
                        a.stride, a.L, K, N, a.k, a_src, NMAT == 2 ? 1 : 0, a.pair_perm, a.expert_off, tile_e,  \
                        tile_m0, n_tiles, nct / np, np, NMAT == 2 ? a.hbuf : nullptr, NMAT == 2 ? nullptr : y); \
   }
-  if (FMT != MOE_FMT_FP8_E4M3 && N % kBN<NMAT, 8> == 0) GK(8) else GK(4)  // FP8: 32-row tiles, two workgroups per CU
+  if (N % kBN<NMAT, 8> == 0) GK(8) else GK(4)
 #undef GK
 }
 
@@ -538,7 +538,7 @@ hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
 }  // namespace
 
 size_t grouped_tiles_bytes(int T, int k, int E) {
-  // the FP4 formats use 96-row tiles and FP8 32-row tiles: size for the longer list
+  // the FP4 formats use 96-row tiles and FP8 64-row tiles: size for the longer list
   const int max_tiles = max_tiles_for<MOE_FMT_FP8_E4M3>(T * k, E);
   return align256((size_t)(2 * max_tiles + 1) * 4);
 }
