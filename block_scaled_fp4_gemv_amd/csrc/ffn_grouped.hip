@@ -7,16 +7,16 @@
 // here in registers, straight into MFMA operands.
 //
 // Pairs arrive sorted by expert (pair_perm / expert_off).  A device-built tile
-// list holds one (expert, first row) entry per 96 rows of each expert (64 for
+// list holds one (expert, first row) entry per 128 rows of each expert (64 for
 // FP8, whose per-step partial sums need more registers).  A workgroup of NW
 // waves (8 when the output width allows, else 4) owns one tile x NW*32 output columns
 // per matrix for gate/up (NW*64 for down): wave w takes the weight fragments
-// of its 32 (64) columns and all rows of the tile (up to six 16-row subtiles,
-// v_mfma_f32_16x16x32_bf16), so
-// each dequantized weight operand feeds one MFMA per subtile and an expert's
-// weights are fetched and dequantized once per column tile whenever it has at
-// most 96 rows.  The subtile count is a template parameter chosen per tile,
-// so the inner loop has no branches.
+// of its 32 (64) columns and all rows of the tile (up to eight 16-row
+// subtiles for gate/up, six for down, v_mfma_f32_16x16x32_bf16), so each
+// dequantized weight operand feeds one MFMA per subtile and an expert's gate
+// and up weights are fetched and dequantized once per column tile whenever it
+// has at most 128 rows (FP8: 64).  The subtile count is a template parameter
+// chosen per tile, so the inner loop has no branches.
 //
 // K runs in steps of 128 (one weight fragment).  The pre-shuffled blob gives
 // lane l its 32 consecutive k of the fragment with one 16-byte load; MFMA i
@@ -54,8 +54,11 @@ template <int NMAT, int NW>
 constexpr int kBN = NW * kCG<NMAT> * kFragRows;
 constexpr int ROWB = BK * 2;                 // LDS bytes per activation row per step
 
+// 16-row subtiles per tile of the list (gate/up runs a whole tile; down runs
+// tiles of more than 6 subtiles as two halves, its accumulators being twice
+// as wide)
 template <int FMT>
-constexpr int kSubMax = FMT == MOE_FMT_FP8_E4M3 ? 4 : 6;  // 16-row subtiles per tile
+constexpr int kSubMax = FMT == MOE_FMT_FP8_E4M3 ? 4 : 8;
 template <int FMT>
 constexpr int kTileRows = kFragRows * kSubMax<FMT>;
 
@@ -467,15 +470,39 @@ __global__ __launch_bounds__(64 * NW, NW == 4 && FMT != MOE_FMT_FP8_E4M3 ? 2 : 1
   t.pair_perm = pair_perm;
   t.hout = hout;
   t.yout = yout;
-  switch ((t.rows + kFragRows - 1) / kFragRows) {
+  const int ns = (t.rows + kFragRows - 1) / kFragRows;
+  if (NMAT == 1 && ns > 6) {
+    // down: the first 64 rows, then the rest, each with the tile's sweep
+    TileArgs t2 = t;
+    t.rows = 4 * kFragRows;
+    grouped_tile<FMT, NMAT, 4, NW>(t, As);
+    t2.row_base += 4 * kFragRows;
+    t2.rows -= 4 * kFragRows;
+    t2.rows_perm += 4 * kFragRows;
+    __syncthreads();  // the first half's last LDS reads are done before the second stages
+    switch (ns - 4) {
+      case 3: grouped_tile<FMT, NMAT, 3, NW>(t2, As); break;
+      default: grouped_tile<FMT, NMAT, 4, NW>(t2, As); break;
+    }
+    return;
+  }
+  switch (ns) {
     case 1: grouped_tile<FMT, NMAT, 1, NW>(t, As); break;
     case 2: grouped_tile<FMT, NMAT, 2, NW>(t, As); break;
     case 3: grouped_tile<FMT, NMAT, 3, NW>(t, As); break;
     case 4: grouped_tile<FMT, NMAT, 4, NW>(t, As); break;
     default:
       if constexpr (kSubMax<FMT> >= 6) {
-        if (t.rows > 5 * kFragRows) grouped_tile<FMT, NMAT, 6, NW>(t, As);
-        else grouped_tile<FMT, NMAT, 5, NW>(t, As);
+        switch (ns) {
+          case 5: grouped_tile<FMT, NMAT, 5, NW>(t, As); break;
+          case 6: grouped_tile<FMT, NMAT, 6, NW>(t, As); break;
+          default:
+            if constexpr (NMAT == 2) {
+              if (ns == 7) grouped_tile<FMT, NMAT, 7, NW>(t, As);
+              else grouped_tile<FMT, NMAT, 8, NW>(t, As);
+            }
+            break;
+        }
       }
       break;
   }
@@ -514,7 +541,8 @@ void launch_grouped_k(const FfnArgs& a, int max_tiles, const int32_t* tile_e, co
                        a.stride, a.L, K, N, a.k, a_src, NMAT == 2 ? 1 : 0, a.pair_perm, a.expert_off, tile_e,  \
                        tile_m0, n_tiles, nct / np, np, NMAT == 2 ? a.hbuf : nullptr, NMAT == 2 ? nullptr : y); \
   }
-  if (N % kBN<NMAT, 8> == 0) GK(8) else GK(4)
+  // gate/up widths are multiples of 256 (8-wave tiles); down takes 4 waves for hidden 256
+  if constexpr (NMAT == 2) GK(8) else if (N % kBN<NMAT, 8> == 0) GK(8) else GK(4)
 #undef GK
 }
 
@@ -523,7 +551,7 @@ hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
   const int n_pairs = a.T * a.k;
   const int max_tiles = max_tiles_for<FMT>(n_pairs, a.E);
   int32_t *tile_e = tiles, *tile_m0 = tiles + max_tiles, *n_tiles = tiles + 2 * max_tiles;
-  if (a.F % kBN<2, 4> || a.H % kBN<1, 4> || a.H % BK || a.F % BK) return hipErrorInvalidValue;
+  if (a.F % kBN<2, 8> || a.H % kBN<1, 4> || a.H % BK || a.F % BK) return hipErrorInvalidValue;
   if (!a.tiles_ready)  // else the permutation kernel wrote the list (grouped_tile_rows / grouped_max_tiles)
     hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E, kTileRows<FMT>, tile_e,
                        tile_m0, n_tiles);
@@ -538,7 +566,7 @@ hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
 }  // namespace
 
 size_t grouped_tiles_bytes(int T, int k, int E) {
-  // the FP4 formats use 96-row tiles and FP8 64-row tiles: size for the longer list
+  // the FP4 formats use 128-row tiles and FP8 64-row tiles: size for the longer list
   const int max_tiles = max_tiles_for<MOE_FMT_FP8_E4M3>(T * k, E);
   return align256((size_t)(2 * max_tiles + 1) * 4);
 }

@@ -656,9 +656,10 @@ def test_grouped_35b_shape(fmt, T):
 
 @pytest.mark.parametrize("fmt", [NV, MX, F8])
 def test_grouped_many_rows_per_expert(fmt):
-    """About 128 rows per expert: several row tiles per expert (96-row FP4
-    tiles, 32-row FP8 tiles), odd subtile counts, and down workgroups that
-    sweep two column tiles (hidden 512 = 4 column tiles, width 1024 = 8 steps)."""
+    """About 128 rows per expert: several row tiles per expert (128-row FP4
+    tiles, which the down kernel runs as two halves past 96 rows; 64-row FP8
+    tiles), odd subtile counts, and down workgroups that sweep two column tiles
+    (hidden 512 = 4 column tiles, width 1024 = 8 steps)."""
     _grouped_case(fmt, 512, 16, 1024, 4, 512, cfg=45, sample=96)
 
 
