@@ -293,6 +293,23 @@ __global__ __launch_bounds__(TOPK ? 576 : 512) void k_gateup_gemv(
     tau_g = reinterpret_cast<const float*>(blob + L.tau)[0];
     tau_u = reinterpret_cast<const float*>(blob + L.tau)[1];
   }
+  // the workgroups of a streamed miss also bring its down matrix (codes and
+  // scales) into the slot, so the down kernel reads every pair from VRAM; the
+  // first chunks of each thread are requested before the gate/up fragments,
+  // so that their round trips over the link overlap
+  constexpr int kEarly = 4;
+  const size_t cdb = (size_t)H * F / (FMT == MOE_FMT_FP8_E4M3 ? 1 : 2);
+  const size_t sdb = FMT == MOE_FMT_NVFP4 ? (size_t)H * F / 16 : FMT == MOE_FMT_MXFP4 ? (size_t)H * F / 32
+                                                                                    : (size_t)H * (F / 128) * 4;
+  const size_t nc = cdb / 16, ns = sdb / 16, step = (size_t)gridDim.x * blockDim.x;
+  const size_t c0 = (size_t)g * blockDim.x + threadIdx.x;
+  uint4 early[kEarly], early_s = make_uint4(0u, 0u, 0u, 0u);
+  if (fill) {
+#pragma unroll
+    for (int i = 0; i < kEarly; ++i)
+      if (c0 + i * step < nc) early[i] = reinterpret_cast<const uint4*>(blob + L.cd)[c0 + i * step];
+    if (c0 < ns) early_s = reinterpret_cast<const uint4*>(blob + L.sd)[c0];
+  }
   float ag = 0.0f, au = 0.0f;
   if (w < nw) {
     gateup_partial<FMT, NB>(blob, L, H / kFragK, g, xl, w, nw, lane, ag, au, fill);
@@ -301,18 +318,16 @@ __global__ __launch_bounds__(TOPK ? 576 : 512) void k_gateup_gemv(
       if (set_first) order(topk_candidate<NV>(sel, j));
   }
   if (fill) {
-    // the workgroups of a streamed miss also bring its down matrix (codes and
-    // scales) into the slot, so the down kernel reads every pair from VRAM
-    const size_t cd = (size_t)H * F / (FMT == MOE_FMT_FP8_E4M3 ? 1 : 2);
-    const size_t sd = FMT == MOE_FMT_NVFP4 ? (size_t)H * F / 16 : FMT == MOE_FMT_MXFP4 ? (size_t)H * F / 32
-                                                                                     : (size_t)H * (F / 128) * 4;
-    const size_t nc = cd / 16, ns = sd / 16, step = (size_t)gridDim.x * blockDim.x;
     const uint4* sc4 = reinterpret_cast<const uint4*>(blob + L.cd);
     uint4* dc4 = reinterpret_cast<uint4*>(fill + L.cd);
-    for (size_t c = (size_t)g * blockDim.x + threadIdx.x; c < nc; c += step) dc4[c] = sc4[c];
+#pragma unroll
+    for (int i = 0; i < kEarly; ++i)
+      if (c0 + i * step < nc) dc4[c0 + i * step] = early[i];
+    for (size_t c = c0 + kEarly * step; c < nc; c += step) dc4[c] = sc4[c];
     const uint4* ss4 = reinterpret_cast<const uint4*>(blob + L.sd);
     uint4* ds4 = reinterpret_cast<uint4*>(fill + L.sd);
-    for (size_t c = (size_t)g * blockDim.x + threadIdx.x; c < ns; c += step) ds4[c] = ss4[c];
+    if (c0 < ns) ds4[c0] = early_s;
+    for (size_t c = c0 + step; c < ns; c += step) ds4[c] = ss4[c];
   }
   ag = row_lanes_sum(ag);
   au = row_lanes_sum(au);

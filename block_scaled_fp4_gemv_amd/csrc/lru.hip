@@ -60,6 +60,21 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     float* __restrict__ topk_w) {
   __shared__ int s_idx[kMaxFusedPairs];
   const int32_t* idx = idx_in;
+  const int tid = threadIdx.x;
+  // the cache state and the clock are requested first, so that their loads
+  // overlap the fused top-k
+  constexpr int kPer = kMaxE / kThreads;
+  static_assert(kMaxS <= kMaxE, "state registers sized by kMaxE");
+  int r_eslot[kPer], r_sexp[kPer];
+  long long r_stamp[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid + i * kThreads;
+    r_eslot[i] = e < E ? expert_slot[e] : -1;
+    r_sexp[i] = e < S ? slot_expert[e] : -1;
+    r_stamp[i] = e < S ? slot_stamp[e] : 0;
+  }
+  const long long c0 = *clock;
   if constexpr (NV > 0) {
     __shared__ TopkScratch s_topk[kThreads / 64];
     const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63, T = n / k;
@@ -90,18 +105,20 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
   __shared__ int s_miss_exp[kMaxS];
   __shared__ int s_scan[kThreads / 64];
   __shared__ int s_nmiss, s_ncand;
-  const int tid = threadIdx.x;
 
-  for (int e = tid; e < E; e += blockDim.x) {
-    s_first[e] = n;
-    s_last[e] = -1;
-    const int sl = expert_slot[e];
-    s_eslot[e] = sl;
-    s_resident[e] = sl >= 0;
-  }
-  for (int s = tid; s < S; s += blockDim.x) {
-    s_sexp[s] = slot_expert[s];
-    s_stamp[s] = slot_stamp[s];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid + i * kThreads;
+    if (e < E) {
+      s_first[e] = n;
+      s_last[e] = -1;
+      s_eslot[e] = r_eslot[i];
+      s_resident[e] = r_eslot[i] >= 0;
+    }
+    if (e < S) {
+      s_sexp[e] = r_sexp[i];
+      s_stamp[e] = r_stamp[i];
+    }
   }
   __syncthreads();
   for (int q = tid; q < n; q += blockDim.x) {
@@ -184,7 +201,6 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     s_eslot[e] = s;
   }
   __syncthreads();
-  const long long c0 = *clock;
   // stamps: last access of each requested expert
   for (int q = tid; q < n; q += blockDim.x) {
     const int e = idx[q];
