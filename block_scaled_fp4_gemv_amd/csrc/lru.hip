@@ -251,6 +251,162 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
   }
 }
 
+// ------------------------------------------------------------ one-wave step
+// The same step for at most 64 accesses on at most 64 slots, on one wavefront
+// and without barriers: lane q holds access q and lane s slot s, and the
+// cross-lane steps are ballots and lane reads.  It writes the same state,
+// pair slots, pair order and miss record as k_lru_lookup.  FUSED: the accesses
+// are the top-k of one token's logits (E <= 64*NE), selected here first.
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int NE, bool FUSED>
+__global__ __launch_bounds__(64) void k_lru_lookup_wave(
+    int E, int S, int32_t* __restrict__ slot_expert, int32_t* __restrict__ expert_slot,
+    int64_t* __restrict__ slot_stamp, int64_t* __restrict__ clock,
+    const int32_t* __restrict__ idx_in, int n, int32_t* __restrict__ pair_slot,
+    int32_t* __restrict__ pair_order, int32_t* __restrict__ rec, int n_max,
+    const float* __restrict__ logits, int k, unsigned flags, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+  const int lane = threadIdx.x;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  // the state at the step start, requested before the top-k
+  int es[NE];  // expert_slot[lane + 64 i]
+#pragma unroll
+  for (int i = 0; i < NE; ++i) es[i] = lane + 64 * i < E ? expert_slot[lane + 64 * i] : -1;
+  const int sexp0 = lane < S ? slot_expert[lane] : -1;
+  const long long stamp0 = lane < S ? slot_stamp[lane] : 0;
+  const long long c0 = *clock;
+  // expert of access q = lane
+  int e = -1;
+  if constexpr (FUSED) {
+    __shared__ TopkScratch s_topk;
+    float v[NE];
+    wave_load_logits<NE>(logits, E, v);
+    float wt;
+    wave_topk_regs<NE>(v, E, k, flags, e, wt, s_topk);
+    if (lane < k) {
+      topk_idx[lane] = e;
+      topk_w[lane] = wt;
+    }
+  } else {
+    if (lane < n) e = idx_in[lane];
+  }
+  const bool act = lane < n;
+  if (!act) e = -1;
+  // the expert's slot at the step start: expert_slot[e] sits in lane e % 64, register e / 64
+  int slot0 = -1;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int v = __shfl(es[i], e & 63);
+    if (act && (e >> 6) == i) slot0 = v;
+  }
+  // first and last access of the access's expert
+  int first = lane, last = lane;
+  for (int p = 0; p < n; ++p) {
+    const int ep = __builtin_amdgcn_readlane(e, p);
+    if (act && ep == e) {
+      first = min(first, p);
+      last = max(last, p);
+    }
+  }
+  const bool resident = slot0 >= 0;
+  // distinct missed experts, ranked by first access
+  const uint64_t miss_first = __ballot(act && first == lane && !resident);
+  const int n_miss = __popcll(miss_first);
+  const int miss_rank = __popcll(miss_first & lt);
+  // slots requested this step: the start slots of the resident experts accessed
+  uint64_t req = 0;
+  for (uint64_t m = __ballot(act && resident); m; m &= m - 1)
+    req |= 1ull << __builtin_amdgcn_readlane(slot0, __builtin_ctzll(m));
+  // candidate victims (lane s = slot s): slots not requested, ordered by
+  // (occupied, stamp), ties by index
+  const bool cand = lane < S && !((req >> lane) & 1ull);
+  uint64_t key = cand ? ((uint64_t)(sexp0 >= 0) << 62) | (uint64_t)stamp0 : ~0ull;
+  const int n_cand = __popcll(__ballot(cand));
+  if (n_cand < n_miss) {
+    if (lane == 0) {
+      rec[0] = MOE_E_CAPACITY;
+      rec[1] = n_miss;
+      rec[2] = 0;
+      rec[3] = 0;
+      rec[4] = n_max;
+    }
+    return;
+  }
+  // lane r < n_miss: victim slot of the r-th missed expert (the r-th smallest key),
+  // that expert and the one it evicts
+  int victim = -1, new_e = -1, old_e = -1;
+  uint64_t mf = miss_first;
+  for (int r = 0; r < n_miss; ++r) {
+    uint64_t bk = key;
+    int bs = lane;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t ok = shfl_xor_u64(bk, off);
+      const int os = __shfl_xor(bs, off);
+      if (ok < bk || (ok == bk && os < bs)) {
+        bk = ok;
+        bs = os;
+      }
+    }
+    const int vs = __builtin_amdgcn_readfirstlane(bs);
+    const int er = __builtin_amdgcn_readlane(e, __builtin_ctzll(mf));
+    mf &= mf - 1;
+    const int eo = __builtin_amdgcn_readlane(sexp0, vs);
+    if (lane == vs) key = ~0ull;
+    if (lane == r) {
+      victim = vs;
+      new_e = er;
+      old_e = eo;
+    }
+  }
+  // slot state after the install (lane s = slot s)
+  int sexp = sexp0;
+  long long stamp = stamp0;
+  for (int r = 0; r < n_miss; ++r)
+    if (lane == __builtin_amdgcn_readlane(victim, r)) sexp = __builtin_amdgcn_readlane(new_e, r);
+  // the access's slot after the install: a missed expert's victim, by the
+  // miss rank of its first access
+  const int rr = __shfl(miss_rank, first & 63);
+  const int vslot = __shfl(victim, rr & 63);
+  const int slot = act && !resident ? vslot : slot0;
+  // the last access of each expert stamps its slot with clock0 + index + 1
+  for (uint64_t m = __ballot(act && last == lane); m; m &= m - 1) {
+    const int q = __builtin_ctzll(m);
+    if (lane == __builtin_amdgcn_readlane(slot, q)) stamp = c0 + q + 1;
+  }
+  // pair order: resident-at-start accesses first, then the others, each ascending
+  const uint64_t hm = __ballot(act && resident), mm = __ballot(act && !resident);
+  const int nh = __popcll(hm);
+  if (act) {
+    pair_slot[lane] = slot;
+    pair_order[resident ? __popcll(hm & lt) : nh + __popcll(mm & lt)] = lane;
+  }
+  if (lane < S) {
+    slot_expert[lane] = sexp;
+    slot_stamp[lane] = stamp;
+  }
+  if (lane < n_miss) {
+    if (old_e >= 0) expert_slot[old_e] = -1;
+    expert_slot[new_e] = victim;
+    rec[5 + lane] = new_e;
+    rec[5 + n_max + lane] = victim;
+  }
+  if (lane == 0) {
+    *clock = c0 + n;
+    rec[0] = MOE_OK;
+    rec[1] = n_miss;
+    rec[2] = nh;
+    rec[3] = n - n_miss;
+    rec[4] = n_max;
+  }
+}
+
 __global__ void k_lru_reset(int E, int S, int32_t* slot_expert, int32_t* expert_slot,
                             int64_t* slot_stamp, int64_t* clock) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -274,6 +430,17 @@ hipError_t launch_lru_reset(const moe_lru& l, hipStream_t s) {
 hipError_t launch_lru_lookup(const moe_lru& l, const int32_t* topk_idx, int n_pairs,
                              int32_t* pair_slot, int32_t* pair_order, int32_t* miss_rec, int n_max,
                              hipStream_t s) {
+  if (l.S <= 64 && n_pairs <= 64) {  // one wavefront
+#define W(NE)                                                                                           \
+  hipLaunchKernelGGL((k_lru_lookup_wave<NE, false>), dim3(1), dim3(64), 0, s, l.E, l.S, l.slot_expert,  \
+                     l.expert_slot, l.slot_stamp, l.clock, topk_idx, n_pairs, pair_slot, pair_order,     \
+                     miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr)
+    if (l.E <= 64) W(1);
+    else if (l.E <= 256) W(4);
+    else W(16);
+#undef W
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_lru_lookup<0>, dim3(1), dim3(kThreads), 0, s, l.E, l.S, l.slot_expert,
                      l.expert_slot, l.slot_stamp, l.clock, topk_idx, n_pairs, pair_slot, pair_order,
                      miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr);
@@ -284,6 +451,17 @@ hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int T, 
                                   int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
                                   int32_t* miss_rec, int n_max, hipStream_t s) {
   if (T > kThreads / 64 || k > 16) return hipErrorInvalidValue;
+  if (T == 1 && l.S <= 64) {  // one wavefront
+#define W(NE)                                                                                           \
+  hipLaunchKernelGGL((k_lru_lookup_wave<NE, true>), dim3(1), dim3(64), 0, s, l.E, l.S, l.slot_expert,   \
+                     l.expert_slot, l.slot_stamp, l.clock, nullptr, k, pair_slot, pair_order, miss_rec,  \
+                     n_max, logits, k, flags, topk_idx, topk_w)
+    if (l.E <= 64) W(1);
+    else if (l.E <= 256) W(4);
+    else W(16);
+#undef W
+    return hipGetLastError();
+  }
 #define L(NV)                                                                                           \
   hipLaunchKernelGGL(k_lru_lookup<NV>, dim3(1), dim3(kThreads), 0, s, l.E, l.S, l.slot_expert,          \
                      l.expert_slot, l.slot_stamp, l.clock, nullptr, T * k, pair_slot, pair_order, miss_rec, \

@@ -250,16 +250,24 @@ def _lookup_vs_oracle(E, S, trace):
         assert int(st.clock.item()) == ref.clock
 
 
-def test_lru_lookup_matches_oracle_top8_trace():
+@pytest.mark.parametrize("E,S,T", [(256, 64, 1), (256, 64, 6), (512, 96, 1), (256, 96, 10)])
+def test_lru_lookup_matches_oracle_top8_trace(E, S, T):
+    """Top-8 traces (about 80% of a token's experts kept from the previous
+    step; experts repeat across the tokens of a step): up to 64 slots and 64
+    accesses take the one-wavefront lookup, 96 slots or 80 accesses the
+    workgroup one."""
     rng = np.random.default_rng(0)
-    E, S, k = 256, 64, 8
-    prev = rng.choice(E, k, replace=False)
+    k = 8
+    prev = [rng.choice(E, k, replace=False) for _ in range(T)]
     trace = []
-    for _ in range(200):
-        keep = prev[rng.random(k) < 0.8]
-        fresh = rng.choice(np.setdiff1d(np.arange(E), keep), k - len(keep), replace=False)
-        prev = np.concatenate([keep, fresh])
-        trace.append(prev.reshape(1, k).copy())
+    for _ in range(200 if T == 1 else 60):
+        step = []
+        for t in range(T):
+            keep = prev[t][rng.random(k) < 0.8]
+            fresh = rng.choice(np.setdiff1d(np.arange(E), keep), k - len(keep), replace=False)
+            prev[t] = np.concatenate([keep, fresh])
+            step.append(prev[t])
+        trace.append(np.stack(step).copy())
     _lookup_vs_oracle(E, S, trace)
 
 
@@ -427,38 +435,38 @@ def test_cached_layer_forward(fmt):
             assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
 
 
-@pytest.mark.parametrize("fmt", [NV, F8])
-def test_cached_layer_enqueue(fmt):
+@pytest.mark.parametrize("fmt,T", [(NV, 1), (F8, 1), (NV, 3)])
+def test_cached_layer_enqueue(fmt, T):
     """The one-stream executor (device hit/miss split, misses streamed from the
     pinned host pool and written into their slots), three steps enqueued back to
     back between synchronisations: every step's routing and output equal the
     all-resident moe_layer_forward bit for bit, the device miss record equals the
-    oracle LRU, and
-    after each step the occupied slots hold exactly the host blobs of their
-    experts."""
+    oracle LRU, and after each step the occupied slots hold exactly the host
+    blobs of their experts.  One token per step takes the one-wavefront lookup
+    with the top-k fused; three tokens the workgroup lookup."""
     from oracle import lru as olru
     H, E, F, k, S = 256, 16, 512, 2, 6
     L = Layer(fmt, H, E, F, cfg=23, layer=0, w_std=0.02)
-    xs = ar1_states(0, 23, 24, H, [L.router], k)
+    n = 24 if T == 1 else 8
+    xs = ar1_states(0, 23, n * T, H, [L.router], k)
     pool_res, R = L.device()
     hp = L.host_pool()
     host = torch.empty(E * L.stride, dtype=torch.uint8).pin_memory()
     host.numpy()[:] = hp
     slots = torch.zeros(S * L.stride, dtype=torch.uint8, device="cuda")
-    cl = B.CachedLayer(R, host, slots, E, S, 1, k, rec_on_device=True)
-    ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    cl = B.CachedLayer(R, host, slots, E, S, T, k, rec_on_device=True)
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, T, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
     ref_lru = olru.StampLRU(E, S)
     eb = B.moe_expert_bytes(fmt, H, F)
-    n = xs.shape[0]
-    outs = [torch.empty((1, H), dtype=torch.uint16, device="cuda") for _ in range(n)]
-    idxs = [torch.empty((1, k), dtype=torch.int32, device="cuda") for _ in range(n)]
-    ws_ = [torch.empty((1, k), dtype=torch.float32, device="cuda") for _ in range(n)]
+    outs = [torch.empty((T, H), dtype=torch.uint16, device="cuda") for _ in range(n)]
+    idxs = [torch.empty((T, k), dtype=torch.int32, device="cuda") for _ in range(n)]
+    ws_ = [torch.empty((T, k), dtype=torch.float32, device="cuda") for _ in range(n)]
     recs = []
-    pair_slot = torch.empty(k, dtype=torch.int32, device="cuda")
-    pair_order = torch.empty(k, dtype=torch.int32, device="cuda")
+    pair_slot = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pair_order = torch.empty(T * k, dtype=torch.int32, device="cuda")
     for t in range(n):
-        B.moe_cached_layer_enqueue(fmt, L.stride, H, F, E, k, cl, _x_dev(xs[t:t + 1]), idxs[t], ws_[t], pair_slot,
-                                   pair_order, outs[t], ws)
+        B.moe_cached_layer_enqueue(fmt, L.stride, H, F, E, k, cl, _x_dev(xs[t * T:(t + 1) * T]), idxs[t], ws_[t],
+                                   pair_slot, pair_order, outs[t], ws)
         recs.append(cl.miss_rec.clone())
         if t % 3 == 2 or t == n - 1:
             torch.cuda.synchronize()
@@ -471,15 +479,16 @@ def test_cached_layer_enqueue(fmt):
     for t in range(n):
         # batch <= 4: the same router GEMV, in-kernel top-k, gate/up and fused
         # down + combine arithmetic as the resident decode layer
-        idx_r, w_r, out_res = B.moe_layer_forward(fmt, pool_res, L.stride, H, F, E, k, _x_dev(xs[t:t + 1]), R)
+        idx_r, w_r, out_res = B.moe_layer_forward(fmt, pool_res, L.stride, H, F, E, k,
+                                                  _x_dev(xs[t * T:(t + 1) * T]), R)
         torch.cuda.synchronize()
         assert torch.equal(idxs[t], idx_r) and torch.equal(ws_[t], w_r), f"step {t}"
         assert torch.equal(outs[t], out_res), f"step {t}"
         r = ref_lru.step(idxs[t].cpu().numpy().ravel())
         rec = recs[t].cpu().numpy()
         assert rec[0] == 0 and (rec[3], rec[1]) == (r["n_hits"], r["n_miss"]), f"step {t}"
-    _check_route(xs[:1], L.router, k, idxs[0], ws_[0])
-    ref = moe.moe_layer(fmt, xs[:1], L.router, L.experts, k)
+    _check_route(xs[:T], L.router, k, idxs[0], ws_[0])
+    ref = moe.moe_layer(fmt, xs[:T], L.router, L.experts, k)
     assert_rows_close(bf16_dev_to_f64(outs[0]), fm.bf16_to_f64(ref["out"]), what="out")
 
 
