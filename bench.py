@@ -420,8 +420,9 @@ def main():
     lws = [B.new_layer_workspace(fmt, 1, H, F, k, E) for _ in range(n_layers)]
 
     def layer(l):
+        # the next layer's router (a static weight) is read ahead during this layer's down kernel
         B.moe_layer_forward(fmt, pools[l], stride, H, F, E, k, x, routers[l], topk_idx=idx[l],
-                            topk_w=w[l], out=out[l], ws=lws[l])
+                            topk_w=w[l], out=out[l], ws=lws[l], warm=routers[(l + 1) % n_layers])
 
     def step():
         for l in range(n_layers):
@@ -493,7 +494,8 @@ def main():
                                f"top-{k}, expert width {F}, batch 1",
                    "layers": n_layers, "hidden": H, "experts": E, "top_k": k, "expert_width": F,
                    "format": {1: "nvfp4", 2: "mxfp4", 3: "fp8"}[fmt], "batch": 1,
-                   "graph": "one HIP graph per step"},
+                   "graph": "one HIP graph per step",
+                   "read_ahead": "each layer's down kernel warms the next layer's router (moe_layer_forward_prefetch)"},
         "weight_stream_GBps": round(stream_gbps, 1),
         "weight_stream_frac_of_hbm": round(stream_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"kernel": "moe_layer_forward decode layer (router GEMV, gate/up+SwiGLU with "

@@ -53,6 +53,8 @@ SIGNATURES = {
     "moe_layer_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_layer_forward": (_i32, [_i32, _vp, _sz, _i32, _i32, _i32, _i32, _u32, _vp, _i32, _vp, _vp, _vp,
                                  _vp, _vp, _sz, _vp]),
+    "moe_layer_forward_prefetch": (_i32, [_i32, _vp, _sz, _i32, _i32, _i32, _i32, _u32, _vp, _i32, _vp, _vp,
+                                          _vp, _vp, _vp, _sz, _vp, _sz, _vp]),
     "moe_cached_layer_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_cache_fill_device": (_i32, [_vp, _vp, _vp, _sz, _sz, _vp, _vp, _vp, _vp]),
     "moe_cached_layer_enqueue": (_i32, [_i32, _sz, _i32, _i32, _i32, _i32, _u32,
@@ -309,7 +311,10 @@ def new_layer_workspace(fmt, T, H, F, k, E, device="cuda"):
 
 
 def moe_layer_forward(fmt, pool, stride, H, F, E, k, x, router, flags=0, topk_idx=None, topk_w=None,
-                      out=None, ws=None, stream=None):
+                      out=None, ws=None, stream=None, warm=None):
+    """moe_layer_forward; with `warm` (a device tensor, e.g. the next layer's
+    router) moe_layer_forward_prefetch, which reads it ahead during the decode
+    down kernel."""
     import torch
     T = x.shape[0]
     dev = x.device
@@ -321,10 +326,17 @@ def moe_layer_forward(fmt, pool, stride, H, F, E, k, x, router, flags=0, topk_id
         out = torch.empty((T, H), dtype=torch.uint16, device=dev)
     if ws is None:
         ws = new_layer_workspace(fmt, T, H, F, k, E, dev)
-    st = lib().moe_layer_forward(fmt, _ptr(pool), stride, H, F, E, k, flags, _ptr(x), T, _ptr(router),
-                                 _ptr(topk_idx), _ptr(topk_w), _ptr(out), _ptr(ws), ws.numel(),
-                                 _stream(stream))
-    _check(st, "moe_layer_forward")
+    if warm is None:
+        st = lib().moe_layer_forward(fmt, _ptr(pool), stride, H, F, E, k, flags, _ptr(x), T, _ptr(router),
+                                     _ptr(topk_idx), _ptr(topk_w), _ptr(out), _ptr(ws), ws.numel(),
+                                     _stream(stream))
+        _check(st, "moe_layer_forward")
+    else:
+        st = lib().moe_layer_forward_prefetch(fmt, _ptr(pool), stride, H, F, E, k, flags, _ptr(x), T,
+                                              _ptr(router), _ptr(topk_idx), _ptr(topk_w), _ptr(out), _ptr(ws),
+                                              ws.numel(), _ptr(warm), warm.numel() * warm.element_size(),
+                                              _stream(stream))
+        _check(st, "moe_layer_forward_prefetch")
     return topk_idx, topk_w, out
 
 

@@ -512,14 +512,37 @@ __global__ __launch_bounds__(512) void k_down_gemv(
 // Down for all k pairs of token blockIdx.y (wave j = pair j) on rows
 // 16*blockIdx.x.., with the gate-weighted combine fused:
 // out[t] = bf16(sum_j w_j * y_j) accumulated in fp32 in j order.
-// Dynamic LDS: k rows of h (F bf16 each).
+// Dynamic LDS: k rows of h (F bf16 each).  Workgroups past the H/16 row groups
+// (token 0 only) read an equal share of `warm` and discard it, so that a later
+// kernel finds those bytes in the memory-side cache.
 template <int FMT, int NB>
 __global__ __launch_bounds__(1024) void k_down_combine_gemv(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int H, int F, int k,
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ pair_slot,
     const uint16_t* __restrict__ hbuf, const float* __restrict__ topk_w, float* __restrict__ y,
-    uint16_t* __restrict__ out, const int32_t* __restrict__ rec) {
+    uint16_t* __restrict__ out, const int32_t* __restrict__ rec, const uint8_t* __restrict__ warm,
+    size_t warm_bytes) {
   extern __shared__ __attribute__((aligned(16))) uint16_t hl_dyn[];
+  if ((int)blockIdx.x >= H / kFragRows) {
+    if (blockIdx.y != 0) return;
+    const int nb = gridDim.x - H / kFragRows, b = blockIdx.x - H / kFragRows;
+    const size_t n16 = warm_bytes / 16, per = (n16 + nb - 1) / nb, i0 = (size_t)b * per;
+    const size_t i1 = min(n16, i0 + per);
+    const uint4* p4 = reinterpret_cast<const uint4*>(warm);
+    uint32_t acc = 0;
+    for (size_t i = i0 + threadIdx.x; i < i1; i += 4 * blockDim.x) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t iu = i + (size_t)u * blockDim.x;
+        v[u] = iu < i1 ? p4[iu] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].w;
+    }
+    if (H == 0 && acc == 1u) out[0] = 0;  // never (H > 0): keeps the loads
+    return;
+  }
   if (rec && rec[0] != MOE_OK) return;  // cache capacity error: the pairs did not run
   __shared__ float ys[16][16], ws[16];
   const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
@@ -564,6 +587,17 @@ __global__ __launch_bounds__(1024) void k_down_combine_gemv(
     for (int jj = 0; jj < k; ++jj) acc = fmaf(ws[jj], ys[jj][threadIdx.x], acc);
     out[(size_t)t * H + kFragRows * g + threadIdx.x] = f32_to_bf16_rne(acc);
   }
+}
+
+// Compute units of the current device (one device model per process).
+int compute_units() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      n = cu;
+  }
+  return n;
 }
 
 template <int FMT, bool TOPK, int NV>
@@ -641,7 +675,8 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
 #define LC(NB)                                                                                         \
   case NB:                                                                                             \
     hipLaunchKernelGGL((k_down_combine_gemv<FMT, NB>), grid, dim3(64 * a.k), lds, s, a.pool, a.stride, a.L, \
-                       a.H, a.F, a.k, a.topk_idx, a.pair_slot, a.hbuf, a.topk_w, a.y, a.out, a.subset_rec); \
+                       a.H, a.F, a.k, a.topk_idx, a.pair_slot, a.hbuf, a.topk_w, a.y, a.out, a.subset_rec, \
+                       a.warm, a.warm_bytes);                                                         \
     break;
 #define LD(NB)                                                                                         \
   case NB:                                                                                             \
@@ -652,7 +687,9 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   const size_t lds = (size_t)a.k * a.F * 2;
   // fused down + combine: all pairs of each token (a miss record only guards it, mode 4)
   if (a.out && a.k <= 16 && lds <= 64 * 1024 && !a.pair_subset && (!a.subset_rec || a.subset_mode == 4)) {
-    dim3 grid(a.H / kFragRows, a.T);
+    // warming workgroups on the compute units the row groups leave idle
+    const int n_warm = a.warm && a.warm_bytes >= 16 ? max(0, compute_units() - a.H / kFragRows) : 0;
+    dim3 grid(a.H / kFragRows + n_warm, a.T);
     switch (S <= 1 ? 1 : S <= 2 ? 2 : 4) {  // one wave per pair: batches of <= 4 steps
       LC(1) LC(2) LC(4)
       default: return hipErrorInvalidValue;

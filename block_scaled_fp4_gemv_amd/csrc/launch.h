@@ -30,6 +30,10 @@ struct FfnArgs {
   float* ybuf;     // workspace [T*k][H] fp32 (grouped path with fused combine)
   int32_t* tiles;  // workspace: grouped-path tile list (grouped_tiles_bytes)
   int tiles_ready;  // the tile list was written with the permutation
+  // fused decode down + combine: bytes to read (and discard) on otherwise idle
+  // compute units, so that a later kernel finds them in the memory-side cache
+  const uint8_t* warm;
+  size_t warm_bytes;
 };
 size_t grouped_tiles_bytes(int T, int k, int E);
 // Tile list geometry of the grouped path for a format: rows per tile and the

@@ -321,7 +321,17 @@ int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, in
                       unsigned route_flags, const uint16_t* x, int T, const float* router,
                       int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
                       moe_stream_t stream) {
+  return moe_layer_forward_prefetch(fmt, pool, stride, H, F, E, k, route_flags, x, T, router, topk_idx, topk_w,
+                                    out, ws, ws_bytes, nullptr, 0, stream);
+}
+
+int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, int F, int E, int k,
+                               unsigned route_flags, const uint16_t* x, int T, const float* router,
+                               int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                               const void* warm, size_t warm_bytes, moe_stream_t stream) {
   g_err[0] = 0;
+  if ((warm == nullptr) != (warm_bytes == 0)) return fail(MOE_E_ARG, "warm and warm_bytes: both set or both 0");
+  if (warm && !aligned(warm, 16)) return fail(MOE_E_ARG, "warm must be 16-byte aligned");
   int st = check_shape(fmt, H, F);
   if (st) return st;
   st = check_route_dims(T, H, E, k);
@@ -356,6 +366,8 @@ int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, in
   a.hbuf = reinterpret_cast<uint16_t*>(p);
   a.ybuf = reinterpret_cast<float*>(p + align256((size_t)T * k * F * 2));
   a.tiles = reinterpret_cast<int32_t*>(p + align256((size_t)T * k * F * 2) + align256((size_t)T * k * H * 4));
+  a.warm = static_cast<const uint8_t*>(warm);
+  a.warm_bytes = warm_bytes;
   hipError_t e;
   if (T <= 4) {
     e = launch_router_logits(x, router, T, H, E, r.logits, s);

@@ -268,6 +268,23 @@ int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, in
                       int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
                       moe_stream_t stream);
 
+/* moe_layer_forward with a read-ahead hint for a stack of layers: while the
+ * decode down + combine kernel runs (T <= 4), workgroups on the compute units
+ * its row groups leave idle read the device buffer `warm` (warm_bytes, the
+ * multiple of 16 below it; contents unchanged) and discard it, so that the
+ * kernel that reads it next (typically the next layer's router, a static
+ * weight) finds it in the memory-side cache.  Parameters are fetched ahead of
+ * use as the pages' bandwidth-aware parameter placement has it (page
+ * "FreeToken：753B大模型塞进单卡的本地部署硬件账该怎么算", section
+ * "按带宽动态分配参数存储").  Results are those of moe_layer_forward bit for
+ * bit.  warm and warm_bytes are both NULL/0 (no hint) or both set; warm is
+ * 16-byte aligned device memory (MOE_E_ARG otherwise).  Larger T ignores the
+ * hint. */
+int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, int F, int E, int k,
+                               unsigned route_flags, const uint16_t* x, int T, const float* router,
+                               int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                               const void* warm, size_t warm_bytes, moe_stream_t stream);
+
 /* ------------------------------------------- cached layer (host executor) */
 
 /* One layer's VRAM expert cache, caller-owned: the router, the pinned host

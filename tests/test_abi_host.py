@@ -207,3 +207,23 @@ def test_prefill_streamed_argument_errors_before_any_hip_call():
     assert call(arr(4), need, pools=(vp * 2)(fake, fake)) == B.MOE_E_ARG
     assert call(arr(4), need, layers=-1) == B.MOE_E_ARG
     assert call(arr(4), need, layers=0) == B.MOE_OK            # nothing to do
+
+
+def test_layer_forward_prefetch_argument_errors_before_any_hip_call():
+    """The read-ahead hint is both set or both absent, and 16-byte aligned; the
+    checks run before any HIP call (fake addresses are never dereferenced)."""
+    L = B.lib()
+    fmt, H, F, E, k, T = 1, 2048, 512, 256, 8, 1
+    need = L.moe_layer_workspace(fmt, T, H, F, k, E)
+    stride = B.blob_stride(fmt, H, F)
+    fake = 0x100000
+
+    def call(warm, warm_bytes, ws_bytes=need):
+        return L.moe_layer_forward_prefetch(fmt, fake, stride, H, F, E, k, 0, fake, T, fake, fake, fake, fake,
+                                            fake, ws_bytes, warm, warm_bytes, None)
+    assert call(None, 64) == B.MOE_E_ARG           # bytes without a buffer
+    assert call(fake, 0) == B.MOE_E_ARG            # buffer without bytes
+    assert call(fake + 8, 64) == B.MOE_E_ARG       # misaligned
+    assert call(fake, 64, need - 1) == B.MOE_E_WORKSPACE
+    assert L.moe_layer_forward_prefetch(fmt, fake, stride, H, F, E, k, 0, fake, 0, fake, fake, fake, fake,
+                                        fake, need, fake, 64, None) == B.MOE_OK   # T = 0: nothing to do

@@ -620,6 +620,27 @@ def test_layer_forward(fmt, T):
     assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
 
 
+@pytest.mark.parametrize("fmt", [NV, F8])
+def test_layer_forward_prefetch_equals_layer_forward(fmt):
+    """moe_layer_forward_prefetch (the decode down kernel also reads a warm
+    buffer on its idle compute units) gives the outputs of moe_layer_forward bit
+    for bit, for one to four tokens, with a buffer larger and smaller than one
+    row of warming workgroups; larger T ignores the hint."""
+    H, E, F, k = 2048, 64, 512, 8
+    L = Layer(fmt, H, E, F, cfg=31, layer=0, w_std=0.02)
+    pool, R = L.device()
+    R2 = torch.from_numpy(sy.router(0, 31, 1, E, H)).cuda()
+    small = torch.zeros(40, dtype=torch.float32, device="cuda")
+    for T in (1, 4, 9):
+        xd = _x_dev(iid_tokens(0, 31, T, H, [L.router], k))
+        ref = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, xd, R)
+        for warm in (R2, small):
+            got = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, xd, R, warm=warm)
+            torch.cuda.synchronize()
+            for a, b in zip(got, ref):
+                assert torch.equal(a, b), (T, warm.numel())
+
+
 def test_layer_forward_renorm_and_tiny():
     fmt, H, E, F, k, T = MX, 256, 8, 512, 2, 4
     L = Layer(fmt, H, E, F, cfg=0, layer=0, w_std=0.02)
