@@ -687,8 +687,8 @@ hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
   const size_t lds = (size_t)a.k * a.F * 2;
   // fused down + combine: all pairs of each token (a miss record only guards it, mode 4)
   if (a.out && a.k <= 16 && lds <= 64 * 1024 && !a.pair_subset && (!a.subset_rec || a.subset_mode == 4)) {
-    // warming workgroups on the compute units the row groups leave idle
-    const int n_warm = a.warm && a.warm_bytes >= 16 ? max(0, compute_units() - a.H / kFragRows) : 0;
+    // warming workgroups: the compute units the row groups leave idle, at least 64
+    const int n_warm = a.warm && a.warm_bytes >= 16 ? max(64, compute_units() - a.H / kFragRows) : 0;
     dim3 grid(a.H / kFragRows + n_warm, a.T);
     switch (S <= 1 ? 1 : S <= 2 ? 2 : 4) {  // one wave per pair: batches of <= 4 steps
       LC(1) LC(2) LC(4)

@@ -269,8 +269,9 @@ int moe_layer_forward(int fmt, const void* pool, size_t stride, int H, int F, in
                       moe_stream_t stream);
 
 /* moe_layer_forward with a read-ahead hint for a stack of layers: while the
- * decode down + combine kernel runs (T <= 4), workgroups on the compute units
- * its row groups leave idle read the device buffer `warm` (warm_bytes, the
+ * decode down + combine kernel runs (T <= 4), extra workgroups (as many as
+ * its row groups leave compute units idle, at least 64) read the device
+ * buffer `warm` (warm_bytes, the
  * multiple of 16 below it; contents unchanged) and discard it, so that the
  * kernel that reads it next (typically the next layer's router, a static
  * weight) finds it in the memory-side cache.  Parameters are fetched ahead of
