@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--cache", default="cache35b", choices=["cache35b", "none"],
                    help="cache-constrained decode timed on the same layers (VRAM slot pools + pinned host pools)")
     p.add_argument("--cache-warmup", type=int, default=64)
+    p.add_argument("--no-read-ahead", action="store_true",
+                   help="plain moe_layer_forward per decode layer (no warming of the next router)")
     p.add_argument("--cache-steps", type=int, default=128)
     p.add_argument("--cache-host-sync", action="store_true",
                    help="time the host-waiting executor (moe_cached_layer_forward) instead")
@@ -422,7 +424,8 @@ def main():
     def layer(l):
         # the next layer's router (a static weight) is read ahead during this layer's down kernel
         B.moe_layer_forward(fmt, pools[l], stride, H, F, E, k, x, routers[l], topk_idx=idx[l],
-                            topk_w=w[l], out=out[l], ws=lws[l], warm=routers[(l + 1) % n_layers])
+                            topk_w=w[l], out=out[l], ws=lws[l],
+                            warm=None if args.no_read_ahead else routers[(l + 1) % n_layers])
 
     def step():
         for l in range(n_layers):
@@ -495,7 +498,8 @@ def main():
                    "layers": n_layers, "hidden": H, "experts": E, "top_k": k, "expert_width": F,
                    "format": {1: "nvfp4", 2: "mxfp4", 3: "fp8"}[fmt], "batch": 1,
                    "graph": "one HIP graph per step",
-                   "read_ahead": "each layer's down kernel warms the next layer's router (moe_layer_forward_prefetch)"},
+                   "read_ahead": None if args.no_read_ahead else
+                   "each layer's down kernel warms the next layer's router (moe_layer_forward_prefetch)"},
         "weight_stream_GBps": round(stream_gbps, 1),
         "weight_stream_frac_of_hbm": round(stream_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"kernel": "moe_layer_forward decode layer (router GEMV, gate/up+SwiGLU with "
