@@ -111,6 +111,12 @@ def test_decode_753b_shape_sampled(fmt):
     torch.cuda.synchronize()
     assert torch.equal(idx2, idx) and torch.equal(w2, w)
     assert torch.equal(out2, out)
+    # with the read-ahead of another router (the down kernel's 384 row groups
+    # fill the chip, so it takes the 64-workgroup minimum)
+    R2 = torch.from_numpy(sy.router(0, 4, 1, E, H)).cuda()
+    idx3, w3, out3 = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, xd, R, warm=R2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx3, idx) and torch.equal(w3, w) and torch.equal(out3, out)
 
 
 # ----------------------------------------------------------------- routing
