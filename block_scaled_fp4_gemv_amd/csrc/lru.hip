@@ -8,7 +8,7 @@
 //
 // One workgroup performs one step for T*k accesses, with the whole state
 // staged in LDS:
-//  * hits are judged against the state at the start of the step;
+//  * hits are classified against the state at the start of the step;
 //  * each distinct missed expert (in order of first appearance) takes a
 //    victim among slots whose expert is not requested this step: empty slots
 //    by ascending index first, then occupied slots by ascending stamp;

@@ -171,7 +171,7 @@ int moe_lru_reset(const moe_lru* lru, moe_stream_t stream);
 size_t moe_miss_record_words(int T, int k, int S);
 
 /* One LRU step for the T*k accesses topk_idx (pair order q = t*k+j).
- * Hits are judged against the state at the start of the step.  Each distinct
+ * Hits are classified against the state at the start of the step.  Each distinct
  * missed expert takes a victim slot among slots whose expert is not requested
  * in this step: empty slots by ascending index first, then occupied slots by
  * ascending stamp.  Every access, in pair order, advances the clock and stamps

@@ -8,7 +8,7 @@ batch-aware rule below is a stated reading (one pool per layer, cold start):
 
 * One pool of S slots per layer over E experts; it starts cold (all empty).
 * A step presents T*k accesses in pair order q = t*k + j.
-* Hits are judged against the state at the start of the step.
+* Hits are classified against the state at the start of the step.
 * Each distinct missed expert (in order of first appearance) takes one victim
   slot.  Victims come only from slots whose expert is not requested in this
   step: first the empty slots in ascending index, then occupied slots in
