@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode35b", choices=["decode35b", "decode753b"])
-    p.add_argument("--prefill", default="prefill35b", choices=["prefill35b", "prefill753b", "none"],
+    p.add_argument("--prefill", default="prefill35b", choices=["prefill35b", "prefill35b_16k", "prefill753b", "none"],
                    help="prefill workload timed alongside the decode headline")
     p.add_argument("--prefill-reps", type=int, default=20)
     p.add_argument("--cache", default="cache35b", choices=["cache35b", "none"],
@@ -263,7 +263,9 @@ def prefill_leg(name, fmt_override, reps, threads):
             "mfma_util_vs_bf16_peak": round(mf / MFMA_PEAK_TFLOPS["bf16"], 4),
             "mfma_util_vs_fp4_peak": round(mf / MFMA_PEAK_TFLOPS["fp4"], 4),
             "roofline_frac": round(max(hbm_frac, flops_mfma / (MFMA_PEAK_TFLOPS["bf16"] * 1e12) / t), 4),
-            "router_fp32_gflop": round(flops_router / 1e9, 2)}
+            "router_fp32_gflop": round(flops_router / 1e9, 2),
+            **({"role": f"compute-bound point: {T * k // E} rows per expert on average, "
+                        f"{flops_mfma / bytes_alg:.0f} flop per algorithmic byte"} if name == "prefill35b_16k" else {})}
 
 
 def prefill_stream_leg(fmt, hosts, pools, routers, stride, reps):

@@ -47,6 +47,10 @@ WORKLOADS = {
     # 35B-A3B-like prefill: 2048 tokens through one layer
     "prefill35b": Workload("prefill35b", 2, H=2048, E=256, k=8, F=512, layers=1, fmt=1, T=2048,
                            steps=1, w_std=0.02),
+    # the same layer at 16384 tokens (512 rows per expert, about 1800 flop per
+    # weight byte): a compute-bound point for the grouped MFMA kernels
+    "prefill35b_16k": Workload("prefill35b_16k", 5, H=2048, E=256, k=8, F=512, layers=1, fmt=1,
+                               T=16384, steps=1, w_std=0.02, weights_cfg=2),
     # cache-constrained decode: the decode35b layers (same weights), 64 of 256
     # experts per layer in VRAM, the rest in pinned host memory; own AR(1) states
     "cache35b": Workload("cache35b", 3, H=2048, E=256, k=8, F=512, layers=40, fmt=1, T=1,

@@ -704,6 +704,25 @@ def test_grouped_ragged_tiles():
     _grouped_case(NV, 512, 16, 1024, 4, 37, cfg=44)
 
 
+@pytest.mark.parametrize("fmt", [NV, F8])
+def test_layer_forward_prefill_16k_sampled(fmt):
+    """16384 tokens through one 35B-shape layer: about 512 rows per expert, so
+    four full row tiles per expert for FP4 (eight for FP8); 64 sampled tokens,
+    and every pair's expert row count checked against the routing."""
+    H, E, F, k, T = 2048, 256, 512, 8, 16384
+    L = Layer(fmt, H, E, F, cfg=2, layer=0, w_std=0.02)
+    x = iid_tokens(0, 5, T, H, [L.router], k)
+    pool, R = L.device()
+    idx, w, out = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, _x_dev(x), R)
+    torch.cuda.synchronize()
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
+    assert counts.sum() == T * k and counts.max() <= 4 * T * k // E
+    rows = np.unique(np.linspace(0, T - 1, 64).astype(int))
+    _check_route(x[rows], L.router, k, idx.cpu()[rows], w.cpu()[rows])
+    ref = moe.moe_layer(fmt, x[rows], L.router, L.experts, k)
+    assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what="out")
+
+
 def test_layer_forward_prefill_2048_sampled():
     """2048-token prefill through one 35B-shape NVFP4 layer (grouped path), 64 sampled tokens."""
     fmt, H, E, F, k, T = NV, 2048, 256, 512, 8, 2048
