@@ -704,10 +704,10 @@ def test_grouped_ragged_tiles():
     _grouped_case(NV, 512, 16, 1024, 4, 37, cfg=44)
 
 
-@pytest.mark.parametrize("fmt", [NV, F8])
+@pytest.mark.parametrize("fmt", [NV, MX, F8])
 def test_layer_forward_prefill_16k_sampled(fmt):
     """16384 tokens through one 35B-shape layer: about 512 rows per expert, so
-    four full row tiles per expert for FP4 (eight for FP8); 64 sampled tokens,
+    four full row tiles per expert for the FP4 formats (eight for FP8); 64 sampled tokens,
     and every pair's expert row count checked against the routing."""
     H, E, F, k, T = 2048, 256, 512, 8, 16384
     L = Layer(fmt, H, E, F, cfg=2, layer=0, w_std=0.02)
