@@ -17,6 +17,20 @@ batch-aware rule below is a stated reading (one pool per layer, cold start):
 * Hit rate = (accesses - distinct misses) / accesses: a repeated access to an
   expert filled earlier in the same step counts as a hit.
 
+Elastic resize ([39TOK] section "设计核心", the third mechanism: at a scheduler
+safe point the GPU expert cache is resized to the memory at hand and rebuilt,
+with no restart and no reload of the host-resident expert pool).  The pages
+give no rule for which experts survive or where they go; the stated reading:
+
+* Between steps, the pool goes from S to S' slots.  The min(S', resident)
+  experts with the latest last use are kept; the others leave the cache.
+* A kept expert whose slot is below S' keeps it.  The other kept experts take
+  the lowest free slots below S', in ascending order of their old slot.
+* Stamps and the clock are unchanged; slots added by growing start empty.
+* The blob copies this implies: every kept blob into a new pool, or, rebuilding
+  the same pool in place, only the blobs that change slot (from slots >= S'
+  into free slots < S', so no copy reads what another writes).
+
 ``StampLRU`` is the form the GPU kernel implements (four arrays).  ``ListLRU``
 is an independent move-to-MRU list simulation of the same policy; the tests
 require both to give identical slot tables at every step.
@@ -83,6 +97,38 @@ class StampLRU:
                     n_hits=n - len(misses), n_access=n)
 
 
+def _placement(kept_slots, S_new):
+    """Old slot -> new slot for the kept slots (the placement rule above)."""
+    stay = sorted(s for s in kept_slots if s < S_new)
+    movers = sorted(s for s in kept_slots if s >= S_new)
+    taken = set(stay)
+    free = [t for t in range(S_new) if t not in taken]
+    new_of = {s: s for s in stay}
+    new_of.update(zip(movers, free))
+    return new_of, movers
+
+
+def stamp_resize(lru, S_new):
+    """Resize a StampLRU to S_new slots; returns the copy plans as lists of
+    (old slot, new slot): ``all`` for a new pool, ``in_place`` for the same pool."""
+    occupied = [s for s in range(lru.S) if lru.slot_expert[s] >= 0]
+    kept = sorted(occupied, key=lambda s: -int(lru.slot_stamp[s]))[:S_new]
+    new_of, movers = _placement(kept, S_new)
+    se = np.full(S_new, -1, dtype=np.int32)
+    st = np.zeros(S_new, dtype=np.int64)
+    es = np.full(lru.E, -1, dtype=np.int32)
+    for s, t in new_of.items():
+        e = int(lru.slot_expert[s])
+        se[t], st[t], es[e] = e, lru.slot_stamp[s], t
+    plan_all = [(s, new_of[s]) for s in sorted(new_of)]
+    plan_in_place = [(s, new_of[s]) for s in movers]
+    lru.S, lru.slot_expert, lru.slot_stamp, lru.expert_slot = S_new, se, st, es
+    return dict(all=plan_all, in_place=plan_in_place)
+
+
+StampLRU.resize = stamp_resize
+
+
 class ListLRU:
     """Move-to-MRU list form of the same policy (independent formulation)."""
 
@@ -126,6 +172,27 @@ class ListLRU:
                     pair_slot=np.array([self.slot_of[e] for e in pair_experts], dtype=np.int32),
                     n_miss=len(misses), miss_expert=np.array(misses, dtype=np.int32),
                     miss_slot=np.array(victims, dtype=np.int32))
+
+
+def _list_resize(lru, S_new):
+    """The same resize on the move-to-MRU list: the last S_new entries of the
+    recency list survive, and placement follows the same stated rule."""
+    kept = lru.recency[max(0, len(lru.recency) - S_new):]
+    keep = set(kept)
+    old = {e: s for e, s in lru.slot_of.items() if e in keep}
+    order = sorted(old.items(), key=lambda es: es[1])          # by old slot
+    new = {e: s for e, s in order if s < S_new}
+    used = set(new.values())
+    holes = (t for t in range(S_new) if t not in used)
+    for e, s in order:
+        if s >= S_new:
+            new[e] = next(holes)
+    lru.recency = list(kept)
+    lru.slot_of = new
+    lru.S = S_new
+
+
+ListLRU.resize = _list_resize
 
 
 def simulate_hit_rate(steps, E: int, S: int, skip: int = 0):

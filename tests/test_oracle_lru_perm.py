@@ -89,6 +89,105 @@ def test_duplicates_within_step_and_pair_order():
     assert r["miss_expert"].tolist() == [3, 5]
 
 
+# ------------------------------------------------------------ elastic resize
+
+def _last_use(trace):
+    """Expert -> index of its last access in the flattened pair order (brute force)."""
+    last, i = {}, 0
+    for step in trace:
+        for e in np.asarray(step).ravel():
+            last[int(e)] = i
+            i += 1
+    return last
+
+
+@pytest.mark.parametrize("seed,S,S_new", [(0, 8, 5), (1, 8, 3), (2, 8, 8), (3, 8, 12), (4, 12, 1),
+                                          (5, 6, 9)])
+def test_resize_stamp_and_list_forms_agree(seed, S, S_new):
+    """Both formulations give the same slot table after a resize and at every
+    later step; the kept experts are the S_new most recently used residents,
+    found here by brute force from the raw access sequence."""
+    rng = np.random.default_rng(seed)
+    E = 24
+    a, b = lru.StampLRU(E, S), lru.ListLRU(E, S)
+    trace = [rng.integers(0, E, (2, 2)) for _ in range(40)]
+    for st in trace:
+        assert a.step(st)["status"] == lru.OK and b.step(st)["status"] == lru.OK
+    resident = [int(e) for e in a.slot_expert if e >= 0]
+    last = _last_use(trace)
+    want = set(sorted(resident, key=lambda e: -last[e])[:S_new])
+    before = a.slot_expert.copy()
+    plan = a.resize(S_new)
+    b.resize(S_new)
+    assert a.S == S_new and np.array_equal(a.slot_expert, b.slot_table())
+    assert set(int(e) for e in a.slot_expert if e >= 0) == want
+    for t, e in enumerate(a.slot_expert):          # expert_slot is the inverse table
+        if e >= 0:
+            assert a.expert_slot[e] == t
+    assert (a.expert_slot >= 0).sum() == len(want)
+    for s_old, t in plan["all"]:                   # a kept expert below S_new never moves
+        assert a.slot_expert[t] == before[s_old]
+        assert (s_old == t) == (s_old < S_new)
+    assert plan["in_place"] == [(s_old, t) for s_old, t in plan["all"] if s_old != t]
+    for st in [rng.integers(0, E, (2, 2)) for _ in range(40)]:
+        ra, rb = a.step(st), b.step(st)
+        assert ra["status"] == rb["status"]
+        if ra["status"] == lru.OK:
+            assert np.array_equal(ra["pair_slot"], rb["pair_slot"])
+        assert np.array_equal(a.slot_expert, b.slot_table())
+
+
+def test_resize_grow_keeps_every_slot_and_adds_empty_ones():
+    a = lru.StampLRU(16, 4)
+    for e in (3, 7, 1, 9, 7):
+        a.step(np.array([[e]]))
+    before, stamps, clock = a.slot_expert.copy(), a.slot_stamp.copy(), a.clock
+    plan = a.resize(7)
+    assert list(a.slot_expert) == list(before) + [-1, -1, -1]
+    assert list(a.slot_stamp) == list(stamps) + [0, 0, 0] and a.clock == clock
+    assert plan["in_place"] == [] and plan["all"] == [(s, s) for s in range(4)]
+
+
+def test_resize_shrink_fills_the_lowest_free_slots_in_old_slot_order():
+    """Slots 0..5 hold experts 10..15, last used in the order 12, 15, 10, 14, 11, 13
+    (13 most recent).  Shrinking to 3 keeps 13, 11, 14; 11 stays in slot 1; 13
+    (old slot 3) and 14 (old slot 4) take the free slots 0 and 2 in ascending
+    order of their old slot: 13 -> 0, 14 -> 2."""
+    a = lru.StampLRU(16, 6)
+    a.step(np.arange(10, 16).reshape(-1, 1))
+    for e in (12, 15, 10, 14, 11, 13):
+        a.step(np.array([[e]]))
+    plan = a.resize(3)
+    assert [int(e) for e in a.slot_expert] == [13, 11, 14]
+    assert plan["in_place"] == [(3, 0), (4, 2)]
+    assert plan["all"] == [(1, 1), (3, 0), (4, 2)]
+
+
+def test_resize_working_set_hits_follow_the_capacity():
+    """A cyclic working set of W = 6 experts: all hits while S >= W, none after
+    shrinking to S = 5 (an LRU scan of S+1 items), all hits again one cycle after
+    growing back to 6."""
+    W = 6
+    a = lru.StampLRU(32, 8)
+    cycle = [np.array([[e]]) for e in range(W)]
+
+    def run(n_cycles):
+        hits = acc = 0
+        for _ in range(n_cycles):
+            for st in cycle:
+                r = a.step(st)
+                hits, acc = hits + r["n_hits"], acc + r["n_access"]
+        return hits / acc
+
+    run(1)
+    assert run(3) == 1.0
+    a.resize(5)
+    assert run(3) == 0.0
+    a.resize(W)
+    run(1)
+    assert run(3) == 1.0
+
+
 @pytest.mark.parametrize("T,k,E", [(16, 2, 8), (1, 8, 256), (300, 8, 64), (1, 1, 1)])
 def test_permutation_properties(T, k, E):
     rng = np.random.default_rng(T)
