@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--no-read-ahead", action="store_true",
                    help="plain moe_layer_forward per decode layer (no warming of the next router)")
     p.add_argument("--cache-steps", type=int, default=128)
+    p.add_argument("--cache-elastic-steps", type=int, default=64,
+                   help="after the timed cache steps: resize every layer's slot cache (half in place, then "
+                        "1.5x into new pools) and run this many steps after each resize (0 = skip)")
     p.add_argument("--cache-host-sync", action="store_true",
                    help="time the host-waiting executor (moe_cached_layer_forward) instead")
     p.add_argument("--prefill-stream-reps", type=int, default=3,
@@ -98,7 +101,7 @@ def build_stack(wl, fmt, n_layers, threads, keep_host=False, replicate=False):
     return pools, routers, stride, hosts
 
 
-def cache_leg(name, fmt, hosts, routers, stride, warmup, steps, host_sync=False):
+def cache_leg(name, fmt, hosts, routers, stride, warmup, steps, host_sync=False, elastic_steps=0):
     """Cache-constrained decode: each layer keeps S of its E experts in a VRAM slot
     pool.  Default: moe_cached_layer_enqueue per layer on one stream (router, LRU
     lookup, every pair's experts with the misses streamed from the pinned host
@@ -117,7 +120,8 @@ def cache_leg(name, fmt, hosts, routers, stride, warmup, steps, host_sync=False)
     layers = [B.CachedLayer(routers[l], hosts[l], torch.zeros(S * stride, dtype=torch.uint8, device="cuda"),
                             E, S, 1, k, rec_on_device=not host_sync) for l in range(n_layers)]
     ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
-    xs = torch.from_numpy(sy.ar1_sequence(0, wl.cfg_id, warmup + steps, H)).cuda()
+    n_el = 0 if host_sync else 2 * elastic_steps
+    xs = torch.from_numpy(sy.ar1_sequence(0, wl.cfg_id, warmup + steps + n_el, H)).cuda()
     idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
     w = torch.empty((1, k), dtype=torch.float32, device="cuda")
     pair_slot = torch.empty(k, dtype=torch.int32, device="cuda")
@@ -173,6 +177,46 @@ def cache_leg(name, fmt, hosts, routers, stride, warmup, steps, host_sync=False)
         assert (r[:, :, 0] == 0).all(), "cache capacity error"
         tot = np.array([r[:, :, 3].sum(), r[:, :, 1].sum()], np.int64)
     acc = steps * n_layers * k
+    elastic = []
+    if n_el:
+        # elastic slot pools: halve every layer's cache in place, then grow it to
+        # 1.5x into new pools; each resize is timed with events, and the decode
+        # steps that follow it run from a newly captured graph
+        t = warmup + steps
+        for S_new, in_place in ((S // 2, True), (S + S // 2, False)):
+            wsz = B.moe_lru_resize_workspace(S_new)
+            wsr = torch.empty(n_layers * wsz, dtype=torch.uint8, device="cuda")
+            pools = [None if in_place else torch.zeros(S_new * stride, dtype=torch.uint8, device="cuda")
+                     for _ in layers]
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i, L in enumerate(layers):
+                L.resize(S_new, eb, stride, slot_pool=pools[i], ws=wsr[i * wsz:(i + 1) * wsz])
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            copied = int(wsr.view(torch.int32).reshape(n_layers, -1)[:, 0].sum().item())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                enqueue_layers()
+            torch.cuda.synchronize()
+            graph[0] = g
+            recs.clear()
+            t0 = time.perf_counter()
+            for _ in range(elastic_steps):
+                step(t)
+                t += 1
+            torch.cuda.synchronize()
+            dte = time.perf_counter() - t0
+            r = torch.stack(recs).cpu().numpy()
+            assert (r[:, :, 0] == 0).all(), "cache capacity error"
+            elastic.append({"slots": S_new, "pool": "rebuilt in place" if in_place else "new pools",
+                            "resize_ms_all_layers": round(ms, 3), "blobs_copied": copied,
+                            "copy_GBps": round(copied * eb / (ms * 1e-3) / 1e9, 1) if ms > 0 else None,
+                            "steps_after": elastic_steps, "tokens_per_s": round(elastic_steps / dte, 2),
+                            "hit_rate": round(float(r[:, :, 3].sum()) / (elastic_steps * n_layers * k), 4),
+                            "misses_per_token": round(float(r[:, :, 1].sum()) / elastic_steps, 2)})
     return {"workload": f"{name}: {n_layers} layers, hidden {H}, {E} experts, top-{k}, width {F}, "
                         f"{S} VRAM slots per layer, batch 1, pinned host pool",
             "executor": "moe_cached_layer_forward (host waits per layer)" if host_sync else
@@ -182,7 +226,8 @@ def cache_leg(name, fmt, hosts, routers, stride, warmup, steps, host_sync=False)
             "warmup_steps": warmup, "timed_steps": steps, "hit_rate": round(float(tot[0]) / acc, 4),
             "misses_per_token": round(float(tot[1]) / steps, 2),
             "h2d_GBps": round(float(tot[1]) * eb / dt / 1e9, 2), "expert_blob_bytes": eb,
-            "timing": "host wall clock over the timed steps, synchronised at both ends"}
+            "timing": "host wall clock over the timed steps, synchronised at both ends",
+            **({"elastic": elastic} if elastic else {})}
 
 
 def algorithmic_bytes(wl, fmt):
@@ -516,7 +561,7 @@ def main():
     if want_cache:
         log(f"cache leg {args.cache} ...")
         res["cache"] = cache_leg(args.cache, fmt, hosts, routers, stride, args.cache_warmup, args.cache_steps,
-                                 host_sync=args.cache_host_sync)
+                                 host_sync=args.cache_host_sync, elastic_steps=args.cache_elastic_steps)
         log(f"cache: {res['cache']['tokens_per_s']} tok/s, hit rate {res['cache']['hit_rate']}, "
             f"{res['cache']['h2d_GBps']} GB/s H2D")
         if args.prefill_stream_reps > 0:

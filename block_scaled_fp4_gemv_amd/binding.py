@@ -43,6 +43,9 @@ SIGNATURES = {
     "moe_route_workspace": (_sz, [_i32, _i32, _i32, _i32]),
     "moe_route": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_lru_reset": (_i32, [ctypes.POINTER(moe_lru), _vp]),
+    "moe_lru_resize_workspace": (_sz, [_i32]),
+    "moe_lru_resize": (_i32, [ctypes.POINTER(moe_lru), _vp, ctypes.POINTER(moe_lru), _vp, _sz, _sz, _vp, _sz,
+                              _vp]),
     "moe_miss_record_words": (_sz, [_i32, _i32, _i32]),
     "moe_cache_lookup": (_i32, [ctypes.POINTER(moe_lru), _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_cache_fill": (_i32, [_vp, _vp, _vp, _sz, _sz, _vp, _vp, _vp]),
@@ -246,6 +249,22 @@ def moe_lru_reset(state, stream=None):
     _check(lib().moe_lru_reset(ctypes.byref(s), _stream(stream)), "moe_lru_reset")
 
 
+def moe_lru_resize_workspace(S_new):
+    return int(lib().moe_lru_resize_workspace(S_new))
+
+
+def moe_lru_resize(src, src_pool, dst, dst_pool, expert_bytes, stride, ws=None, stream=None):
+    """Resize a layer's slot cache from ``src`` (LRUState) to ``dst`` (LRUState with
+    the new S; may share src's tensors) and move the kept blobs from ``src_pool``
+    into ``dst_pool`` (the same tensor rebuilds the pool in place)."""
+    import torch
+    if ws is None:
+        ws = torch.empty(moe_lru_resize_workspace(dst.S), dtype=torch.uint8, device=src.slot_expert.device)
+    a, b = src.c(), dst.c()
+    _check(lib().moe_lru_resize(ctypes.byref(a), _ptr(src_pool), ctypes.byref(b), _ptr(dst_pool), expert_bytes,
+                                stride, _ptr(ws), ws.numel(), _stream(stream)), "moe_lru_resize")
+
+
 def moe_miss_record_words(T, k, S):
     return int(lib().moe_miss_record_words(T, k, S))
 
@@ -354,18 +373,46 @@ class CachedLayer:
     def __init__(self, router, host_pool, slot_pool, E, S, T, k, rec_on_device=False):
         import torch
         self.router, self.host_pool, self.slot_pool = router, host_pool, slot_pool
+        self.T, self.k, self.rec_on_device = T, k, rec_on_device
         self.lru = LRUState(E, S, router.device)
         moe_lru_reset(self.lru)
-        n = moe_miss_record_words(T, k, S)
-        self.miss_rec = (torch.zeros(n, dtype=torch.int32, device=router.device) if rec_on_device
-                         else torch.zeros(n, dtype=torch.int32).pin_memory())
+        self._new_record()
         self.lookup_done, self.slots_free, self.fill_done = (torch.cuda.Event() for _ in range(3))
         for ev in (self.lookup_done, self.slots_free, self.fill_done):
             ev.record()  # creates the underlying HIP event
         torch.cuda.current_stream().synchronize()
-        self.c = moe_cached_layer(_ptr(router), _ptr(host_pool), _ptr(slot_pool), self.lru.c(),
+        self._bind()
+
+    def _new_record(self):
+        import torch
+        n = moe_miss_record_words(self.T, self.k, self.lru.S)
+        self.miss_rec = (torch.zeros(n, dtype=torch.int32, device=self.router.device) if self.rec_on_device
+                         else torch.zeros(n, dtype=torch.int32).pin_memory())
+
+    def _bind(self):
+        self.c = moe_cached_layer(_ptr(self.router), _ptr(self.host_pool), _ptr(self.slot_pool), self.lru.c(),
                                   _ptr(self.miss_rec), self.lookup_done.cuda_event, self.slots_free.cuda_event,
                                   self.fill_done.cuda_event)
+
+    def resize(self, S_new, expert_bytes, stride, slot_pool=None, ws=None, stream=None):
+        """Elastic resize to S_new slots (moe_lru_resize) between steps.  slot_pool=None
+        rebuilds the current pool in place (it must hold S_new blobs); else the kept
+        blobs move into the given pool, which the layer uses from then on."""
+        pool = self.slot_pool if slot_pool is None else slot_pool
+        if pool.numel() < S_new * stride:
+            raise ValueError(f"slot pool holds {pool.numel() // stride} blobs < {S_new}")
+        if slot_pool is None and S_new <= self.lru.S:   # the state shrinks inside its own tensors
+            dst = LRUState.__new__(LRUState)
+            dst.E, dst.S = self.lru.E, S_new
+            dst.slot_expert, dst.slot_stamp = self.lru.slot_expert[:S_new], self.lru.slot_stamp[:S_new]
+            dst.expert_slot, dst.clock = self.lru.expert_slot, self.lru.clock
+        else:
+            dst = LRUState(self.lru.E, S_new, self.router.device)
+        moe_lru_resize(self.lru, self.slot_pool, dst, pool, expert_bytes, stride, ws=ws, stream=stream)
+        self.lru, self.slot_pool = dst, pool
+        if moe_miss_record_words(self.T, self.k, S_new) != self.miss_rec.numel():
+            self._new_record()
+        self._bind()
 
 
 def moe_cached_layer_forward(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w, pair_slot, pair_order, out,

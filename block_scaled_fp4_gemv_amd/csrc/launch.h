@@ -97,6 +97,10 @@ hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int T, 
 // pool (pinned, device-addressable) into their victim slots.
 hipError_t launch_cache_fill(const int32_t* miss_rec, const uint8_t* host_pool, uint8_t* slot_pool,
                              size_t expert_bytes, size_t stride, hipStream_t s);
+// Rebuild a layer's slot cache for to.S slots (state and blobs; plan: 1 + 2 * to.S
+// int32 of workspace).  from_pool == to_pool rebuilds the pool in place.
+hipError_t launch_lru_resize(const moe_lru& from, const uint8_t* from_pool, const moe_lru& to, uint8_t* to_pool,
+                             size_t expert_bytes, size_t stride, int32_t* plan, hipStream_t s);
 hipError_t launch_lru_lookup(const moe_lru& l, const int32_t* topk_idx, int n_pairs,
                              int32_t* pair_slot, int32_t* pair_order, int32_t* miss_rec, int n_max,
                              hipStream_t s);

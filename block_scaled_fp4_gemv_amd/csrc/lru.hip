@@ -508,3 +508,111 @@ hipError_t launch_cache_fill(const int32_t* miss_rec, const uint8_t* host_pool, 
                      stride);
   return hipGetLastError();
 }
+
+// ------------------------------------------------------------- elastic resize
+// One layer's slot cache rebuilt for a new slot count (the elastic GPU expert
+// cache of page "8GB 笔记本 39.3 tok/s、单卡跑 753B：FreeToken 把 frontier MoE
+// 拉回本地", section "设计核心": resized at a scheduler safe point without
+// reloading the host-resident expert pool).  Kept: the S1 latest-stamped
+// residents (occupied slots carry distinct clock values, so ranking by stamp is
+// exact).  A kept expert below S1 keeps its slot; the others take the lowest
+// free slots below S1 in ascending order of their old slot.  Stamps and the
+// clock carry over; added slots start empty.
+namespace {
+constexpr int kResizeThreads = 1024;
+
+// Exclusive count of `flag` over the threads before this one, and the total.
+__device__ int block_count_excl(bool flag, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t b = __ballot(flag);
+  __syncthreads();  // the previous call's readers of wsum are done
+  if (lane == 0) wsum[wave] = __popcll(b);
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int w = 0; w < kResizeThreads / 64; ++w) {
+    if (w < wave) before += wsum[w];
+    tot += wsum[w];
+  }
+  *total = tot;
+  return before + __popcll(b & ((1ull << lane) - 1ull));
+}
+
+// One workgroup; thread i stands for old slot i and new slot i.  Every old
+// value is read before any new value is written, so the new state may occupy
+// the old state's memory.  plan: [0] copy count, then (old slot, new slot)
+// pairs in ascending old slot: every kept slot, or with in_place only those
+// whose slot changes.
+__global__ __launch_bounds__(kResizeThreads) void k_lru_resize_plan(
+    int E, int S0, const int32_t* se0, const int64_t* st0, const int64_t* clk0, int S1, int32_t* se1,
+    int32_t* es1, int64_t* st1, int64_t* clk1, int in_place, int32_t* __restrict__ plan) {
+  __shared__ int32_t o_e[kResizeThreads], n_e[kResizeThreads], n_es[kResizeThreads], free_slot[kResizeThreads];
+  __shared__ int64_t o_st[kResizeThreads], n_st[kResizeThreads];
+  __shared__ int wsum[kResizeThreads / 64];
+  __shared__ int64_t s_clock;
+  const int i = threadIdx.x;
+  const int32_t e_i = i < S0 ? se0[i] : -1;
+  const int64_t st_i = i < S0 ? st0[i] : 0;
+  if (i == 0) s_clock = *clk0;
+  o_e[i] = e_i;
+  o_st[i] = st_i;
+  __syncthreads();
+  int rank = 0;  // occupied slots used later than this one
+  if (e_i >= 0)
+    for (int j = 0; j < S0; ++j) rank += (o_e[j] >= 0 && o_st[j] > st_i) ? 1 : 0;
+  const bool kept = e_i >= 0 && rank < S1;
+  const bool stay = kept && i < S1, mover = kept && i >= S1;
+  const bool is_free = i < S1 && !stay;  // new slot i, not held by a staying expert
+  int n_free, n_mov, n_copy;
+  const int fi = block_count_excl(is_free, wsum, &n_free);
+  if (is_free) free_slot[fi] = i;
+  const int mi = block_count_excl(mover, wsum, &n_mov);
+  n_e[i] = -1;
+  n_st[i] = 0;
+  n_es[i] = -1;
+  __syncthreads();
+  const int dst = stay ? i : mover ? free_slot[mi] : -1;
+  if (dst >= 0) {
+    n_e[dst] = e_i;
+    n_st[dst] = st_i;
+    n_es[e_i] = dst;
+  }
+  const bool copy = in_place ? mover : kept;
+  const int ci = block_count_excl(copy, wsum, &n_copy);  // its barriers also publish n_e / n_st / n_es
+  if (copy) {
+    plan[1 + 2 * ci] = i;
+    plan[2 + 2 * ci] = dst;
+  }
+  if (i == 0) plan[0] = n_copy;
+  if (i < S1) {
+    se1[i] = n_e[i];
+    st1[i] = n_st[i];
+  }
+  if (i < E) es1[i] = n_es[i];
+  if (i == 0) *clk1 = s_clock;
+}
+
+// Blob copies of a plan: blockIdx.y picks the copy, the x blocks split the blob.
+__global__ __launch_bounds__(256) void k_lru_resize_copy(const int32_t* __restrict__ plan,
+                                                         const uint8_t* from, uint8_t* to,
+                                                         size_t expert_bytes, size_t stride) {
+  const int m = blockIdx.y;
+  if (m >= plan[0]) return;
+  const uint4* src = reinterpret_cast<const uint4*>(from + (size_t)plan[1 + 2 * m] * stride);
+  uint4* dst = reinterpret_cast<uint4*>(to + (size_t)plan[2 + 2 * m] * stride);
+  const size_t chunks = expert_bytes / 16, step = (size_t)gridDim.x * blockDim.x;
+  for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += step) dst[c] = src[c];
+}
+}  // namespace
+
+hipError_t launch_lru_resize(const moe_lru& from, const uint8_t* from_pool, const moe_lru& to, uint8_t* to_pool,
+                             size_t expert_bytes, size_t stride, int32_t* plan, hipStream_t s) {
+  const int in_place = from_pool == to_pool ? 1 : 0;
+  hipLaunchKernelGGL(k_lru_resize_plan, dim3(1), dim3(kResizeThreads), 0, s, from.E, from.S, from.slot_expert,
+                     from.slot_stamp, from.clock, to.S, to.slot_expert, to.expert_slot, to.slot_stamp, to.clock,
+                     in_place, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_lru_resize_copy, dim3(16, to.S), dim3(256), 0, s, plan, from_pool, to_pool, expert_bytes,
+                     stride);
+  return hipGetLastError();
+}

@@ -194,6 +194,38 @@ int moe_lru_reset(const moe_lru* lru, moe_stream_t stream) {
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_lru_reset");
 }
 
+size_t moe_lru_resize_workspace(int S_new) {
+  if (S_new < 1 || S_new > 1024) return 0;
+  return align256((size_t)(1 + 2 * S_new) * 4);
+}
+
+int moe_lru_resize(const moe_lru* from, const void* from_pool, const moe_lru* to, void* to_pool,
+                   size_t expert_bytes, size_t stride, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  g_err[0] = 0;
+  for (const moe_lru* l : {from, to}) {
+    if (!l || !l->slot_expert || !l->expert_slot || !l->slot_stamp || !l->clock)
+      return fail(MOE_E_ARG, "NULL lru state");
+    if (l->E < 1 || l->E > 1024 || l->S < 1 || l->S > 1024)
+      return fail(MOE_E_ARG, "E=%d S=%d outside [1, 1024]", l->E, l->S);
+  }
+  if (from->E != to->E) return fail(MOE_E_ARG, "E %d -> %d: the expert count cannot change", from->E, to->E);
+  if (!from_pool || !to_pool) return fail(MOE_E_ARG, "NULL pool");
+  if (!expert_bytes || expert_bytes % 256 || stride < expert_bytes || stride % 256)
+    return fail(MOE_E_ARG, "bad expert_bytes %zu / stride %zu", expert_bytes, stride);
+  if (!aligned(from_pool, 16) || !aligned(to_pool, 16)) return fail(MOE_E_ARG, "pools must be 16-byte aligned");
+  if (from_pool != to_pool) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(from_pool), a1 = a0 + (uintptr_t)from->S * stride;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(to_pool), b1 = b0 + (uintptr_t)to->S * stride;
+    if (a0 < b1 && b0 < a1) return fail(MOE_E_ARG, "pools overlap without being the same pool");
+  }
+  const size_t need = moe_lru_resize_workspace(to->S);
+  if (!ws || ws_bytes < need) return fail(MOE_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  if (!aligned(ws, 4)) return fail(MOE_E_ARG, "workspace must be 4-byte aligned");
+  hipError_t e = launch_lru_resize(*from, static_cast<const uint8_t*>(from_pool), *to, static_cast<uint8_t*>(to_pool),
+                                   expert_bytes, stride, static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_lru_resize");
+}
+
 size_t moe_miss_record_words(int T, int k, int S) {
   if (T < 0 || k < 1 || S < 1) return 0;
   const long long n = (long long)T * k;

@@ -162,6 +162,35 @@ typedef struct moe_lru {
 /* Set the state to a cold cache (all slots empty, clock 0).  Stream-ordered. */
 int moe_lru_reset(const moe_lru* lru, moe_stream_t stream);
 
+/* Elastic slot cache: resize one layer's cache to another slot count and
+ * rebuild it, keeping the host pool as it is (page "8GB 笔记本 39.3 tok/s、单卡跑
+ * 753B：FreeToken 把 frontier MoE 拉回本地", section "设计核心", the third
+ * mechanism: at a scheduler safe point the GPU expert cache is resized to the
+ * memory at hand and rebuilt, with no restart and no reload of the
+ * host-resident expert pool).  The pages fix no rule for what survives; this
+ * call keeps the min(to->S, resident) experts with the latest stamps; a kept
+ * expert whose slot is below to->S keeps it, the others take the lowest free
+ * slots below to->S in ascending order of their old slot.  Stamps and the
+ * clock carry over; slots added by growing start empty.
+ *   from, from_pool  the current state and its pool (from->S blobs at `stride`)
+ *   to, to_pool      the state and pool after the call (to->S slots, to->E ==
+ *                    from->E).  to's arrays may be from's own memory (every old
+ *                    value is read before any is written).  to_pool is either
+ *                    from_pool itself (rebuilt in place: only the blobs that
+ *                    change slot are copied, from slots >= to->S into free
+ *                    slots below it; the allocation must hold to->S blobs) or
+ *                    memory that does not overlap from_pool (every kept blob is
+ *                    copied).
+ *   ws               moe_lru_resize_workspace(to->S) bytes (the copy plan)
+ * Call it between steps: no lookup, fill or FFN of this layer may be in flight
+ * on another stream.  Two kernels on `stream`; nothing is allocated.  Errors:
+ * MOE_E_ARG (NULL state or pool, E or S outside [1, 1024], E changed,
+ * expert_bytes or stride not a multiple of 256, stride < expert_bytes, pools
+ * not 16-byte aligned or partly overlapping), MOE_E_WORKSPACE, MOE_E_HIP. */
+size_t moe_lru_resize_workspace(int S_new);
+int moe_lru_resize(const moe_lru* from, const void* from_pool, const moe_lru* to, void* to_pool,
+                   size_t expert_bytes, size_t stride, void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* int32 words of a miss record for T*k accesses to a pool of S slots:
  *   [0] status (MOE_OK or MOE_E_CAPACITY)   [1] n_miss (distinct missed experts)
  *   [2] n_hit_pairs (pairs whose expert was resident at the start of the step)

@@ -227,3 +227,29 @@ def test_layer_forward_prefetch_argument_errors_before_any_hip_call():
     assert call(fake, 64, need - 1) == B.MOE_E_WORKSPACE
     assert L.moe_layer_forward_prefetch(fmt, fake, stride, H, F, E, k, 0, fake, 0, fake, fake, fake, fake,
                                         fake, need, fake, 64, None) == B.MOE_OK   # T = 0: nothing to do
+
+
+def test_lru_resize_argument_errors_before_any_hip_call():
+    """moe_lru_resize checks states, pools, sizes and the workspace on the host
+    (fake addresses are never dereferenced: every case fails before a launch)."""
+    L = B.lib()
+    fake, eb, stride = 0x10000000, 1769728, 1769728
+    st = lambda E, S, p=fake: B.moe_lru(E, S, p, p, p, p)  # noqa: E731
+    need = L.moe_lru_resize_workspace(32)
+    assert need >= (1 + 2 * 32) * 4 and need % 256 == 0
+    assert L.moe_lru_resize_workspace(0) == 0 and L.moe_lru_resize_workspace(1025) == 0
+
+    def call(a, pa, b, pb, e=eb, s=stride, ws=fake, wsb=need):
+        return L.moe_lru_resize(ctypes.byref(a), pa, ctypes.byref(b), pb, e, s, ws, wsb, None)
+    other = fake + 64 * stride                                     # a second, disjoint pool
+    assert call(st(256, 64, None), fake, st(256, 32), other) == B.MOE_E_ARG    # NULL state arrays
+    assert call(st(256, 64), fake, st(256, 0), other) == B.MOE_E_ARG           # S < 1
+    assert call(st(256, 64), fake, st(256, 1025), other) == B.MOE_E_ARG        # S > 1024
+    assert call(st(256, 64), fake, st(128, 32), other) == B.MOE_E_ARG          # E changed
+    assert call(st(256, 64), None, st(256, 32), other) == B.MOE_E_ARG          # NULL pool
+    assert call(st(256, 64), fake, st(256, 32), other, e=eb + 16) == B.MOE_E_ARG   # not a multiple of 256
+    assert call(st(256, 64), fake, st(256, 32), other, s=eb - 256) == B.MOE_E_ARG  # stride < expert_bytes
+    assert call(st(256, 64), fake + 8, st(256, 32), other) == B.MOE_E_ARG      # misaligned pool
+    assert call(st(256, 64), fake, st(256, 32), fake + stride) == B.MOE_E_ARG  # partly overlapping pools
+    assert call(st(256, 64), fake, st(256, 32), other, wsb=need - 1) == B.MOE_E_WORKSPACE
+    assert call(st(256, 64), fake, st(256, 32), other, ws=None) == B.MOE_E_WORKSPACE

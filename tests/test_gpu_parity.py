@@ -277,6 +277,73 @@ def test_lru_lookup_matches_oracle_top8_trace(E, S, T):
     _lookup_vs_oracle(E, S, trace)
 
 
+def _blob(e, nbytes):
+    """Recognisable bytes standing for expert e's blob."""
+    return ((np.arange(nbytes) * 7 + e * 131 + 1) % 251).astype(np.uint8)
+
+
+def _lru_steps(st, ref, steps, T, k):
+    """Run lookups on the device state and the oracle side by side, checking each."""
+    S = st.S
+    rec = torch.zeros(B.moe_miss_record_words(T, k, S), dtype=torch.int32).pin_memory()
+    pair_slot = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pair_order = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    for step in steps:
+        B.moe_cache_lookup(st, torch.from_numpy(step.astype(np.int32)).cuda(), pair_slot, pair_order, rec)
+        torch.cuda.synchronize()
+        r = ref.step(step)
+        assert rec.numpy()[0] == r["status"]
+        if r["status"] == 0:
+            assert np.array_equal(pair_slot.cpu().numpy(), r["pair_slot"])
+        assert np.array_equal(st.slot_expert.cpu().numpy(), ref.slot_expert)
+        assert np.array_equal(st.expert_slot.cpu().numpy(), ref.expert_slot)
+        assert np.array_equal(st.slot_stamp.cpu().numpy(), ref.slot_stamp)
+        assert int(st.clock.item()) == ref.clock
+
+
+@pytest.mark.parametrize("E,S0,S1,T,k", [(32, 8, 3, 1, 2), (32, 8, 5, 2, 2), (32, 8, 8, 2, 2), (32, 8, 12, 2, 2),
+                                         (32, 12, 1, 1, 1), (256, 64, 32, 1, 8), (256, 64, 96, 1, 8),
+                                         (1024, 1024, 512, 8, 8)])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_lru_resize_matches_oracle(E, S0, S1, T, k, in_place):
+    """Elastic resize after a routed trace: the state equals the oracle's bit for
+    bit, every slot holds its expert's blob, and later lookups agree.  In place:
+    the same pool tensor (and, when shrinking, the same state tensors)."""
+    from oracle import lru
+    rng = np.random.default_rng(E + S0 + S1)
+    trace = lambda n: [np.stack([rng.choice(E, k, replace=False) for _ in range(T)]) for _ in range(n)]  # noqa
+    st, ref = B.LRUState(E, S0), lru.StampLRU(E, S0)
+    B.moe_lru_reset(st)
+    _lru_steps(st, ref, trace(40 if E < 1024 else 60), T, k)
+    nb = 512
+    n_pool = max(S0, S1) if in_place else S0
+    pool_np = np.zeros((n_pool, nb), np.uint8)
+    for s_, e_ in enumerate(ref.slot_expert):
+        if e_ >= 0:
+            pool_np[s_] = _blob(int(e_), nb)
+    pool = torch.from_numpy(pool_np.ravel().copy()).cuda()
+    if in_place and S1 <= S0:
+        dst = B.LRUState.__new__(B.LRUState)
+        dst.E, dst.S = E, S1
+        dst.slot_expert, dst.slot_stamp = st.slot_expert[:S1], st.slot_stamp[:S1]
+        dst.expert_slot, dst.clock = st.expert_slot, st.clock
+    else:
+        dst = B.LRUState(E, S1)
+    dst_pool = pool if in_place else torch.zeros(S1 * nb, dtype=torch.uint8, device="cuda")
+    B.moe_lru_resize(st, pool, dst, dst_pool, nb, nb)
+    torch.cuda.synchronize()
+    ref.resize(S1)
+    assert np.array_equal(dst.slot_expert.cpu().numpy(), ref.slot_expert)
+    assert np.array_equal(dst.expert_slot.cpu().numpy(), ref.expert_slot)
+    assert np.array_equal(dst.slot_stamp.cpu().numpy(), ref.slot_stamp)
+    assert int(dst.clock.item()) == ref.clock
+    got = dst_pool.cpu().numpy().reshape(-1, nb)
+    for t, e_ in enumerate(ref.slot_expert):
+        if e_ >= 0:
+            assert np.array_equal(got[t], _blob(int(e_), nb)), (t, e_)
+    _lru_steps(dst, ref, trace(30), T, k)
+
+
 def test_lru_lookup_duplicates_and_capacity():
     rng = np.random.default_rng(1)
     E, S = 32, 6
@@ -496,6 +563,54 @@ def test_cached_layer_enqueue(fmt, T):
     _check_route(xs[:T], L.router, k, idxs[0], ws_[0])
     ref = moe.moe_layer(fmt, xs[:T], L.router, L.experts, k)
     assert_rows_close(bf16_dev_to_f64(outs[0]), fm.bf16_to_f64(ref["out"]), what="out")
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+def test_cached_layer_resized_between_steps(in_place):
+    """A cached layer resized between steps (6 -> 3 slots in place, or 6 -> 9
+    into a new pool, then back to 5): every step's output still equals the
+    all-resident layer bit for bit, the miss records follow the oracle LRU with
+    the same resizes, and the occupied slots hold their experts' host blobs."""
+    from oracle import lru as olru
+    fmt, H, E, F, k, S, T = NV, 256, 16, 512, 2, 6, 1
+    L = Layer(fmt, H, E, F, cfg=23, layer=0, w_std=0.02)
+    n = 30
+    xs = ar1_states(0, 23, n, H, [L.router], k)
+    pool_res, R = L.device()
+    hp = L.host_pool()
+    host = torch.empty(E * L.stride, dtype=torch.uint8).pin_memory()
+    host.numpy()[:] = hp
+    slots = torch.zeros(S * L.stride, dtype=torch.uint8, device="cuda")
+    cl = B.CachedLayer(R, host, slots, E, S, T, k, rec_on_device=True)
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, T, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    ref_lru = olru.StampLRU(E, S)
+    eb = B.moe_expert_bytes(fmt, H, F)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.uint16, device="cuda")
+    pair_slot = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pair_order = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    plan = {10: 3 if in_place else 9, 20: 5}
+    for t in range(n):
+        if t in plan:
+            S_new = plan[t]
+            pool = None if in_place else torch.zeros(S_new * L.stride, dtype=torch.uint8, device="cuda")
+            cl.resize(S_new, eb, L.stride, slot_pool=pool)
+            ref_lru.resize(S_new)
+        B.moe_cached_layer_enqueue(fmt, L.stride, H, F, E, k, cl, _x_dev(xs[t:t + 1]), idx, w, pair_slot,
+                                   pair_order, out, ws)
+        torch.cuda.synchronize()
+        idx_r, w_r, out_res = B.moe_layer_forward(fmt, pool_res, L.stride, H, F, E, k, _x_dev(xs[t:t + 1]), R)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx_r) and torch.equal(out, out_res), f"step {t}"
+        r = ref_lru.step(idx.cpu().numpy().ravel())
+        rec = cl.miss_rec.cpu().numpy()
+        assert rec[0] == 0 and (rec[3], rec[1]) == (r["n_hits"], r["n_miss"]), f"step {t}"
+        assert np.array_equal(cl.lru.slot_expert.cpu().numpy(), ref_lru.slot_expert), f"step {t}"
+        for s_, e_ in enumerate(ref_lru.slot_expert):
+            if e_ >= 0:
+                got = cl.slot_pool[s_ * L.stride:s_ * L.stride + eb].cpu().numpy()
+                assert np.array_equal(got, hp[e_ * L.stride:e_ * L.stride + eb]), f"step {t} slot {s_}"
 
 
 def test_cached_layer_enqueue_capacity():
