@@ -514,8 +514,8 @@ hipError_t launch_cache_fill(const int32_t* miss_rec, const uint8_t* host_pool, 
 // cache of page "8GB 笔记本 39.3 tok/s、单卡跑 753B：FreeToken 把 frontier MoE
 // 拉回本地", section "设计核心": resized at a scheduler safe point without
 // reloading the host-resident expert pool).  Kept: the S1 latest-stamped
-// residents (occupied slots carry distinct clock values, so ranking by stamp is
-// exact).  A kept expert below S1 keeps its slot; the others take the lowest
+// residents (occupied slots carry distinct clock values; equal stamps, which
+// only a hand-written state can hold, go to the lower slot first).  A kept expert below S1 keeps its slot; the others take the lowest
 // free slots below S1 in ascending order of their old slot.  Stamps and the
 // clock carry over; added slots start empty.
 namespace {
@@ -556,9 +556,12 @@ __global__ __launch_bounds__(kResizeThreads) void k_lru_resize_plan(
   o_e[i] = e_i;
   o_st[i] = st_i;
   __syncthreads();
-  int rank = 0;  // occupied slots used later than this one
+  // rank: occupied slots used later than this one; equal stamps (never produced
+  // by the lookup, possible in a state written by hand) rank the lower slot
+  // first, so at most S1 experts are kept whatever the state holds
+  int rank = 0;
   if (e_i >= 0)
-    for (int j = 0; j < S0; ++j) rank += (o_e[j] >= 0 && o_st[j] > st_i) ? 1 : 0;
+    for (int j = 0; j < S0; ++j) rank += (o_e[j] >= 0 && (o_st[j] > st_i || (o_st[j] == st_i && j < i))) ? 1 : 0;
   const bool kept = e_i >= 0 && rank < S1;
   const bool stay = kept && i < S1, mover = kept && i >= S1;
   const bool is_free = i < S1 && !stay;  // new slot i, not held by a staying expert

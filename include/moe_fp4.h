@@ -168,7 +168,8 @@ int moe_lru_reset(const moe_lru* lru, moe_stream_t stream);
  * mechanism: at a scheduler safe point the GPU expert cache is resized to the
  * memory at hand and rebuilt, with no restart and no reload of the
  * host-resident expert pool).  The pages fix no rule for what survives; this
- * call keeps the min(to->S, resident) experts with the latest stamps; a kept
+ * call keeps the min(to->S, resident) experts with the latest stamps (equal
+ * stamps, which lookups never produce, keep the lower slot first); a kept
  * expert whose slot is below to->S keeps it, the others take the lowest free
  * slots below to->S in ascending order of their old slot.  Stamps and the
  * clock carry over; slots added by growing start empty.

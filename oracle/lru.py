@@ -112,7 +112,8 @@ def stamp_resize(lru, S_new):
     """Resize a StampLRU to S_new slots; returns the copy plans as lists of
     (old slot, new slot): ``all`` for a new pool, ``in_place`` for the same pool."""
     occupied = [s for s in range(lru.S) if lru.slot_expert[s] >= 0]
-    kept = sorted(occupied, key=lambda s: -int(lru.slot_stamp[s]))[:S_new]
+    # latest stamp first; equal stamps (not produced by step) take the lower slot first
+    kept = sorted(occupied, key=lambda s: (-int(lru.slot_stamp[s]), s))[:S_new]
     new_of, movers = _placement(kept, S_new)
     se = np.full(S_new, -1, dtype=np.int32)
     st = np.zeros(S_new, dtype=np.int64)

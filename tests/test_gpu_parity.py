@@ -344,6 +344,46 @@ def test_lru_resize_matches_oracle(E, S0, S1, T, k, in_place):
     _lru_steps(dst, ref, trace(30), T, k)
 
 
+@pytest.mark.parametrize("S0,S1", [(12, 5), (12, 12), (7, 10)])
+def test_lru_resize_tied_stamps_keep_the_lower_slot(S0, S1):
+    """A state written by hand with equal stamps (lookups never produce them):
+    the resize keeps at most S1 experts, ties going to the lower slot, exactly
+    as the oracle does; the pool moves with it."""
+    from oracle import lru
+    E, nb = 32, 256
+    rng = np.random.default_rng(S0 * 100 + S1)
+    se = np.where(rng.random(S0) < 0.8, rng.permutation(E)[:S0], -1).astype(np.int32)
+    stamps = np.where(se >= 0, rng.integers(1, 4, S0), 0).astype(np.int64)
+    es = np.full(E, -1, np.int32)
+    for s_, e_ in enumerate(se):
+        if e_ >= 0:
+            es[e_] = s_
+    ref = lru.StampLRU(E, S0)
+    ref.slot_expert, ref.slot_stamp, ref.expert_slot, ref.clock = se.copy(), stamps.copy(), es.copy(), 9
+    st = B.LRUState(E, S0)
+    st.slot_expert.copy_(torch.from_numpy(se))
+    st.slot_stamp.copy_(torch.from_numpy(stamps))
+    st.expert_slot.copy_(torch.from_numpy(es))
+    st.clock.fill_(9)
+    pool_np = np.zeros((S0, nb), np.uint8)
+    for s_, e_ in enumerate(se):
+        if e_ >= 0:
+            pool_np[s_] = _blob(int(e_), nb)
+    pool = torch.from_numpy(pool_np.ravel().copy()).cuda()
+    dst, dst_pool = B.LRUState(E, S1), torch.zeros(S1 * nb, dtype=torch.uint8, device="cuda")
+    B.moe_lru_resize(st, pool, dst, dst_pool, nb, nb)
+    torch.cuda.synchronize()
+    ref.resize(S1)
+    assert np.array_equal(dst.slot_expert.cpu().numpy(), ref.slot_expert)
+    assert np.array_equal(dst.expert_slot.cpu().numpy(), ref.expert_slot)
+    assert np.array_equal(dst.slot_stamp.cpu().numpy(), ref.slot_stamp)
+    assert int(dst.clock.item()) == 9
+    got = dst_pool.cpu().numpy().reshape(-1, nb)
+    for t, e_ in enumerate(ref.slot_expert):
+        if e_ >= 0:
+            assert np.array_equal(got[t], _blob(int(e_), nb))
+
+
 def test_lru_lookup_duplicates_and_capacity():
     rng = np.random.default_rng(1)
     E, S = 32, 6
