@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--prefill", default="prefill35b", choices=["prefill35b", "prefill35b_16k", "prefill753b", "none"],
                    help="prefill workload timed alongside the decode headline")
     p.add_argument("--prefill-reps", type=int, default=20)
+    p.add_argument("--compute-bound-reps", type=int, default=10,
+                   help="with --prefill prefill35b: also time the same layer at 16384 tokens, the compute-bound "
+                        "point (0 = skip)")
     p.add_argument("--cache", default="cache35b", choices=["cache35b", "none"],
                    help="cache-constrained decode timed on the same layers (VRAM slot pools + pinned host pools)")
     p.add_argument("--cache-warmup", type=int, default=64)
@@ -577,6 +580,13 @@ def main():
         torch.cuda.empty_cache()
         res["prefill"] = prefill_leg(args.prefill, args.fmt, args.prefill_reps, args.threads)
         log(f"prefill: {res['prefill']['layer_us']} us/layer, {res['prefill']['tokens_per_s']} tok/s")
+        if args.prefill == "prefill35b" and args.compute_bound_reps > 0:
+            log("compute-bound prefill point prefill35b_16k ...")
+            torch.cuda.empty_cache()
+            res["prefill_compute_bound"] = prefill_leg("prefill35b_16k", args.fmt, args.compute_bound_reps,
+                                                       args.threads)
+            log(f"prefill35b_16k: {res['prefill_compute_bound']['layer_us']} us/layer, bf16 MFMA "
+                f"{res['prefill_compute_bound']['mfma_util_vs_bf16_peak']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(wl, fmt, xs, args.cpu_sample_steps, n_layers)
