@@ -418,6 +418,9 @@ class CachedLayer:
 def moe_cached_layer_forward(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w, pair_slot, pair_order, out,
                              ws, flags=0, stream=None, copy_stream=None):
     """Returns (n_hits, n_miss) of the step; raises MoeError on MOE_E_CAPACITY."""
+    if layer.rec_on_device:
+        raise MoeError(MOE_E_ARG, "moe_cached_layer_forward reads the miss record on the host: "
+                                  "the layer needs a pinned record (rec_on_device=False)")
     T = x.shape[0]
     hits, miss = ctypes.c_int32(0), ctypes.c_int32(0)
     st = lib().moe_cached_layer_forward(fmt, stride, H, F, E, k, flags, ctypes.byref(layer.c), _ptr(x), T,

@@ -510,6 +510,14 @@ int moe_cached_layer_forward(int fmt, size_t stride, int H, int F, int E, int k,
   g_err[0] = 0;
   if (!L || !L->router || !L->host_pool || !L->slot_pool || !L->miss_rec || !L->lookup_done)
     return fail(MOE_E_ARG, "incomplete moe_cached_layer");
+  {
+    // the record is read on the host after the lookup: it must be host memory
+    hipPointerAttribute_t at{};
+    const hipError_t pe = hipPointerGetAttributes(&at, L->miss_rec);
+    if (pe == hipSuccess && at.type == hipMemoryTypeDevice)
+      return fail(MOE_E_ARG, "miss_rec is device memory; moe_cached_layer_forward needs a [pinned] record");
+    (void)hipGetLastError();  // an unregistered host pointer reports an error here; it is host memory
+  }
   const size_t need = moe_cached_layer_workspace(fmt, T, H, F, k, E);
   if (!need) return fail(MOE_E_ARG, "bad shape or format");
   if (!ws || !aligned(ws, 256) || ws_bytes < need)

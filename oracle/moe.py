@@ -157,13 +157,6 @@ def moe_layer(fmt: int, x_bf16, router, experts, k: int, renorm: bool = False,
     return res
 
 
-def pair_output(fmt: int, x_row_bf16, canon: dict):
-    """y for one (token, expert) pair: used to check sampled outputs at full size."""
-    G, U, D = dequant_expert(fmt, canon)
-    h, y = expert_ffn(G, U, D, fm.bf16_to_f64(np.asarray(x_row_bf16)[None, :]))
-    return h[0], y[0]
-
-
 def dense_masked_layer(fmt: int, x_bf16, router, experts, E: int, k: int,
                        renorm: bool = False):
     """Pin for ``moe_layer``: evaluate EVERY expert on every token, then mix

@@ -87,7 +87,7 @@ def test_decode_35b_shape(fmt):
             assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
 
 
-@pytest.mark.parametrize("fmt", [NV, F8])
+@pytest.mark.parametrize("fmt", [NV, MX, F8])
 def test_decode_753b_shape_sampled(fmt):
     """hidden 6144, 256 experts, top-8, width 2048 (one layer, one token): the
     expert FFN against the oracle, and moe_layer_forward (whose gate/up streams
@@ -728,6 +728,33 @@ def test_cached_layer_capacity_error():
     assert int(cl.lru.clock.item()) == 0 and bool((cl.lru.slot_expert == -1).all())
 
 
+def test_cached_layer_forward_rejects_a_device_record():
+    """The host-waiting executor reads the miss record on the host: a record in
+    device memory is an argument error (from the binding and from the C ABI
+    itself), and nothing is enqueued."""
+    import ctypes
+    fmt, H, E, F, k, S = MX, 256, 8, 512, 2, 4
+    L = Layer(fmt, H, E, F, cfg=0, layer=0, w_std=0.02)
+    x = _x_dev(iid_tokens(0, 0, 1, H, [L.router], k))
+    _, R = L.device()
+    host = torch.empty(E * L.stride, dtype=torch.uint8).pin_memory()
+    host.numpy()[:] = L.host_pool()
+    slots = torch.zeros(S * L.stride, dtype=torch.uint8, device="cuda")
+    cl = B.CachedLayer(R, host, slots, E, S, 1, k, rec_on_device=True)
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    bufs = [torch.empty(s_, dtype=d, device="cuda") for s_, d in
+            (((1, k), torch.int32), ((1, k), torch.float32), (k, torch.int32), (k, torch.int32), ((1, H), torch.uint16))]
+    with pytest.raises(B.MoeError):
+        B.moe_cached_layer_forward(fmt, L.stride, H, F, E, k, cl, x, *bufs, ws)
+    p = B._ptr
+    st = B.lib().moe_cached_layer_forward(fmt, L.stride, H, F, E, k, 0, ctypes.byref(cl.c), p(x), 1, p(bufs[0]),
+                                          p(bufs[1]), p(bufs[2]), p(bufs[3]), p(bufs[4]), p(ws), ws.numel(),
+                                          None, None, None, None)
+    assert st == B.MOE_E_ARG
+    torch.cuda.synchronize()
+    assert int(cl.lru.clock.item()) == 0
+
+
 @pytest.mark.parametrize("fmt", [NV, MX])
 def test_decode_wide_experts_combine_fallback(fmt):
     """Width 8192 with top-8: the k rows of h (k*F*2 bytes) exceed the fused
@@ -878,15 +905,27 @@ def test_layer_forward_prefill_16k_sampled(fmt):
     assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what="out")
 
 
-def test_layer_forward_prefill_2048_sampled():
-    """2048-token prefill through one 35B-shape NVFP4 layer (grouped path), 64 sampled tokens."""
-    fmt, H, E, F, k, T = NV, 2048, 256, 512, 8, 2048
+@pytest.mark.parametrize("fmt", [NV, MX, F8])
+def test_layer_forward_prefill_2048_sampled(fmt):
+    """2048-token prefill through one 35B-shape layer (grouped path) in each
+    format: routing of every token, the per-pair y and the layer output of 64
+    sampled tokens against the oracle."""
+    H, E, F, k, T = 2048, 256, 512, 8, 2048
     L = Layer(fmt, H, E, F, cfg=2, layer=0, w_std=0.02)
     x = iid_tokens(0, 2, T, H, [L.router], k)
     pool, R = L.device()
-    idx, w, out = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, _x_dev(x), R)
+    xd = _x_dev(x)
+    idx, w, out = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, xd, R)
+    idx2, w2, perm, off = B.moe_route(xd, R, k)
+    y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+    B.moe_expert_ffn(fmt, pool, L.stride, H, F, E, xd, idx2, pair_perm=perm, expert_off=off, topk_w=w2, y=y,
+                     flags=B.MOE_FFN_GROUPED)
     torch.cuda.synchronize()
+    oidx, ow, _ = moe.route(x, L.router, k)
+    assert np.array_equal(idx.cpu().numpy(), oidx) and torch.equal(idx2, idx)
+    assert np.allclose(w.cpu().numpy(), ow, rtol=1e-3, atol=1e-7)
     rows = np.unique(np.linspace(0, T - 1, 64).astype(int))
-    _check_route(x[rows], L.router, k, idx.cpu()[rows], w.cpu()[rows])
     ref = moe.moe_layer(fmt, x[rows], L.router, L.experts, k)
+    yg = y.cpu().numpy().reshape(T, k, H)[rows].reshape(-1, H)
+    assert_rows_close(yg, ref["y"].reshape(-1, H), what="y")
     assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what="out")
