@@ -58,6 +58,8 @@ SIGNATURES = {
                                  _vp, _vp, _sz, _vp]),
     "moe_layer_forward_prefetch": (_i32, [_i32, _vp, _sz, _i32, _i32, _i32, _i32, _u32, _vp, _i32, _vp, _vp,
                                           _vp, _vp, _vp, _sz, _vp, _sz, _vp]),
+    "moe_layer_forward_static": (_i32, [_i32, _vp, _sz, _i32, _i32, _i32, _i32, _u32, _vp, _i32, _vp, _vp, _vp,
+                                        _vp, _vp]),
     "moe_cached_layer_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_cache_fill_device": (_i32, [_vp, _vp, _vp, _sz, _sz, _vp, _vp, _vp, _vp]),
     "moe_cached_layer_enqueue": (_i32, [_i32, _sz, _i32, _i32, _i32, _i32, _u32,

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <cstdarg>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -421,6 +422,67 @@ int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, 
   a.expert_off = off;
   e = grouped ? launch_ffn_grouped(a, s) : launch_ffn_gemv(a, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_layer_forward(ffn)");
+}
+
+// ------------------------------------------------- allocation-free layer call
+
+// The workspace of moe_layer_forward_static: one static device array, held by
+// every GPU the library runs on until the process ends.  Host code must never
+// pass `scratch` itself to a kernel or a copy (on the host the name stands for
+// a host-side symbol, not the device address); the device address comes from
+// hipGetSymbolAddress, once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on the first call
+// on each device); MOE_OK or an error status.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_E_ARG, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_layer_forward_static(int fmt, const void* pool, size_t stride, int H, int F, int E, int k,
+                             unsigned route_flags, const uint16_t* x, int T, const float* router,
+                             int32_t* topk_idx, float* topk_w, uint16_t* out, moe_stream_t stream) {
+  g_err[0] = 0;
+  int st = check_shape(fmt, H, F);
+  if (st) return st;
+  st = check_route_dims(T, H, E, k);
+  if (st) return st;
+  const size_t need = moe_layer_workspace(fmt, T, H, F, k, E);
+  if (!need) return fail(MOE_E_ARG, "bad shape or format");
+  if (need > (size_t)MOE_STATIC_SCRATCH_BYTES)
+    return fail(MOE_E_WORKSPACE, "this call needs %zu bytes of workspace, more than the %u of the static scratch array "
+                "(use moe_layer_forward with a caller workspace)", need, (unsigned)MOE_STATIC_SCRATCH_BYTES);
+  if (route_flags & ~MOE_ROUTE_RENORM) return fail(MOE_E_ARG, "unknown route flags 0x%x", route_flags);
+  const size_t eb = blob_layout(fmt, H, F).total;
+  if (stride < eb || stride % 256) return fail(MOE_E_ARG, "stride %zu < blob %zu or not 256-multiple", stride, eb);
+  if (!pool || !aligned(pool, 256)) return fail(MOE_E_ARG, "pool NULL or not 256-aligned");
+  if (T == 0) return MOE_OK;
+  if (!x || !router || !topk_idx || !topk_w || !out) return fail(MOE_E_ARG, "NULL argument");
+  if (!aligned(x, 16) || !aligned(router, 16) || !aligned(out, 16))
+    return fail(MOE_E_ARG, "x, router and out must be 16-byte aligned");
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st) return st;
+  return moe_layer_forward(fmt, pool, stride, H, F, E, k, route_flags, x, T, router, topk_idx, topk_w, out, ws,
+                           (size_t)MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 size_t moe_prefill_streamed_workspace(int fmt, int T, int H, int F, int k, int E) {

@@ -24,7 +24,9 @@
  *   - The caller owns and allocates every buffer (weights, slot pool, host
  *     pool, LRU state, outputs, workspaces), every stream and every event.
  *     The library allocates no memory and keeps no mutable global state
- *     except the per-thread error text; calls are reentrant.
+ *     except the per-thread error text and the static scratch array that
+ *     moe_layer_forward_static uses in place of a caller workspace; calls are
+ *     reentrant (that one only when serialised per GPU).
  *   - Every GPU call is stream-ordered: it validates its arguments on the
  *     host, enqueues its kernels and returns.  Errors are negative status
  *     codes; nothing aborts or throws across the ABI.  Shape/argument errors
@@ -315,6 +317,29 @@ int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, 
                                unsigned route_flags, const uint16_t* x, int T, const float* router,
                                int32_t* topk_idx, float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
                                const void* warm, size_t warm_bytes, moe_stream_t stream);
+
+/* moe_layer_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The workspace is instead a static device array of
+ * MOE_STATIC_SCRATCH_BYTES in the library, one per GPU it runs on, held until
+ * the process ends; the caller still passes the inputs and outputs.  The call
+ * allocates nothing (no hipMalloc/hipFree, no allocating library routine); the
+ * array's device address is looked up once per device, on the first call made
+ * with that device current.
+ *   Limits: a call whose moe_layer_workspace(fmt, T, H, F, k, E) exceeds
+ *   MOE_STATIC_SCRATCH_BYTES returns MOE_E_WORKSPACE and enqueues nothing
+ *   (batch-1 decode needs well under 1 MiB at every supported shape; a
+ *   2048-token prefill of the 35B-class layer needs about 155 MiB and must use
+ *   moe_layer_forward).
+ *   Sharing: every call on one GPU uses the same array, which keeps whatever
+ *   the last call left (nothing in it needs to start at zero).  Calls that
+ *   overlap on one GPU (other streams, other threads) race on it: serialise
+ *   them, e.g. on one stream.
+ * Results equal moe_layer_forward's bit for bit. */
+#define MOE_STATIC_SCRATCH_BYTES (32u << 20)
+int moe_layer_forward_static(int fmt, const void* pool, size_t stride, int H, int F, int E, int k,
+                             unsigned route_flags, const uint16_t* x, int T, const float* router,
+                             int32_t* topk_idx, float* topk_w, uint16_t* out, moe_stream_t stream);
 
 /* ------------------------------------------- cached layer (host executor) */
 

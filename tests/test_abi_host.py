@@ -253,3 +253,25 @@ def test_lru_resize_argument_errors_before_any_hip_call():
     assert call(st(256, 64), fake, st(256, 32), fake + stride) == B.MOE_E_ARG  # partly overlapping pools
     assert call(st(256, 64), fake, st(256, 32), other, wsb=need - 1) == B.MOE_E_WORKSPACE
     assert call(st(256, 64), fake, st(256, 32), other, ws=None) == B.MOE_E_WORKSPACE
+
+
+def test_layer_forward_static_checks_before_any_hip_call():
+    """The allocation-free layer call refuses bad arguments and a workspace larger
+    than its static array on the host, without touching a GPU."""
+    L = B.lib()
+    fmt, H, E, F, k = 1, 2048, 256, 512, 8
+    stride = B.blob_stride(fmt, H, F)
+    fake = 1 << 20                      # an aligned address that is never dereferenced
+    # 2048 tokens need ~155 MiB of workspace: more than the 32 MiB array
+    assert L.moe_layer_forward_static(fmt, fake, stride, H, F, E, k, 0, fake, 2048, fake, fake, fake, fake,
+                                      None) == B.MOE_E_WORKSPACE
+    assert L.moe_layer_forward_static(fmt, None, stride, H, F, E, k, 0, fake, 1, fake, fake, fake, fake,
+                                      None) == B.MOE_E_ARG
+    assert L.moe_layer_forward_static(fmt, fake, stride, H, F, E, k, 0, None, 1, fake, fake, fake, fake,
+                                      None) == B.MOE_E_ARG
+    assert L.moe_layer_forward_static(fmt, fake, stride + 16, H, F, E, k, 0, fake, 1, fake, fake, fake, fake,
+                                      None) == B.MOE_E_ARG
+    assert L.moe_layer_forward_static(9, fake, stride, H, F, E, k, 0, fake, 1, fake, fake, fake, fake,
+                                      None) == B.MOE_E_FORMAT
+    assert L.moe_layer_forward_static(fmt, fake, stride, H, F, E, k, 0, fake, 0, fake, fake, fake, fake,
+                                      None) == B.MOE_OK
