@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--prefill-stream-reps", type=int, default=3,
                    help="streamed-prefill leg passes (0 = skip; runs with the cache leg's host pools)")
     p.add_argument("--fmt", type=int, default=0, help="override weight format (1 NVFP4, 2 MXFP4, 3 FP8)")
+    p.add_argument("--mx-native", action="store_true",
+                   help="MXFP4 prefill on the native scaled MFMA (FP4 weights x two FP8 activation terms) instead "
+                        "of bf16 MFMA with the weights dequantized in registers")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (testing only)")
     p.add_argument("--replicate-layers", action="store_true",
                    help="generate layer 0's experts once and give every other layer its own device copy "
@@ -246,9 +249,11 @@ def algorithmic_bytes(wl, fmt):
 
 
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+MX_NATIVE_INSTR = ("v_mfma_scale_f32_16x16x128_f8f6f4, FP4 weights x FP8 activations (two terms per bf16 value, "
+                   "so the expert flops count twice in the instruction's own rate)")
 
 
-def prefill_leg(name, fmt_override, reps, threads):
+def prefill_leg(name, fmt_override, reps, threads, mx_native=False):
     """Time moe_layer_forward over a T-token prefill of one layer (grouped MFMA path)."""
     import numpy as np
     import torch
@@ -281,15 +286,29 @@ def prefill_leg(name, fmt_override, reps, threads):
     def run():
         l = rep[0] % 2
         rep[0] += 1
-        B.moe_layer_forward(fmt, pools[l], stride, H, F, E, k, x, Rs[l], topk_idx=idx, topk_w=w, out=out, ws=ws)
+        B.moe_layer_forward(fmt, pools[l], stride, H, F, E, k, x, Rs[l], topk_idx=idx, topk_w=w, out=out, ws=ws,
+                            flags=B.MOE_LAYER_MX_NATIVE if mx_native else 0)
 
     for _ in range(3):
         run()
     torch.cuda.synchronize()
+    # one HIP graph per weight set (the layer's kernels replayed without host
+    # launch gaps, as in the decode step)
+    graphs = []
+    for l in range(2):
+        g = torch.cuda.CUDAGraph()
+        rep[0] = l
+        with torch.cuda.graph(g):
+            run()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in evs:
+    for i, (a, b) in enumerate(evs):
         a.record()
-        run()
+        graphs[i % 2].replay()
         b.record()
     torch.cuda.synchronize()
     us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1000
@@ -299,6 +318,7 @@ def prefill_leg(name, fmt_override, reps, threads):
     flops_mfma = 2.0 * T * k * (2 * F * H + H * F)
     flops_router = 2.0 * T * E * H
     t = us * 1e-6
+    native = fmt == 2 and mx_native
     hbm_frac = bytes_alg / t / (HBM_PEAK_GBPS * 1e9)
     mf = flops_mfma / t / 1e12
     fmt_name = {1: "nvfp4", 2: "mxfp4", 3: "fp8"}[fmt]
@@ -307,11 +327,15 @@ def prefill_leg(name, fmt_override, reps, threads):
             "tokens_per_s": round(T / t, 1), "layer_us": round(us, 2), "experts_used": used,
             "algorithmic_bytes": bytes_alg, "hbm_GBps": round(bytes_alg / t / 1e9, 1),
             "hbm_frac": round(hbm_frac, 4), "expert_mfma_tflops": round(mf, 2),
-            "mfma_instruction": "v_mfma_f32_16x16x32_bf16 (weights dequantized in registers)",
+            "mfma_instruction": (MX_NATIVE_INSTR if native else
+                                 "v_mfma_f32_16x16x32_bf16 (weights dequantized in registers)"),
             "mfma_util_vs_bf16_peak": round(mf / MFMA_PEAK_TFLOPS["bf16"], 4),
+            **({"mfma_util_vs_fp8_peak": round(mf / MFMA_PEAK_TFLOPS["fp8"], 4)} if native else {}),
             "mfma_util_vs_fp4_peak": round(mf / MFMA_PEAK_TFLOPS["fp4"], 4),
             "roofline_frac": round(max(hbm_frac, flops_mfma / (MFMA_PEAK_TFLOPS["bf16"] * 1e12) / t), 4),
             "router_fp32_gflop": round(flops_router / 1e9, 2),
+            "timing": f"moe_layer_forward captured in one HIP graph per weight set (two sets, replayed "
+                      f"alternately); HIP events around each replay, median of {reps}",
             **({"role": f"compute-bound point: {T * k // E} rows per expert on average, "
                         f"{flops_mfma / bytes_alg:.0f} flop per algorithmic byte"} if name == "prefill35b_16k" else {})}
 
@@ -578,13 +602,13 @@ def main():
         log(f"prefill leg {args.prefill} ...")
         del pools
         torch.cuda.empty_cache()
-        res["prefill"] = prefill_leg(args.prefill, args.fmt, args.prefill_reps, args.threads)
+        res["prefill"] = prefill_leg(args.prefill, args.fmt, args.prefill_reps, args.threads, args.mx_native)
         log(f"prefill: {res['prefill']['layer_us']} us/layer, {res['prefill']['tokens_per_s']} tok/s")
         if args.prefill == "prefill35b" and args.compute_bound_reps > 0:
             log("compute-bound prefill point prefill35b_16k ...")
             torch.cuda.empty_cache()
             res["prefill_compute_bound"] = prefill_leg("prefill35b_16k", args.fmt, args.compute_bound_reps,
-                                                       args.threads)
+                                                       args.threads, args.mx_native)
             log(f"prefill35b_16k: {res['prefill_compute_bound']['layer_us']} us/layer, bf16 MFMA "
                 f"{res['prefill_compute_bound']['mfma_util_vs_bf16_peak']}")
     if not args.no_cpu_baseline:

@@ -19,6 +19,8 @@ MOE_OK, MOE_E_ARG, MOE_E_FORMAT, MOE_E_CAPACITY, MOE_E_WORKSPACE, MOE_E_HIP = 0,
 MOE_FMT_NVFP4, MOE_FMT_MXFP4, MOE_FMT_FP8_E4M3 = 1, 2, 3
 MOE_ROUTE_RENORM = 1
 MOE_FFN_AUTO, MOE_FFN_GEMV, MOE_FFN_GROUPED = 0, 1, 2
+MOE_FFN_MX_NATIVE = 4           # MXFP4 grouped path on the scaled MFMA (FP8 activation terms)
+MOE_LAYER_MX_NATIVE = 0x100     # the same for moe_layer_forward (in its route flags)
 
 _vp, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
 

@@ -34,6 +34,21 @@
 // step computes, with one barrier per step.
 // Gate/up writes h = bf16(silu(g) * u) in expert-sorted row order; down
 // writes y (fp32) to the rows of the original pairs.
+//
+// MXFP4 also runs natively on the gfx950 scaled MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4): the weight operand is the FP4 codes and
+// E8M0 block scales exactly as the blob stores them (lane l's 16 bytes and
+// scale byte of a fragment are the operand layout of that instruction), and
+// the bf16 activations enter as two FP8 E4M3 terms, hi = e4m3(a / 2^e) with
+// 2^e mapping the 32-element block's largest |a| into [128, 256), and lo the
+// same for the remainder a - hi * 2^e, each with its E8M0 block scale.  For a
+// bf16 value the two terms are exact unless it lies some 2^14 below its
+// block's largest (then its lowest bits fall below lo's subnormal step).  The
+// x rows are split once by a small kernel, h rows by the gate/up epilogue; a
+// 128-k step is two MFMAs per 16x16 tile and no weight is converted.  On that
+// instruction lane l of the 8-bit operand holds k 16(l/16)..+15 and
+// 64+16(l/16)..+15 of row l%16, while the 4-bit operand holds k 32(l/16)..+31,
+// and lane group b supplies the scale of k-block b for both.
 #include "common.h"
 #include "launch.h"
 
@@ -42,6 +57,13 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// Internal format tag: MXFP4 blobs run on the scaled MFMA (see above).
+constexpr int kMxNat = 4;
+template <int FMT>
+constexpr bool kNat = FMT == kMxNat;
+constexpr int kNatScaleRow = 8;  // LDS bytes of scales per activation row per step: (hi, lo) x 4 blocks
 
 constexpr int BK = kFragK;   // k per step
 // 16-column weight groups per wave: each activation operand read from LDS
@@ -165,7 +187,98 @@ struct TileArgs {
   const int32_t* pair_perm;
   uint16_t* hout;
   float* yout;
+  // native MXFP4: activation rows as FP8 terms (lo plane a_plane bytes after
+  // the hi plane) and their scales; gate/up writes h the same way
+  const uint8_t* a_q;
+  size_t a_plane;
+  const uint8_t* a_s;
+  uint8_t* hq;
+  uint8_t* hs;
+  size_t h_plane;
+  uint8_t* sbuf;  // LDS: the staged scales, [2][rows][kNatScaleRow]
 };
+
+// ------------------------------------------------ FP8 two-term split (native MXFP4)
+
+// E8M0 exponent e (clamped to [-127, 120]) with m / 2^e in [128, 256) for a
+// normal m > 0; 0 for m = 0.
+__device__ __forceinline__ int block_exp(float m) {
+  if (m == 0.0f) return 0;
+  const int e = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127 - 7;
+  return e < -127 ? -127 : (e > 120 ? 120 : e);
+}
+__device__ __forceinline__ float exp2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }  // 2^-e
+
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  return fmaxf(v, dpp_f32<kDppXor2>(v));
+}
+
+// Eight values (one quarter of a 32-element block; the block's other quarters
+// are held by the other lanes of this lane's aligned quad, all of which must
+// be active) -> their hi and lo FP8 codes and the block's scales (byte 0: hi
+// E8M0, byte 1: lo E8M0).
+__device__ __forceinline__ uint32_t split_quad8(const float (&f)[8], uint2& hi, uint2& lo) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  const int eh = block_exp(quad_max(m));
+  const float sh = exp2_neg(eh), uh = exp2_neg(-eh);
+  uint32_t ch[2];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * w] * sh, f[4 * w + 1] * sh, 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * w + 2] * sh, f[4 * w + 3] * sh, c, true);
+    ch[w] = (uint32_t)c;
+  }
+  float r[8], rm = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {  // remainders, exact in fp32
+    r[4 * w + 0] = f[4 * w + 0] - __builtin_amdgcn_cvt_f32_fp8((int)ch[w], 0) * uh;
+    r[4 * w + 1] = f[4 * w + 1] - __builtin_amdgcn_cvt_f32_fp8((int)ch[w], 1) * uh;
+    r[4 * w + 2] = f[4 * w + 2] - __builtin_amdgcn_cvt_f32_fp8((int)ch[w], 2) * uh;
+    r[4 * w + 3] = f[4 * w + 3] - __builtin_amdgcn_cvt_f32_fp8((int)ch[w], 3) * uh;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rm = fmaxf(rm, fabsf(r[i]));
+  const int el = block_exp(quad_max(rm));
+  const float sl = exp2_neg(el);
+  uint32_t cl[2];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * w] * sl, r[4 * w + 1] * sl, 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * w + 2] * sl, r[4 * w + 3] * sl, c, true);
+    cl[w] = (uint32_t)c;
+  }
+  hi = make_uint2(ch[0], ch[1]);
+  lo = make_uint2(cl[0], cl[1]);
+  return (uint32_t)(eh + 127) | ((uint32_t)(el + 127) << 8);
+}
+
+__device__ __forceinline__ void unpack_bf16x8(uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Rows of bf16 [n_rows][K] -> FP8 terms q (hi plane, then lo plane `plane`
+// bytes later, both [n_rows][K]) and scales s [n_rows][K/32][2]; one thread per
+// 8 elements (n8 = n_rows * K / 8, a multiple of 4).
+__global__ __launch_bounds__(256) void k_split_rows(const uint16_t* __restrict__ x, size_t n8, size_t plane,
+                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;  // whole quads only (n8 % 4 == 0, blocks of 256)
+  float f[8];
+  unpack_bf16x8(reinterpret_cast<const uint4*>(x)[i], f);
+  uint2 hi, lo;
+  const uint32_t sc = split_quad8(f, hi, lo);
+  reinterpret_cast<uint2*>(q)[i] = hi;
+  reinterpret_cast<uint2*>(q + plane)[i] = lo;
+  if ((i & 3) == 0) reinterpret_cast<uint16_t*>(s)[i >> 2] = (uint16_t)sc;
+}
 
 // Activation staging by the 64*NW threads: thread -> rows tid/16 + 4*NW*j
 // (j < NP), 16-byte chunk tid%16, NP passes covering the tile's 16*NS rows.
@@ -205,9 +318,58 @@ __device__ __forceinline__ void b_load(BFrag<FMT> (&dst)[NMAT][kCG<NMAT>], const
 // scale.
 template <int FMT, int NMAT, int NS>
 __device__ __forceinline__ void tile_step(floatx4_t (&acc)[NMAT][kCG<NMAT>][NS], const uint8_t* __restrict__ buf,
-                                          const BFrag<FMT> (&wf)[NMAT][kCG<NMAT>], int lane) {
+                                          const BFrag<FMT> (&wf)[NMAT][kCG<NMAT>], int lane,
+                                          const uint8_t* __restrict__ sbuf = nullptr) {
   const int am = lane & 15, aq = lane >> 4;
-  if constexpr (FMT != MOE_FMT_FP8_E4M3) {
+  if constexpr (kNat<FMT>) {
+    // per 16-row subtile: the hi and lo terms of rows 16r + lane%16 (k chunks
+    // aq and 4 + aq of each 128-byte term row), two scaled MFMAs per weight
+    // fragment; the FP4 codes and E8M0 scale go in exactly as loaded
+    i32x8_t bo[NMAT][kCG<NMAT>];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int cg = 0; cg < kCG<NMAT>; ++cg) {
+        const u32x4_t& c = wf[m][cg].c[0];
+        bo[m][cg] = i32x8_t{(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
+      }
+    // the hi terms of every subtile, then the lo terms; the operand of subtile
+    // r + 1 is read from LDS while subtile r's MFMAs run, and the reads of later
+    // subtiles are not hoisted
+    const auto read_a = [&](int r, int term, i32x8_t& av8, int& sc) {
+      const int row = kFragRows * r + am, sw = row & 15;
+      const uint8_t* rp = buf + row * ROWB;
+      const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(rp + (((8 * term + aq) ^ sw) << 4));
+      const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(rp + (((8 * term + 4 + aq) ^ sw) << 4));
+      av8 = i32x8_t{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+      // lane group aq supplies the scale of k-block aq of its row
+      sc = (int)sbuf[row * kNatScaleRow + 2 * aq + term];
+    };
+#pragma unroll
+    for (int term = 0; term < 2; ++term) {
+      i32x8_t cur, nxt;
+      int s_cur, s_nxt;
+      read_a(0, term, cur, s_cur);
+#pragma unroll
+      for (int r = 0; r < NS; ++r) {
+        if (r + 1 < NS) read_a(r + 1, term, nxt, s_nxt);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int cg = 0; cg < kCG<NMAT>; ++cg)
+            acc[m][cg][r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                cur, bo[m][cg], acc[m][cg][r], 0, 4, 0, s_cur, 0, (int)(wf[m][cg].s & 0xffu));
+        // an empty asm with a memory clobber keeps the compiler's IR passes from
+        // hoisting later reads; the scheduling barrier does so for the machine scheduler
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (r + 1 < NS) {
+          cur = nxt;
+          s_cur = s_nxt;
+        }
+      }
+    }
+  } else if constexpr (FMT != MOE_FMT_FP8_E4M3) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf16x8_t b[NMAT][kCG<NMAT>];
@@ -287,7 +449,21 @@ __device__ __forceinline__ void tile_epilogue(const TileArgs& t, const floatx4_t
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int rl = lane >> 2, c8 = 8 * (lane & 3), row = kFragRows * r + rl;
       const uint4 val = *reinterpret_cast<const uint4*>(patch + rl * kHPatchLd + c8);
-      if (row < t.rows) *reinterpret_cast<uint4*>(t.hout + (size_t)(t.row_base + row) * t.N + col0 + c8) = val;
+      if constexpr (kNat<FMT>) {
+        // the row's 32 columns are one scale block, held by this lane's quad
+        float f[8];
+        unpack_bf16x8(val, f);
+        uint2 qh, ql;
+        const uint32_t sc = split_quad8(f, qh, ql);
+        if (row < t.rows) {
+          const size_t pr = (size_t)(t.row_base + row);
+          *reinterpret_cast<uint2*>(t.hq + pr * t.N + col0 + c8) = qh;
+          *reinterpret_cast<uint2*>(t.hq + t.h_plane + pr * t.N + col0 + c8) = ql;
+          if ((lane & 3) == 0) reinterpret_cast<uint16_t*>(t.hs)[pr * (t.N / 32) + col0 / 32] = (uint16_t)sc;
+        }
+      } else {
+        if (row < t.rows) *reinterpret_cast<uint4*>(t.hout + (size_t)(t.row_base + row) * t.N + col0 + c8) = val;
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -360,15 +536,44 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
   }
 
   // activation staging rows (rows past the end repeat the last row; they land
-  // in buffer rows no subtile reads)
+  // in buffer rows no subtile reads).  A row index is a token (gate/up) or an
+  // expert-sorted pair (down).
   const int sr = tid >> 4, sc = tid & 15;
+  const auto src_row = [&](int r) -> size_t {
+    const int p = t.row_base + min(r, t.rows - 1);
+    return t.a_by_token ? (size_t)(t.pair_perm[p] / t.k_top) : (size_t)p;
+  };
   const uint16_t* arow[NP];
+  const uint8_t* qrow[NP];
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
-    const int p = t.row_base + min(sr + 4 * NW * j, t.rows - 1);
-    arow[j] = t.a_by_token ? t.a_src + (size_t)(t.pair_perm[p] / t.k_top) * t.K : t.a_src + (size_t)p * t.K;
+    const size_t ar = src_row(sr + 4 * NW * j);
+    if constexpr (kNat<FMT>)  // 16-byte chunk sc: hi chunk sc (< 8) or lo chunk sc - 8
+      qrow[j] = t.a_q + ar * t.K + (sc >= 8 ? t.a_plane : 0) + (size_t)(sc & 7) * 16;
+    else
+      arow[j] = t.a_src + ar * t.K;
   }
+  // native: the block scales of staged row tid (threads below the tile's rows)
+  const bool s_stage = kNat<FMT> && tid < kFragRows * NS;
+  const uint8_t* srow = kNat<FMT> ? t.a_s + src_row(tid) * (size_t)(t.K / 32) * 2 : nullptr;
+  uint2 sv = make_uint2(0u, 0u);
   u32x4_t av[NP];
+  const auto load_act = [&](int s) {
+    if constexpr (kNat<FMT>) {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) av[j] = *reinterpret_cast<const u32x4_t*>(qrow[j] + (size_t)s * BK);
+      if (s_stage) sv = *reinterpret_cast<const uint2*>(srow + (size_t)s * kNatScaleRow);
+    } else {
+      a_load<NP>(av, arow, s, sc);
+    }
+  };
+  const auto store_act = [&](uint8_t* buf, uint8_t* sb) {
+    a_store<NP, NW>(av, buf, sr, sc);
+    if constexpr (kNat<FMT>)
+      if (s_stage) *reinterpret_cast<uint2*>(sb + tid * kNatScaleRow) = sv;
+  };
+  uint8_t* sbuf0 = t.sbuf;
+  uint8_t* sbuf1 = kNat<FMT> ? t.sbuf + kTileRows<FMT> * kNatScaleRow : nullptr;
   BFrag<FMT> wb0[NMAT][kCG<NMAT>], wb1[NMAT][kCG<NMAT>];
   floatx4_t acc[NMAT][kCG<NMAT>][NS];
 #pragma unroll
@@ -393,7 +598,7 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
   const auto k_of = [&](int v) { return min(v, U - 1) % S; };
   uint8_t* buf0 = As;
   uint8_t* buf1 = As + RB * ROWB;
-  a_load<NP>(av, arow, 0, sc);
+  load_act(0);
   b_load<FMT, NMAT>(wb0, codes, scales, grp_of(0), S, 0, lane);
   b_load<FMT, NMAT>(wb1, codes, scales, grp_of(1), S, k_of(1), lane);
   // Down writes a column tile's results after its last k-step (an odd step:
@@ -403,16 +608,16 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
   // registers.
   int u = 0;
   for (; u + 1 < U; u += 2) {
-    a_store<NP, NW>(av, buf0, sr, sc);
-    a_load<NP>(av, arow, k_of(u + 1), sc);
+    store_act(buf0, sbuf0);
+    load_act(k_of(u + 1));
     __syncthreads();
-    tile_step<FMT, NMAT, NS>(acc, buf0, wb0, lane);
+    tile_step<FMT, NMAT, NS>(acc, buf0, wb0, lane, sbuf0);
     __builtin_amdgcn_sched_barrier(0);
     b_load<FMT, NMAT>(wb0, codes, scales, grp_of(u + 2), S, k_of(u + 2), lane);
-    a_store<NP, NW>(av, buf1, sr, sc);
-    a_load<NP>(av, arow, k_of(u + 2), sc);
+    store_act(buf1, sbuf1);
+    load_act(k_of(u + 2));
     __syncthreads();
-    tile_step<FMT, NMAT, NS>(acc, buf1, wb1, lane);
+    tile_step<FMT, NMAT, NS>(acc, buf1, wb1, lane, sbuf1);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NMAT == 1) {
       if ((u + 1) % S == S - 1) {
@@ -423,9 +628,9 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
     b_load<FMT, NMAT>(wb1, codes, scales, grp_of(u + 3), S, k_of(u + 3), lane);
   }
   if (u < U) {  // odd step count: the last step (a pass end)
-    a_store<NP, NW>(av, buf0, sr, sc);
+    store_act(buf0, sbuf0);
     __syncthreads();
-    tile_step<FMT, NMAT, NS>(acc, buf0, wb0, lane);
+    tile_step<FMT, NMAT, NS>(acc, buf0, wb0, lane, sbuf0);
     if constexpr (NMAT == 1) tile_epilogue<FMT, NMAT, NS>(t, acc, grp_of(u), tau, lane);
   }
   if constexpr (NMAT == 2) tile_epilogue<FMT, NMAT, NS>(t, acc, t.ct * (kBN<NMAT, NW> / kFragRows) + gw, tau, lane);
@@ -433,15 +638,19 @@ __device__ __forceinline__ void grouped_tile(const TileArgs& t, uint8_t* __restr
 
 // NMAT = 2: gate/up with SwiGLU into hout (expert-sorted rows, width N).
 // NMAT = 1: down into y rows of the original pairs.
+// Native MXFP4 (FMT = kMxNat): a_q / a_plane / a_s replace a_src, and gate/up
+// writes h's FP8 terms (hq, lo plane h_plane bytes on) and scales (hs) instead of hout.
 template <int FMT, int NMAT, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 4 && FMT != MOE_FMT_FP8_E4M3 ? 2 : 1) void k_grouped(
+__global__ __launch_bounds__(64 * NW, NW == 4 && FMT != MOE_FMT_FP8_E4M3 && !kNat<FMT> ? 2 : 1) void k_grouped(
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int K, int N, int k_top,
     const uint16_t* __restrict__ a_src, int a_by_token, const int32_t* __restrict__ pair_perm,
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ tile_e,
     const int32_t* __restrict__ tile_m0, const int32_t* __restrict__ n_tiles, int n_sweeps, int npass,
-    uint16_t* __restrict__ hout, float* __restrict__ yout) {
+    uint16_t* __restrict__ hout, float* __restrict__ yout, const uint8_t* __restrict__ a_q, size_t a_plane,
+    const uint8_t* __restrict__ a_s, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, size_t h_plane) {
   __shared__ __attribute__((aligned(16))) uint8_t As[2 * kTileRows<FMT> * ROWB +
-                                                   (NMAT == 1 ? NW * kPatchFloats * 4 : NW * kHPatchHalfs * 2)];
+                                                   (NMAT == 1 ? NW * kPatchFloats * 4 : NW * kHPatchHalfs * 2) +
+                                                   (kNat<FMT> ? 2 * kTileRows<FMT> * kNatScaleRow : 0)];
   __shared__ int s_rows[NMAT == 1 ? kTileRows<FMT> : 1];
   // A workgroup takes one row tile and a sweep of npass consecutive column
   // tiles.  Workgroups are handed to the 8 XCDs round-robin by index; within
@@ -470,6 +679,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 && FMT != MOE_FMT_FP8_E4M3 ? 2 : 1
   t.pair_perm = pair_perm;
   t.hout = hout;
   t.yout = yout;
+  t.a_q = a_q;
+  t.a_plane = a_plane;
+  t.a_s = a_s;
+  t.hq = hq;
+  t.hs = hs;
+  t.h_plane = h_plane;
+  t.sbuf = t.epi + (NMAT == 1 ? NW * kPatchFloats * 4 : NW * kHPatchHalfs * 2);
   const int ns = (t.rows + kFragRows - 1) / kFragRows;
   if (NMAT == 1 && ns > 6) {
     // down: the first 64 rows, then the rest, each with the tile's sweep
@@ -533,16 +749,25 @@ void launch_grouped_k(const FfnArgs& a, int max_tiles, const int32_t* tile_e, co
                       const int32_t* n_tiles, float* y, hipStream_t s) {
   const int K = NMAT == 2 ? a.H : a.F, N = NMAT == 2 ? a.F : a.H;
   const uint16_t* a_src = NMAT == 2 ? a.x : a.hbuf;
+  // native MXFP4: x's FP8 terms (gate/up) or h's (down; they replace the bf16 h rows in hbuf)
+  const size_t n_pairs = (size_t)a.T * a.k;
+  uint8_t* hq = reinterpret_cast<uint8_t*>(a.hbuf);
+  const uint8_t* a_q = NMAT == 2 ? a.xq : hq;
+  const size_t a_plane = NMAT == 2 ? (size_t)a.T * a.H : n_pairs * a.F;
+  const uint8_t* a_s = NMAT == 2 ? a.xs : a.hs;
 #define GK(NW)                                                                                                \
   {                                                                                                           \
     const int nct = N / kBN<NMAT, NW>;                                                                        \
     const int np = NMAT == 2 ? 1 : sweep_len(nct, K / BK); /* gate/up keeps its epilogue out of the loop */   \
     hipLaunchKernelGGL((k_grouped<FMT, NMAT, NW>), dim3(max_tiles * (nct / np)), dim3(64 * NW), 0, s, a.pool, \
                        a.stride, a.L, K, N, a.k, a_src, NMAT == 2 ? 1 : 0, a.pair_perm, a.expert_off, tile_e,  \
-                       tile_m0, n_tiles, nct / np, np, NMAT == 2 ? a.hbuf : nullptr, NMAT == 2 ? nullptr : y); \
+                       tile_m0, n_tiles, nct / np, np, NMAT == 2 ? a.hbuf : nullptr, NMAT == 2 ? nullptr : y,  \
+                       a_q, a_plane, a_s, hq, a.hs, n_pairs * a.F);                                           \
   }
-  // gate/up widths are multiples of 256 (8-wave tiles); down takes 4 waves for hidden 256
-  if constexpr (NMAT == 2) GK(8) else if (N % kBN<NMAT, 8> == 0) GK(8) else GK(4)
+  // gate/up widths are multiples of 256 (8-wave tiles); down takes 4 waves for hidden 256.
+  // Native MXFP4 runs 4-wave workgroups, one per compute unit: its scaled MFMAs
+  // need more registers than two waves per SIMD leave.
+  if constexpr (kNat<FMT>) GK(4) else if constexpr (NMAT == 2) GK(8) else if (N % kBN<NMAT, 8> == 0) GK(8) else GK(4)
 #undef GK
 }
 
@@ -556,8 +781,17 @@ hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
     hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E, kTileRows<FMT>, tile_e,
                        tile_m0, n_tiles);
   float* y = a.y ? a.y : a.ybuf;
-  launch_grouped_k<FMT, 2>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
-  launch_grouped_k<FMT, 1>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
+  if (FMT == MOE_FMT_MXFP4 && a.mx_native) {
+    // x rows into their FP8 terms once, then both grouped kernels on the scaled MFMA
+    const size_t n8 = (size_t)a.T * a.H / 8;
+    hipLaunchKernelGGL(k_split_rows, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a.x, n8,
+                       (size_t)a.T * a.H, a.xq, a.xs);
+    launch_grouped_k<kMxNat, 2>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
+    launch_grouped_k<kMxNat, 1>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
+  } else {
+    launch_grouped_k<FMT, 2>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
+    launch_grouped_k<FMT, 1>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.out) return e;
   return launch_combine(y, a.topk_w, a.T, a.H, a.k, a.out, s);

@@ -34,7 +34,19 @@ struct FfnArgs {
   // compute units, so that a later kernel finds them in the memory-side cache
   const uint8_t* warm;
   size_t warm_bytes;
+  // MXFP4 on the grouped path: 1 = the scaled MFMA on the FP4 codes and their
+  // E8M0 scales as stored, the bf16 activations entering as two FP8 terms with
+  // E8M0 scales per 32 elements; 0 = bf16 MFMA on weights dequantized in registers
+  int mx_native;
+  uint8_t* xq;  // workspace (native): x as FP8 terms, [2][T][H] (hi plane, then lo plane)
+  uint8_t* xs;  // workspace (native): their scales, [T][H/32][2] (hi, lo)
+  uint8_t* hs;  // workspace (native): scales of h's FP8 terms, [T*k][F/32][2]; h's codes
+                // ([2][T*k][F]) take the place of the bf16 h rows in hbuf
 };
+// Expert-FFN workspace: its size and the carving of FfnArgs' scratch pointers
+// (hbuf, ybuf, tiles and, for MXFP4, the FP8 activation terms) from it.
+size_t ffn_ws_bytes(int fmt, int T, int H, int F, int k, int E);
+void ffn_ws_carve(FfnArgs& a, uint8_t* ws);
 size_t grouped_tiles_bytes(int T, int k, int E);
 // Tile list geometry of the grouped path for a format: rows per tile and the
 // list capacity (for the permutation kernel to write it).

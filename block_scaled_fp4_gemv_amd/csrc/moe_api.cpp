@@ -56,6 +56,34 @@ int check_route_dims(int T, int H, int E, int k) {
 
 }  // namespace
 
+size_t ffn_ws_bytes(int fmt, int T, int H, int F, int k, int E) {
+  const size_t n = (size_t)T * k;
+  size_t b = align256(n * F * 2) + align256(n * H * 4) + grouped_tiles_bytes(T, k, E) + 256;
+  if (fmt == MOE_FMT_MXFP4)  // FP8 terms of x and the scales of x's and h's terms
+    b += align256((size_t)T * H * 2) + align256((size_t)T * H / 16) + align256(n * F / 16);
+  return b;
+}
+
+void ffn_ws_carve(FfnArgs& a, uint8_t* p) {
+  const size_t n = (size_t)a.T * a.k;
+  a.hbuf = reinterpret_cast<uint16_t*>(p);
+  p += align256(n * a.F * 2);
+  a.ybuf = reinterpret_cast<float*>(p);
+  p += align256(n * a.H * 4);
+  a.tiles = reinterpret_cast<int32_t*>(p);
+  p += grouped_tiles_bytes(a.T, a.k, a.E) + 256;
+  if (a.fmt == MOE_FMT_MXFP4) {
+    a.xq = p;
+    p += align256((size_t)a.T * a.H * 2);
+    a.xs = p;
+    p += align256((size_t)a.T * a.H / 16);
+    a.hs = p;
+  } else {
+    a.xq = a.xs = a.hs = nullptr;
+    a.mx_native = 0;
+  }
+}
+
 extern "C" {
 
 const char* moe_status_str(int s) {
@@ -285,8 +313,7 @@ int moe_cache_fill(const int32_t* rec, const void* host_pool, void* slot_pool, s
 
 size_t moe_ffn_workspace(int fmt, int T, int H, int F, int k, int E) {
   if (!valid_fmt(fmt) || T < 0 || k < 1 || E < 1 || !valid_dim(H) || !valid_dim(F)) return 0;
-  const size_t n = (size_t)T * k;
-  return align256(n * F * 2) + align256(n * H * 4) + grouped_tiles_bytes(T, k, E) + 256;
+  return ffn_ws_bytes(fmt, T, H, F, k, E);
 }
 
 int moe_expert_ffn(int fmt, const void* slot_pool, size_t stride, int H, int F, int E,
@@ -299,7 +326,7 @@ int moe_expert_ffn(int fmt, const void* slot_pool, size_t stride, int H, int F, 
   if (st) return st;
   if (E < 1 || E > 1024) return fail(MOE_E_ARG, "E=%d outside [1, 1024]", E);
   if (T < 0 || k < 1 || k > E || k > 16) return fail(MOE_E_ARG, "T=%d k=%d", T, k);
-  if (flags > MOE_FFN_GROUPED) return fail(MOE_E_ARG, "unknown ffn flags 0x%x", flags);
+  if ((flags & ~MOE_FFN_MX_NATIVE) > MOE_FFN_GROUPED) return fail(MOE_E_ARG, "unknown ffn flags 0x%x", flags);
   if (T == 0) return MOE_OK;
   if (!y && !out) return fail(MOE_E_ARG, "y and out are both NULL");
   if (out && !topk_w) return fail(MOE_E_ARG, "out needs topk_w");
@@ -317,11 +344,12 @@ int moe_expert_ffn(int fmt, const void* slot_pool, size_t stride, int H, int F, 
 
   bool grouped = false;
   const bool have_perm = pair_perm && expert_off;
-  if (flags == MOE_FFN_GROUPED) {
+  const unsigned path = flags & ~MOE_FFN_MX_NATIVE;
+  if (path == MOE_FFN_GROUPED) {
     if (!have_perm) return fail(MOE_E_ARG, "grouped path needs pair_perm and expert_off");
     if (pair_subset) return fail(MOE_E_ARG, "grouped path computes all pairs (pair_subset NULL)");
     grouped = true;
-  } else if (flags == MOE_FFN_AUTO) {
+  } else if (path == MOE_FFN_AUTO) {
     grouped = have_perm && !pair_subset && (long long)T * k >= 2LL * E;
   }
   if (!grouped && out && k > 16) return fail(MOE_E_ARG, "fused combine on the GEMV path needs k <= 16");
@@ -333,10 +361,8 @@ int moe_expert_ffn(int fmt, const void* slot_pool, size_t stride, int H, int F, 
   a.expert_off = expert_off; a.pair_subset = pair_subset;
   a.n_pairs = pair_subset ? n_subset : T * k;
   a.topk_w = topk_w; a.y = y; a.out = out;
-  uint8_t* p = static_cast<uint8_t*>(ws);
-  a.hbuf = reinterpret_cast<uint16_t*>(p);
-  a.ybuf = reinterpret_cast<float*>(p + align256((size_t)T * k * F * 2));
-  a.tiles = reinterpret_cast<int32_t*>(p + align256((size_t)T * k * F * 2) + align256((size_t)T * k * H * 4));
+  a.mx_native = (flags & MOE_FFN_MX_NATIVE) ? 1 : 0;
+  ffn_ws_carve(a, static_cast<uint8_t*>(ws));
   if (T == 0 || a.n_pairs == 0) return MOE_OK;
   hipError_t e = grouped ? launch_ffn_grouped(a, static_cast<hipStream_t>(stream))
                          : launch_ffn_gemv(a, static_cast<hipStream_t>(stream));
@@ -369,7 +395,8 @@ int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, 
   if (st) return st;
   st = check_route_dims(T, H, E, k);
   if (st) return st;
-  if (route_flags & ~MOE_ROUTE_RENORM) return fail(MOE_E_ARG, "unknown route flags 0x%x", route_flags);
+  if (route_flags & ~(MOE_ROUTE_RENORM | MOE_LAYER_MX_NATIVE))
+    return fail(MOE_E_ARG, "unknown route flags 0x%x", route_flags);
   if (k > 16) return fail(MOE_E_ARG, "moe_layer_forward needs k <= 16");
   const size_t eb = blob_layout(fmt, H, F).total;
   if (stride < eb || stride % 256) return fail(MOE_E_ARG, "stride %zu < blob %zu or not 256-multiple", stride, eb);
@@ -384,7 +411,7 @@ int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* p = static_cast<uint8_t*>(ws);
   RouteArgs r{};
-  r.x = x; r.router = router; r.T = T; r.H = H; r.E = E; r.k = k; r.flags = route_flags;
+  r.x = x; r.router = router; r.T = T; r.H = H; r.E = E; r.k = k; r.flags = route_flags & MOE_ROUTE_RENORM;
   r.topk_idx = topk_idx; r.topk_w = topk_w;
   route_ws_carve(r, p);
   p += align256(route_ws_bytes(T, H, E, k));
@@ -396,9 +423,8 @@ int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, 
   a.fmt = fmt; a.H = H; a.F = F; a.E = E; a.T = T; a.k = k;
   a.pool = static_cast<const uint8_t*>(pool); a.stride = stride; a.L = blob_layout(fmt, H, F);
   a.x = x; a.topk_idx = topk_idx; a.topk_w = topk_w; a.out = out; a.n_pairs = T * k;
-  a.hbuf = reinterpret_cast<uint16_t*>(p);
-  a.ybuf = reinterpret_cast<float*>(p + align256((size_t)T * k * F * 2));
-  a.tiles = reinterpret_cast<int32_t*>(p + align256((size_t)T * k * F * 2) + align256((size_t)T * k * H * 4));
+  a.mx_native = (route_flags & MOE_LAYER_MX_NATIVE) ? 1 : 0;
+  ffn_ws_carve(a, p);
   a.warm = static_cast<const uint8_t*>(warm);
   a.warm_bytes = warm_bytes;
   hipError_t e;

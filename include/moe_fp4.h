@@ -77,6 +77,16 @@ enum moe_fmt { MOE_FMT_NVFP4 = 1, MOE_FMT_MXFP4 = 2, MOE_FMT_FP8_E4M3 = 3 };
 #define MOE_FFN_AUTO 0u
 #define MOE_FFN_GEMV 1u    /* per-pair weight-streaming GEMV (batch-1 decode shape)  */
 #define MOE_FFN_GROUPED 2u /* expert-grouped MFMA GEMM (prefill shape); needs pair_perm/expert_off */
+/* OR-ed into moe_expert_ffn's flags (MOE_LAYER_MX_NATIVE into moe_layer_forward's
+ * route_flags): MXFP4 on the grouped path runs the gfx950 scaled MFMA, which
+ * takes the FP4 codes and E8M0 scales as stored and the bf16 activations as
+ * two FP8 E4M3 terms with E8M0 scales per 32 elements (hi and the remainder
+ * lo; exact for every value within 2^14 of its block's largest), instead of
+ * dequantizing the weights in registers into bf16 MFMA operands.  Outputs
+ * agree within the tolerance; without the flag the dequant path runs (it is
+ * the faster one in this build). */
+#define MOE_FFN_MX_NATIVE 4u
+#define MOE_LAYER_MX_NATIVE 0x100u
 
 /* ------------------------------------------------------------------ misc */
 

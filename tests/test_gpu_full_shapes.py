@@ -1,8 +1,9 @@
 """GPU parity at the full sizes of the workloads that are timed.
 
 * the 753B-class prefill (hidden 6144, 256 experts, top-8, width 2048, 4096
-  tokens) in all three weight formats: routing of every token bit-exact, the
-  per-pair ``y`` and the layer output of 32 sampled tokens against the oracle;
+  tokens) in all three weight formats (MXFP4 on both of its grouped paths):
+  routing of every token bit-exact, the per-pair ``y`` and the layer output of
+  32 sampled tokens against the oracle;
 * the cache-constrained decode at its real shape (hidden 2048, 256 experts,
   top-8, width 512, 64 VRAM slots per layer, NVFP4), two layers over 104
   AR(1) steps with an elastic resize to 96 slots on the way: at every step the
@@ -68,21 +69,24 @@ def test_prefill_753b_shape_sampled(fmt):
     pool, R = L.device(needed=oidx[rows])
     xd = _x_dev(x)
     print(f"prefill753b fmt {fmt}: {len(np.unique(oidx[rows]))} experts serve the sampled rows", flush=True)
-    idx, w, out = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, xd, R)
-    torch.cuda.synchronize()
-    assert np.array_equal(idx.cpu().numpy(), oidx)
-    assert np.allclose(w.cpu().numpy(), ow, rtol=1e-3, atol=1e-7)
-    idx2, w2, perm, off = B.moe_route(xd, R, k)
-    y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
-    B.moe_expert_ffn(fmt, pool, L.stride, H, F, E, xd, idx2, pair_perm=perm, expert_off=off, topk_w=w2, y=y,
-                     flags=B.MOE_FFN_GROUPED)
-    torch.cuda.synchronize()
-    assert torch.equal(idx2, idx)
-    ysel = y.view(T, k, H)[torch.from_numpy(rows).cuda()].reshape(-1, H).cpu().numpy()
-    del y
     ref = moe.moe_layer(fmt, x[rows], L.router, L.experts, k)
-    assert_rows_close(ysel, ref["y"].reshape(-1, H), what="y")
-    assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what="out")
+    # MXFP4 also on the native scaled MFMA (FP8 activation terms)
+    for native in ((False, True) if fmt == MX else (False,)):
+        idx, w, out = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, xd, R,
+                                          flags=B.MOE_LAYER_MX_NATIVE if native else 0)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), oidx)
+        assert np.allclose(w.cpu().numpy(), ow, rtol=1e-3, atol=1e-7)
+        idx2, w2, perm, off = B.moe_route(xd, R, k)
+        y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+        B.moe_expert_ffn(fmt, pool, L.stride, H, F, E, xd, idx2, pair_perm=perm, expert_off=off, topk_w=w2, y=y,
+                         flags=B.MOE_FFN_GROUPED | (B.MOE_FFN_MX_NATIVE if native else 0))
+        torch.cuda.synchronize()
+        assert torch.equal(idx2, idx)
+        ysel = y.view(T, k, H)[torch.from_numpy(rows).cuda()].reshape(-1, H).cpu().numpy()
+        del y
+        assert_rows_close(ysel, ref["y"].reshape(-1, H), what=f"y native={native}")
+        assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what=f"out native={native}")
 
 
 def _lru_state(st):

@@ -863,6 +863,38 @@ def _grouped_case(fmt, H, E, F, k, T, cfg, w_std=0.02, sample=None):
     assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what="out")
 
 
+@pytest.mark.parametrize("T", [16, 256, 2048])
+def test_mxfp4_native_and_dequant_paths(T):
+    """MXFP4 on the grouped path: the bf16 dequant path, and the scaled MFMA (FP4
+    codes and E8M0 scales as stored, activations as two FP8 terms) that
+    MOE_FFN_MX_NATIVE asks for: both meet the oracle on every sampled row, and
+    the layer call takes the same choice through its flags."""
+    fmt, H, E, F, k = MX, 2048, 256, 512, 8
+    L = Layer(fmt, H, E, F, cfg=47, layer=0, w_std=0.02)
+    x = iid_tokens(0, 47, T, H, [L.router], k)
+    pool, R = L.device()
+    xd = _x_dev(x)
+    idx, w, perm, off = B.moe_route(xd, R, k)
+    rows = np.unique(np.linspace(0, T - 1, min(T, 48)).astype(int))
+    ref = moe.moe_layer(fmt, x[rows], L.router, L.experts, k)
+    outs = []
+    for flags in (B.MOE_FFN_GROUPED, B.MOE_FFN_GROUPED | B.MOE_FFN_MX_NATIVE):
+        y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+        out = torch.empty((T, H), dtype=torch.uint16, device="cuda")
+        B.moe_expert_ffn(fmt, pool, L.stride, H, F, E, xd, idx, pair_perm=perm, expert_off=off, topk_w=w,
+                         y=y, out=out, flags=flags)
+        torch.cuda.synchronize()
+        yg = y.cpu().numpy().reshape(T, k, H)[rows].reshape(-1, H)
+        assert_rows_close(yg, ref["y"].reshape(-1, H), what=f"y flags {flags}")
+        assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what=f"out flags {flags}")
+        outs.append(out)
+    if T * k >= 2 * E:  # the layer call takes the grouped path: each flag setting gives that path's output
+        for lflags, o in zip((0, B.MOE_LAYER_MX_NATIVE), outs):
+            idx2, w2, out2 = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, xd, R, flags=lflags)
+            torch.cuda.synchronize()
+            assert torch.equal(idx2, idx) and torch.equal(out2, o)
+
+
 def test_grouped_tiny_mxfp4():
     _grouped_case(MX, 256, 8, 512, 2, 16, cfg=0)
 
@@ -903,6 +935,10 @@ def test_layer_forward_prefill_16k_sampled(fmt):
     _check_route(x[rows], L.router, k, idx.cpu()[rows], w.cpu()[rows])
     ref = moe.moe_layer(fmt, x[rows], L.router, L.experts, k)
     assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what="out")
+    if fmt == MX:  # the native scaled-MFMA path at the compute-bound size
+        _, _, out_n = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, _x_dev(x), R, flags=B.MOE_LAYER_MX_NATIVE)
+        torch.cuda.synchronize()
+        assert_rows_close(bf16_dev_to_f64(out_n)[rows], fm.bf16_to_f64(ref["out"]), what="out (native)")
 
 
 @pytest.mark.parametrize("fmt", [NV, MX, F8])
