@@ -196,6 +196,27 @@ def _list_resize(lru, S_new):
 ListLRU.resize = _list_resize
 
 
+class LayerView:
+    """One layer's view of a cache shared by several layers ([39TOK] section
+    "设计核心": the expert cache is one global LRU; the stated reading of its
+    cross-layer form).  The shared state is keyed by (layer, expert): layer j's
+    expert e is key key_base + e, with key_base = j * experts; each layer's
+    lookup is one step of the shared policy on its own keys, so victims may be
+    any slot the step does not request, whichever layer filled it.  Records
+    name the layer's experts, not keys.  ``lru`` is a StampLRU or a ListLRU over
+    all the keys (E = layers * experts)."""
+
+    def __init__(self, lru, key_base: int):
+        self.lru, self.key_base = lru, key_base
+
+    def step(self, pair_experts):
+        keys = [self.key_base + int(e) for e in np.asarray(pair_experts).ravel()]
+        r = self.lru.step(keys)
+        if r["status"] == OK:
+            r["miss_expert"] = np.asarray(r["miss_expert"], dtype=np.int32) - self.key_base
+        return r
+
+
 def simulate_hit_rate(steps, E: int, S: int, skip: int = 0):
     """Hit rate of a sequence of per-step access lists (steps >= skip counted)."""
     lru = StampLRU(E, S)

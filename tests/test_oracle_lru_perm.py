@@ -200,3 +200,89 @@ def test_permutation_properties(T, k, E):
         seg = perm[off[e]:off[e + 1]]
         assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)    # stable
     assert np.array_equal(perm, np.argsort(flat, kind="stable"))      # library sort
+
+
+# ------------------------------------------------ a cache shared by several layers
+
+def _shared_trace(rng, n_layers, E, k, n_steps):
+    """Per step, each layer's top-k accesses; layer j draws from a window of
+    experts whose width grows with j (unequal demand)."""
+    steps = []
+    for t in range(n_steps):
+        step = []
+        for j in range(n_layers):
+            width = k + 2 + 3 * j
+            step.append(rng.choice(width, size=k, replace=False) + (t // 5) % (E - width + 1))
+        steps.append(step)
+    return steps
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_shared_cache_stamp_and_list_forms_agree(seed):
+    """Layers taking turns on one keyed cache: the stamp form and the independent
+    list form give the same slot table and the same records (in experts) at every
+    layer step."""
+    rng = np.random.default_rng(seed)
+    n_layers, E, k, S = 4, 32, 3, 14
+    st, li = lru.StampLRU(n_layers * E, S), lru.ListLRU(n_layers * E, S)
+    vs = [lru.LayerView(st, j * E) for j in range(n_layers)]
+    vl = [lru.LayerView(li, j * E) for j in range(n_layers)]
+    for step in _shared_trace(rng, n_layers, E, k, 60):
+        for j, acc in enumerate(step):
+            a, b = vs[j].step(acc), vl[j].step(acc)
+            assert a["status"] == b["status"] == lru.OK
+            assert np.array_equal(a["pair_slot"], b["pair_slot"])
+            assert np.array_equal(a["miss_expert"], b["miss_expert"]) and np.array_equal(a["miss_slot"], b["miss_slot"])
+            assert np.all((a["miss_expert"] >= 0) & (a["miss_expert"] < E))
+            assert np.array_equal(st.slot_expert, li.slot_table())
+
+
+def test_shared_cache_holds_the_most_recent_keys():
+    """Brute force from the raw access sequence: after every step the cache holds
+    exactly the min(S, distinct) most recently used keys, whichever layer used them."""
+    rng = np.random.default_rng(5)
+    n_layers, E, k, S = 3, 24, 2, 9
+    st = lru.StampLRU(n_layers * E, S)
+    views = [lru.LayerView(st, j * E) for j in range(n_layers)]
+    seq = []
+    for step in _shared_trace(rng, n_layers, E, k, 80):
+        for j, acc in enumerate(step):
+            assert views[j].step(acc)["status"] == lru.OK
+            seq += [j * E + int(e) for e in acc]
+            last = {}
+            for i, key in enumerate(seq):
+                last[key] = i
+            recent = sorted(last, key=lambda key: -last[key])[:S]
+            assert set(int(v) for v in st.slot_expert if v >= 0) == set(recent)
+
+
+def test_shared_cache_gives_a_busy_layer_the_idle_slots():
+    """A worked case: layer 0 cycles through 6 experts, one per step, layer 1
+    repeats one expert.  With 4 slots each, layer 0's cyclic scan of more experts
+    than slots never hits; with the same 8 slots shared, the 7 keys in use fit and
+    after the first cycle every access hits."""
+    E = 16
+    trace = [([t % 6], [9]) for t in range(30)]
+    per = [lru.StampLRU(E, 4), lru.StampLRU(E, 4)]
+    shared = lru.StampLRU(2 * E, 8)
+    views = [lru.LayerView(shared, 0), lru.LayerView(shared, E)]
+    miss_per = miss_shared = 0
+    for t, (a0, a1) in enumerate(trace):
+        for j, acc in enumerate((a0, a1)):
+            rp, rs = per[j].step(acc), views[j].step(acc)
+            if t >= 6:
+                miss_per += rp["n_miss"]
+                miss_shared += rs["n_miss"]
+    assert miss_shared == 0
+    assert miss_per == 24          # every layer-0 access of steps 6..29, none of layer 1
+
+
+def test_shared_cache_with_one_layer_is_the_per_layer_cache():
+    rng = np.random.default_rng(3)
+    a, b = lru.StampLRU(40, 7), lru.StampLRU(40, 7)
+    v = lru.LayerView(b, 0)
+    for _ in range(50):
+        acc = rng.choice(12, size=3, replace=False)
+        ra, rb = a.step(acc), v.step(acc)
+        assert np.array_equal(ra["pair_slot"], rb["pair_slot"]) and ra["n_miss"] == rb["n_miss"]
+
