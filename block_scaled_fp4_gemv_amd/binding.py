@@ -27,7 +27,7 @@ _vp, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_si
 
 class moe_lru(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int32), ("S", ctypes.c_int32), ("slot_expert", _vp),
-                ("expert_slot", _vp), ("slot_stamp", _vp), ("clock", _vp)]
+                ("expert_slot", _vp), ("slot_stamp", _vp), ("clock", _vp), ("key_base", ctypes.c_int32)]
 
 
 class moe_cached_layer(ctypes.Structure):
@@ -233,19 +233,30 @@ def moe_route(x, router, k, flags=0, topk_idx=None, topk_w=None, pair_perm=None,
 # ------------------------------------------------------------------ cache
 
 class LRUState:
-    """Per-layer LRU state in device memory (torch tensors) + the C struct view."""
+    """LRU state in device memory (torch tensors) + the C struct view.  E is the
+    number of keys; key_base the key of this view's expert 0 (views of one state
+    with different key bases let several layers share one cache)."""
 
-    def __init__(self, E, S, device="cuda"):
+    key_base = 0
+
+    def __init__(self, E, S, device="cuda", key_base=0):
         import torch
-        self.E, self.S = E, S
+        self.E, self.S, self.key_base = E, S, key_base
         self.slot_expert = torch.full((S,), -1, dtype=torch.int32, device=device)
         self.expert_slot = torch.full((E,), -1, dtype=torch.int32, device=device)
         self.slot_stamp = torch.zeros(S, dtype=torch.int64, device=device)
         self.clock = torch.zeros(1, dtype=torch.int64, device=device)
 
+    def view(self, key_base):
+        """The same state (same tensors) seen from another key range."""
+        v = LRUState.__new__(LRUState)
+        v.__dict__.update(self.__dict__)
+        v.key_base = key_base
+        return v
+
     def c(self):
         return moe_lru(self.E, self.S, _ptr(self.slot_expert), _ptr(self.expert_slot),
-                       _ptr(self.slot_stamp), _ptr(self.clock))
+                       _ptr(self.slot_stamp), _ptr(self.clock), self.key_base)
 
 
 def moe_lru_reset(state, stream=None):
@@ -374,12 +385,17 @@ class CachedLayer:
     host pool ([pinned] uint8 tensor of E blobs), slot pool (device, S blobs), LRU
     state, a pinned miss record and three events (created here)."""
 
-    def __init__(self, router, host_pool, slot_pool, E, S, T, k, rec_on_device=False):
+    def __init__(self, router, host_pool, slot_pool, E, S, T, k, rec_on_device=False, lru=None):
+        """lru: a shared LRUState view (keyed, e.g. ``state.view(j * E)`` for layer j
+        of a group sharing one cache; slot_pool is then the group's pool)."""
         import torch
         self.router, self.host_pool, self.slot_pool = router, host_pool, slot_pool
         self.T, self.k, self.rec_on_device = T, k, rec_on_device
-        self.lru = LRUState(E, S, router.device)
-        moe_lru_reset(self.lru)
+        if lru is None:
+            self.lru = LRUState(E, S, router.device)
+            moe_lru_reset(self.lru)
+        else:
+            self.lru = lru
         self._new_record()
         self.lookup_done, self.slots_free, self.fill_done = (torch.cuda.Event() for _ in range(3))
         for ev in (self.lookup_done, self.slots_free, self.fill_done):
@@ -410,8 +426,9 @@ class CachedLayer:
             dst.E, dst.S = self.lru.E, S_new
             dst.slot_expert, dst.slot_stamp = self.lru.slot_expert[:S_new], self.lru.slot_stamp[:S_new]
             dst.expert_slot, dst.clock = self.lru.expert_slot, self.lru.clock
+            dst.key_base = self.lru.key_base
         else:
-            dst = LRUState(self.lru.E, S_new, self.router.device)
+            dst = LRUState(self.lru.E, S_new, self.router.device, key_base=self.lru.key_base)
         moe_lru_resize(self.lru, self.slot_pool, dst, pool, expert_bytes, stride, ws=ws, stream=stream)
         self.lru, self.slot_pool = dst, pool
         if moe_miss_record_words(self.T, self.k, S_new) != self.miss_rec.numel():

@@ -102,7 +102,7 @@ hipError_t launch_combine_rec(const float* y, const float* w, int T, int H, int 
 hipError_t launch_lru_reset(const moe_lru& l, hipStream_t s);
 // The same step with the routed experts selected inside the kernel from the
 // router logits (softmax + top-k; T <= 4, k <= 16), writing topk_idx / topk_w.
-hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int T, int k, unsigned flags,
+hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int E_route, int T, int k, unsigned flags,
                                   int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
                                   int32_t* miss_rec, int n_max, hipStream_t s);
 // Copy the blobs named by a miss record (read on the device) from the host

@@ -14,6 +14,11 @@
 //    by ascending index first, then occupied slots by ascending stamp;
 //  * access q (pair order) advances the clock and stamps its slot, so a slot's
 //    final stamp is clock0 + (last access index of its expert) + 1.
+// The state is keyed: expert e of a lookup is key key_base + e, so one state
+// and one slot pool can serve several layers (each layer its own key range),
+// the cross-layer form of the global cache; a per-layer cache has key_base 0.
+// Miss records list experts (key - key_base), as the fills index the layer's
+// own host pool by expert.
 #include "common.h"
 #include "launch.h"
 #include "topk.h"
@@ -50,6 +55,8 @@ __device__ int block_exclusive_scan(int v, int* sh, int* total) {
 // saves a dependent kernel between the router and the lookup.
 constexpr int kMaxFusedPairs = (kThreads / 64) * 16;
 
+// E: keys of the state; key_base: this lookup's first key; E_route: experts
+// of the fused top-k.
 template <int NV>
 __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     int E, int S, int32_t* __restrict__ slot_expert, int32_t* __restrict__ expert_slot,
@@ -57,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     const int32_t* __restrict__ idx_in, int n, int32_t* __restrict__ pair_slot,
     int32_t* __restrict__ pair_order, int32_t* __restrict__ rec, int n_max,
     const float* __restrict__ logits, int k, unsigned flags, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
+    float* __restrict__ topk_w, int key_base, int E_route) {
   __shared__ int s_idx[kMaxFusedPairs];
   const int32_t* idx = idx_in;
   const int tid = threadIdx.x;
@@ -80,10 +87,10 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63, T = n / k;
     if (wv < T) {
       float v[NV];
-      wave_load_logits<NV>(logits + (size_t)wv * E, E, v);
+      wave_load_logits<NV>(logits + (size_t)wv * E_route, E_route, v);
       int e;
       float wt;
-      wave_topk_regs<NV>(v, E, k, flags, e, wt, s_topk[wv]);
+      wave_topk_regs<NV>(v, E_route, k, flags, e, wt, s_topk[wv]);
       if (ln < k) {
         s_idx[wv * k + ln] = e;
         topk_idx[wv * k + ln] = e;
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
   }
   __syncthreads();
   for (int q = tid; q < n; q += blockDim.x) {
-    const int e = idx[q];
+    const int e = key_base + idx[q];
     atomicMin(&s_first[e], q);
     atomicMax(&s_last[e], q);
   }
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     const int q = base + tid;
     int e = -1, flag = 0;
     if (q < n) {
-      e = idx[q];
+      e = key_base + idx[q];
       flag = (s_first[e] == q) && !s_resident[e];
     }
     int tot;
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
   __syncthreads();
   // stamps: last access of each requested expert
   for (int q = tid; q < n; q += blockDim.x) {
-    const int e = idx[q];
+    const int e = key_base + idx[q];
     if (s_last[e] == q) s_stamp[s_eslot[e]] = c0 + q + 1;
     pair_slot[q] = s_eslot[e];
   }
@@ -213,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     int c = 0;
     for (int base = 0; base < n; base += blockDim.x) {
       const int q = base + tid;
-      const int f = q < n ? s_resident[idx[q]] : 0;
+      const int f = q < n ? s_resident[key_base + idx[q]] : 0;
       int tot;
       const int r = block_exclusive_scan(f, s_scan, &tot) + c;
       if (q < n && f) pair_order[r] = q;
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     c = 0;
     for (int base = 0; base < n; base += blockDim.x) {
       const int q = base + tid;
-      const int f = q < n ? !s_resident[idx[q]] : 0;
+      const int f = q < n ? !s_resident[key_base + idx[q]] : 0;
       int tot;
       const int r = block_exclusive_scan(f, s_scan, &tot) + c;
       if (q < n && f) pair_order[nh + r] = q;
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     slot_stamp[s] = s_stamp[s];
   }
   for (int r = tid; r < n_miss; r += blockDim.x) {
-    rec[5 + r] = s_miss_exp[r];
+    rec[5 + r] = s_miss_exp[r] - key_base;
     rec[5 + n_max + r] = s_victim[r];
   }
   if (tid == 0) {
@@ -264,20 +271,23 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// E_route: experts of this lookup (keys key_base .. key_base + E_route - 1;
+// the fused top-k runs over them).
 template <int NE, bool FUSED>
 __global__ __launch_bounds__(64) void k_lru_lookup_wave(
-    int E, int S, int32_t* __restrict__ slot_expert, int32_t* __restrict__ expert_slot,
+    int E_route, int S, int32_t* __restrict__ slot_expert, int32_t* __restrict__ expert_slot,
     int64_t* __restrict__ slot_stamp, int64_t* __restrict__ clock,
     const int32_t* __restrict__ idx_in, int n, int32_t* __restrict__ pair_slot,
     int32_t* __restrict__ pair_order, int32_t* __restrict__ rec, int n_max,
     const float* __restrict__ logits, int k, unsigned flags, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
+    float* __restrict__ topk_w, int key_base) {
+  const int E = E_route;
   const int lane = threadIdx.x;
   const uint64_t lt = (1ull << lane) - 1ull;
   // the state at the step start, requested before the top-k
-  int es[NE];  // expert_slot[lane + 64 i]
+  int es[NE];  // expert_slot[key_base + lane + 64 i]
 #pragma unroll
-  for (int i = 0; i < NE; ++i) es[i] = lane + 64 * i < E ? expert_slot[lane + 64 * i] : -1;
+  for (int i = 0; i < NE; ++i) es[i] = lane + 64 * i < E ? expert_slot[key_base + lane + 64 * i] : -1;
   const int sexp0 = lane < S ? slot_expert[lane] : -1;
   const long long stamp0 = lane < S ? slot_stamp[lane] : 0;
   const long long c0 = *clock;
@@ -369,7 +379,7 @@ __global__ __launch_bounds__(64) void k_lru_lookup_wave(
   int sexp = sexp0;
   long long stamp = stamp0;
   for (int r = 0; r < n_miss; ++r)
-    if (lane == __builtin_amdgcn_readlane(victim, r)) sexp = __builtin_amdgcn_readlane(new_e, r);
+    if (lane == __builtin_amdgcn_readlane(victim, r)) sexp = key_base + __builtin_amdgcn_readlane(new_e, r);
   // the access's slot after the install: a missed expert's victim, by the
   // miss rank of its first access
   const int rr = __shfl(miss_rank, first & 63);
@@ -391,9 +401,9 @@ __global__ __launch_bounds__(64) void k_lru_lookup_wave(
     slot_expert[lane] = sexp;
     slot_stamp[lane] = stamp;
   }
-  if (lane < n_miss) {
+  if (lane < n_miss) {  // slot_expert holds keys; new_e is this lookup's expert
     if (old_e >= 0) expert_slot[old_e] = -1;
-    expert_slot[new_e] = victim;
+    expert_slot[key_base + new_e] = victim;
     rec[5 + lane] = new_e;
     rec[5 + n_max + lane] = victim;
   }
@@ -430,34 +440,35 @@ hipError_t launch_lru_reset(const moe_lru& l, hipStream_t s) {
 hipError_t launch_lru_lookup(const moe_lru& l, const int32_t* topk_idx, int n_pairs,
                              int32_t* pair_slot, int32_t* pair_order, int32_t* miss_rec, int n_max,
                              hipStream_t s) {
-  if (l.S <= 64 && n_pairs <= 64) {  // one wavefront
-#define W(NE)                                                                                           \
-  hipLaunchKernelGGL((k_lru_lookup_wave<NE, false>), dim3(1), dim3(64), 0, s, l.E, l.S, l.slot_expert,  \
-                     l.expert_slot, l.slot_stamp, l.clock, topk_idx, n_pairs, pair_slot, pair_order,     \
-                     miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr)
-    if (l.E <= 64) W(1);
-    else if (l.E <= 256) W(4);
+  const int E_route = l.E - l.key_base;  // the experts a lookup can name
+  if (l.S <= 64 && n_pairs <= 64 && E_route <= 1024) {  // one wavefront
+#define W(NE)                                                                                             \
+  hipLaunchKernelGGL((k_lru_lookup_wave<NE, false>), dim3(1), dim3(64), 0, s, E_route, l.S, l.slot_expert, \
+                     l.expert_slot, l.slot_stamp, l.clock, topk_idx, n_pairs, pair_slot, pair_order,       \
+                     miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr, l.key_base)
+    if (E_route <= 64) W(1);
+    else if (E_route <= 256) W(4);
     else W(16);
 #undef W
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_lru_lookup<0>, dim3(1), dim3(kThreads), 0, s, l.E, l.S, l.slot_expert,
                      l.expert_slot, l.slot_stamp, l.clock, topk_idx, n_pairs, pair_slot, pair_order,
-                     miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr);
+                     miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr, l.key_base, E_route);
   return hipGetLastError();
 }
 
-hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int T, int k, unsigned flags,
+hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int E_route, int T, int k, unsigned flags,
                                   int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
                                   int32_t* miss_rec, int n_max, hipStream_t s) {
-  if (T > kThreads / 64 || k > 16) return hipErrorInvalidValue;
+  if (T > kThreads / 64 || k > 16 || E_route > 1024) return hipErrorInvalidValue;
   if (T == 1 && l.S <= 64) {  // one wavefront
-#define W(NE)                                                                                           \
-  hipLaunchKernelGGL((k_lru_lookup_wave<NE, true>), dim3(1), dim3(64), 0, s, l.E, l.S, l.slot_expert,   \
-                     l.expert_slot, l.slot_stamp, l.clock, nullptr, k, pair_slot, pair_order, miss_rec,  \
-                     n_max, logits, k, flags, topk_idx, topk_w)
-    if (l.E <= 64) W(1);
-    else if (l.E <= 256) W(4);
+#define W(NE)                                                                                             \
+  hipLaunchKernelGGL((k_lru_lookup_wave<NE, true>), dim3(1), dim3(64), 0, s, E_route, l.S, l.slot_expert,  \
+                     l.expert_slot, l.slot_stamp, l.clock, nullptr, k, pair_slot, pair_order, miss_rec,    \
+                     n_max, logits, k, flags, topk_idx, topk_w, l.key_base)
+    if (E_route <= 64) W(1);
+    else if (E_route <= 256) W(4);
     else W(16);
 #undef W
     return hipGetLastError();
@@ -465,9 +476,9 @@ hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int T, 
 #define L(NV)                                                                                           \
   hipLaunchKernelGGL(k_lru_lookup<NV>, dim3(1), dim3(kThreads), 0, s, l.E, l.S, l.slot_expert,          \
                      l.expert_slot, l.slot_stamp, l.clock, nullptr, T * k, pair_slot, pair_order, miss_rec, \
-                     n_max, logits, k, flags, topk_idx, topk_w)
-  if (l.E <= 64) L(1);
-  else if (l.E <= 256) L(4);
+                     n_max, logits, k, flags, topk_idx, topk_w, l.key_base, E_route)
+  if (E_route <= 64) L(1);
+  else if (E_route <= 256) L(4);
   else L(16);
 #undef L
   return hipGetLastError();

@@ -100,7 +100,7 @@ const char* moe_status_str(int s) {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_abi_version(void) { return (1 << 16) | 0; }
+int moe_abi_version(void) { return (1 << 16) | 1; }
 
 // ------------------------------------------------------------------ blobs
 
@@ -269,7 +269,9 @@ int moe_cache_lookup(const moe_lru* lru, const int32_t* topk_idx, int T, int k, 
     return fail(MOE_E_ARG, "NULL lru state");
   if (lru->E < 1 || lru->E > 1024 || lru->S < 1 || lru->S > 1024)
     return fail(MOE_E_ARG, "E=%d S=%d outside [1, 1024]", lru->E, lru->S);
-  if (T < 0 || k < 1 || k > lru->E) return fail(MOE_E_ARG, "T=%d k=%d", T, k);
+  if (lru->key_base < 0 || lru->key_base >= lru->E)
+    return fail(MOE_E_ARG, "key_base %d outside [0, E=%d)", lru->key_base, lru->E);
+  if (T < 0 || k < 1 || k > lru->E - lru->key_base) return fail(MOE_E_ARG, "T=%d k=%d", T, k);
   if (!miss_rec) return fail(MOE_E_ARG, "NULL miss_rec");
   const int n = T * k;
   if (n > 0 && (!topk_idx || !pair_slot || !pair_order)) return fail(MOE_E_ARG, "NULL pair arrays");
@@ -707,8 +709,9 @@ int moe_cached_layer_enqueue(int fmt, size_t stride, int H, int F, int E, int k,
   const size_t route_bytes = moe_route_workspace(T, H, E, k);
   void* route_ws = p;
   p += align256(route_bytes);
-  if (L->lru.E != E || L->lru.S < 1 || L->lru.S > 1024 || E > 1024)
-    return fail(MOE_E_ARG, "LRU state E=%d S=%d for E=%d", L->lru.E, L->lru.S, E);
+  if (L->lru.key_base < 0 || L->lru.key_base + E > L->lru.E || L->lru.E > 1024 || L->lru.S < 1 || L->lru.S > 1024)
+    return fail(MOE_E_ARG, "LRU state of %d keys (this layer from key %d), %d slots, for E=%d", L->lru.E,
+                L->lru.key_base, L->lru.S, E);
   if (T < 0 || k < 1 || k > E || k > 16) return fail(MOE_E_ARG, "T=%d k=%d E=%d", T, k, E);
   if (T <= 4 && k <= 16) {
     // router GEMV, then the lookup kernel selects the experts itself (one kernel fewer)
@@ -718,7 +721,7 @@ int moe_cached_layer_enqueue(int fmt, size_t stride, int H, int F, int E, int k,
     if (!aligned(x, 16) || !aligned(L->router, 16)) return fail(MOE_E_ARG, "x and router must be 16-byte aligned");
     hipError_t e = launch_router_logits(x, L->router, T, H, E, r.logits, s);
     if (e == hipSuccess)
-      e = launch_lru_lookup_topk(L->lru, r.logits, T, k, route_flags, topk_idx, topk_w, pair_slot, pair_order,
+      e = launch_lru_lookup_topk(L->lru, r.logits, E, T, k, route_flags, topk_idx, topk_w, pair_slot, pair_order,
                                  L->miss_rec, T * k < L->lru.S ? T * k : L->lru.S, s);
     if (e != hipSuccess) return hip_fail(e, "cached layer (route + lookup)");
   } else {

@@ -157,18 +157,26 @@ int moe_route(const uint16_t* x, const float* router, int T, int H, int E, int k
 
 /* --------------------------------------------------------------- cache */
 
-/* Per-layer LRU state, caller-owned device memory (page "8GB 笔记本 39.3 tok/s...",
- * section "设计核心": a global LRU expert cache in VRAM).
- *   slot_expert int32 [S]  expert held by each slot, -1 = empty
- *   expert_slot int32 [E]  slot holding each expert, -1 = not resident
+/* LRU state of a VRAM expert cache, caller-owned device memory (page "8GB 笔记本
+ * 39.3 tok/s...", section "设计核心": a global LRU expert cache in VRAM).  The
+ * state is keyed: a lookup's expert e is key key_base + e.  A per-layer cache
+ * has E keys = the layer's experts and key_base 0.  Layers that share one state
+ * and one slot pool (the cross-layer form of the global cache) each pass a
+ * moe_lru with the same arrays and their own key_base, e.g. layer j of a group
+ * at j * experts, with E = the keys of the whole group.
+ *   slot_expert int32 [S]  key held by each slot, -1 = empty
+ *   expert_slot int32 [E]  slot holding each key, -1 = not resident
  *   slot_stamp  int64 [S]  clock value of the slot's last access (0 = never)
- *   clock       int64 [1]  accesses so far */
+ *   clock       int64 [1]  accesses so far
+ *   key_base    key of this lookup's expert 0 (0 <= key_base < E; every routed
+ *               expert e must have key_base + e < E) */
 typedef struct moe_lru {
   int32_t E, S;
   int32_t* slot_expert;
   int32_t* expert_slot;
   int64_t* slot_stamp;
   int64_t* clock;
+  int32_t key_base;
 } moe_lru;
 
 /* Set the state to a cold cache (all slots empty, clock 0).  Stream-ordered. */
