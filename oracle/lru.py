@@ -217,6 +217,20 @@ class LayerView:
         return r
 
 
+def prefetch_step(lru, ranked):
+    """Predictive prefetch after a layer's routed step ([753B] section
+    "按带宽动态分配参数存储": copies guided by the gate's routing run ahead of
+    use; the pages give no predictor, so the stated reading takes the token's
+    runner-up experts).  ``ranked`` is the token's top-(k+m) experts in rank
+    order, the first k being the ones just routed.  The rule is one more step
+    of the same policy over that list: the routed experts are hits and are
+    restamped in rank order, each runner-up that misses takes a victim by the
+    usual rule (so never a slot of this list) and is stamped after them.  The
+    step's misses are the prefetched experts; ``lru`` is a StampLRU or a
+    ListLRU."""
+    return lru.step(list(ranked))
+
+
 def simulate_hit_rate(steps, E: int, S: int, skip: int = 0):
     """Hit rate of a sequence of per-step access lists (steps >= skip counted)."""
     lru = StampLRU(E, S)

@@ -286,3 +286,70 @@ def test_shared_cache_with_one_layer_is_the_per_layer_cache():
         ra, rb = a.step(acc), v.step(acc)
         assert np.array_equal(ra["pair_slot"], rb["pair_slot"]) and ra["n_miss"] == rb["n_miss"]
 
+
+# ----------------------------------------------------------- predictive prefetch
+
+def _ranked_trace(seed, n_steps, E, km):
+    """Per step a ranked list of km distinct experts drifting slowly (the first k
+    are routed, the rest runner-ups)."""
+    rng = np.random.default_rng(seed)
+    base = rng.permutation(E)
+    out = []
+    for t in range(n_steps):
+        if t and rng.random() < 0.5:
+            i, j = rng.integers(0, E, size=2)
+            base[[i, j]] = base[[j, i]]
+        out.append(base[:km].copy())
+        rng.shuffle(base[:km + 3])
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_prefetch_stamp_and_list_forms_agree(seed):
+    E, S, k, m = 40, 12, 4, 3
+    st, li = lru.StampLRU(E, S), lru.ListLRU(E, S)
+    for ranked in _ranked_trace(seed, 80, E, k + m):
+        a, b = st.step(ranked[:k]), li.step(ranked[:k])
+        assert np.array_equal(a["pair_slot"], b["pair_slot"])
+        pa, pb = lru.prefetch_step(st, ranked), lru.prefetch_step(li, ranked)
+        assert pa["status"] == pb["status"] == lru.OK
+        assert np.array_equal(pa["miss_expert"], pb["miss_expert"]) and np.array_equal(pa["miss_slot"], pb["miss_slot"])
+        assert np.array_equal(st.slot_expert, li.slot_table())
+
+
+def test_prefetch_keeps_the_routed_experts_in_place():
+    """The prefetch step never evicts or moves an expert the token was routed to,
+    and afterwards every runner-up is resident."""
+    E, S, k, m = 64, 14, 6, 4
+    st = lru.StampLRU(E, S)
+    for ranked in _ranked_trace(7, 60, E, k + m):
+        r = st.step(ranked[:k])
+        p = lru.prefetch_step(st, ranked)
+        assert p["n_miss"] <= m
+        assert np.array_equal(p["pair_slot"][:k], r["pair_slot"])
+        assert all(st.expert_slot[e] >= 0 for e in ranked)
+
+
+def test_prefetch_of_the_next_expert_removes_every_miss():
+    """A worked case: a window of k experts slides by one each step (t .. t+k-1),
+    and the runner-up is the next one (t+k).  Without prefetch every step after
+    the first misses its newest expert; with it that expert was fetched one step
+    earlier, so no routed access misses after the first step and every prefetch
+    is used (prefetch accuracy 1)."""
+    E, S, k, n = 50, 10, 4, 30
+    plain, pre = lru.StampLRU(E, S), lru.StampLRU(E, S)
+    miss_plain = miss_pre = used = fetched = 0
+    prev_pf = set()
+    for t in range(n):
+        routed = list(range(t, t + k))
+        rp = plain.step(routed)
+        miss_plain += rp["n_miss"] if t else 0
+        r = pre.step(routed)
+        miss_pre += r["n_miss"] if t else 0
+        used += len(prev_pf & set(routed))
+        p = lru.prefetch_step(pre, routed + [t + k])
+        prev_pf = set(int(e) for e in p["miss_expert"])
+        fetched += len(prev_pf)
+    assert miss_plain == n - 1 and miss_pre == 0
+    assert fetched == n and used == n - 1
+
