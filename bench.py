@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--cache-elastic-steps", type=int, default=64,
                    help="after the timed cache steps: resize every layer's slot cache (half in place, then "
                         "1.5x into new pools) and run this many steps after each resize (0 = skip)")
+    p.add_argument("--cache-shared-steps", type=int, default=96,
+                   help="steps of the cross-layer cache comparison (per-layer vs shared pools on a trace with "
+                        "unequal demand; 0 = skip)")
     p.add_argument("--cache-host-sync", action="store_true",
                    help="time the host-waiting executor (moe_cached_layer_forward) instead")
     p.add_argument("--prefill-stream-reps", type=int, default=3,
@@ -234,6 +237,85 @@ def cache_leg(name, fmt, hosts, routers, stride, warmup, steps, host_sync=False,
             "h2d_GBps": round(float(tot[1]) * eb / dt / 1e9, 2), "expert_blob_bytes": eb,
             "timing": "host wall clock over the timed steps, synchronised at both ends",
             **({"elastic": elastic} if elastic else {})}
+
+
+def cache_shared_leg(fmt, hosts, stride, warmup, steps, group=4):
+    """The global cache in its cross-layer form: the decode35b layers with routers
+    whose rows are scaled by exp(sigma * N(0,1)), sigma = layer % 4 (unequal
+    demand: larger sigma concentrates routing on fewer experts), run once with a
+    64-slot cache per layer and once with one 256-slot cache shared by each group
+    of 4 layers (the same slots in all).  Each 40-layer step is one HIP graph."""
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_gemv_amd import binding as B
+    from block_scaled_fp4_gemv_amd import synth as sy
+
+    wl = sy.WORKLOADS["cache35b"]
+    H, E, F, k, S = wl.H, wl.E, wl.F, wl.k, wl.slots
+    n_layers = len(hosts)
+    routers = [torch.from_numpy(sy.router_skewed(0, wl.wcfg, l, E, H, float(l % group))).cuda()
+               for l in range(n_layers)]
+    xs = torch.from_numpy(sy.ar1_sequence(0, wl.cfg_id, warmup + steps, H)).cuda()
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    pair_slot = torch.empty(k, dtype=torch.int32, device="cuda")
+    pair_order = torch.empty(k, dtype=torch.int32, device="cuda")
+    out = torch.empty((1, H), dtype=torch.uint16, device="cuda")
+    xbuf = torch.empty((1, H), dtype=torch.uint16, device="cuda")
+    eb = B.moe_expert_bytes(fmt, H, F)
+    res = {}
+    for mode in ("per_layer", "shared"):
+        layers = []
+        if mode == "per_layer":
+            for l in range(n_layers):
+                pool = torch.zeros(S * stride, dtype=torch.uint8, device="cuda")
+                layers.append(B.CachedLayer(routers[l], hosts[l], pool, E, S, 1, k, rec_on_device=True))
+        else:
+            for g in range(0, n_layers, group):
+                n = min(group, n_layers - g)
+                state = B.LRUState(n * E, n * S)
+                B.moe_lru_reset(state)
+                pool = torch.zeros(n * S * stride, dtype=torch.uint8, device="cuda")
+                for j in range(n):
+                    layers.append(B.CachedLayer(routers[g + j], hosts[g + j], pool, E, n * S, 1, k,
+                                                rec_on_device=True, lru=state.view(j * E)))
+
+        def enqueue():
+            for L in layers:
+                B.moe_cached_layer_enqueue(fmt, stride, H, F, E, k, L, xbuf, idx, w, pair_slot, pair_order, out, ws)
+
+        for t in range(warmup):
+            xbuf.copy_(xs[t:t + 1])
+            enqueue()
+        torch.cuda.synchronize()
+        g_ = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_):
+            enqueue()
+        torch.cuda.synchronize()
+        recs = []
+        t0 = time.perf_counter()
+        for t in range(warmup, warmup + steps):
+            xbuf.copy_(xs[t:t + 1])
+            g_.replay()
+            recs.append(torch.stack([L.miss_rec[:4] for L in layers]))
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        r = torch.stack(recs).cpu().numpy()
+        assert (r[:, :, 0] == 0).all(), "cache capacity error"
+        hits, misses = float(r[:, :, 3].sum()), float(r[:, :, 1].sum())
+        res[mode] = {"slots": f"{S} per layer" if mode == "per_layer" else f"{group * S} per group of {group} layers",
+                     "tokens_per_s": round(steps / dt, 2), "hit_rate": round(hits / (steps * n_layers * k), 4),
+                     "misses_per_token": round(misses / steps, 2),
+                     "h2d_GBps": round(misses * eb / dt / 1e9, 2)}
+        del layers
+        torch.cuda.empty_cache()
+    return {"workload": f"cache35b layers with unequal demand (router rows scaled by exp(sigma * N(0,1)), sigma = "
+                        f"layer % {group}), {n_layers} layers, batch 1",
+            "warmup_steps": warmup, "timed_steps": steps, **res,
+            "miss_reduction": round(1 - res["shared"]["misses_per_token"] /
+                                    max(res["per_layer"]["misses_per_token"], 1e-9), 4)}
 
 
 def algorithmic_bytes(wl, fmt):
@@ -591,6 +673,10 @@ def main():
                                  host_sync=args.cache_host_sync, elastic_steps=args.cache_elastic_steps)
         log(f"cache: {res['cache']['tokens_per_s']} tok/s, hit rate {res['cache']['hit_rate']}, "
             f"{res['cache']['h2d_GBps']} GB/s H2D")
+        if args.cache_shared_steps > 0:
+            log("shared-cache leg ...")
+            res["cache_shared"] = cache_shared_leg(fmt, hosts, stride, args.cache_warmup, args.cache_shared_steps)
+            log(f"shared cache: per-layer {res['cache_shared']['per_layer']}, shared {res['cache_shared']['shared']}")
         if args.prefill_stream_reps > 0:
             log("streamed-prefill leg ...")
             res["prefill_stream"] = prefill_stream_leg(fmt, hosts, pools, routers, stride, args.prefill_stream_reps)

@@ -71,6 +71,11 @@ SIGNATURES = {
                                         ctypes.POINTER(moe_cached_layer), _vp, _i32, _vp, _vp, _vp, _vp,
                                         _vp, _vp, _sz, _vp, _vp, ctypes.POINTER(ctypes.c_int32),
                                         ctypes.POINTER(ctypes.c_int32)]),
+    "moe_prefetch_buffer_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "moe_prefetch_record_offset": (_sz, [_i32]),
+    "moe_cached_layer_enqueue_prefetch": (_i32, [_i32, _sz, _i32, _i32, _i32, _i32, _u32,
+                                                 ctypes.POINTER(moe_cached_layer), _vp, _i32, _vp, _vp, _vp, _vp,
+                                                 _vp, _vp, _sz, _i32, _vp, _sz, _vp, _vp]),
     "moe_prefill_streamed_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_prefill_streamed": (_i32, [_i32, _sz, _i32, _i32, _i32, _i32, _u32, _i32, ctypes.POINTER(_vp),
                                     ctypes.POINTER(_vp), _vp, _i32, ctypes.POINTER(_vp), _vp, _vp,
@@ -469,6 +474,32 @@ def moe_cached_layer_enqueue(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w
                                         _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
                                         _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_cached_layer_enqueue")
+
+
+def moe_prefetch_buffer_bytes(E, k, m, S):
+    return int(lib().moe_prefetch_buffer_bytes(E, k, m, S))
+
+
+def new_prefetch_buffer(E, k, m, S, device="cuda"):
+    import torch
+    return torch.zeros(moe_prefetch_buffer_bytes(E, k, m, S), dtype=torch.uint8, device=device)
+
+
+def prefetch_record(pf_buf, E, k, m, S):
+    """The prefetch step's miss record (a view of pf_buf)."""
+    off = int(lib().moe_prefetch_record_offset(E))
+    return pf_buf[off:off + 4 * moe_miss_record_words(1, k + m, S)].view(dtype=__import__("torch").int32)
+
+
+def moe_cached_layer_enqueue_prefetch(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w, pair_slot, pair_order,
+                                      out, ws, m, pf_buf, pf_stream, flags=0, stream=None):
+    """moe_cached_layer_enqueue with the runner-up prefetch on pf_stream (T = 1)."""
+    T = x.shape[0]
+    st = lib().moe_cached_layer_enqueue_prefetch(fmt, stride, H, F, E, k, flags, ctypes.byref(layer.c), _ptr(x), T,
+                                                 _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
+                                                 _ptr(out), _ptr(ws), ws.numel(), m, _ptr(pf_buf), pf_buf.numel(),
+                                                 _stream(stream), _stream(pf_stream))
+    _check(st, "moe_cached_layer_enqueue_prefetch")
 
 
 # ------------------------------------------------- prefill with streamed experts

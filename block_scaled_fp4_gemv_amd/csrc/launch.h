@@ -102,13 +102,14 @@ hipError_t launch_combine_rec(const float* y, const float* w, int T, int H, int 
 hipError_t launch_lru_reset(const moe_lru& l, hipStream_t s);
 // The same step with the routed experts selected inside the kernel from the
 // router logits (softmax + top-k; T <= 4, k <= 16), writing topk_idx / topk_w.
+// logit_out (optional): the kernel also stores the [T][E_route] logits it read.
 hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int E_route, int T, int k, unsigned flags,
                                   int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
-                                  int32_t* miss_rec, int n_max, hipStream_t s);
+                                  int32_t* miss_rec, int n_max, hipStream_t s, float* logit_out = nullptr);
 // Copy the blobs named by a miss record (read on the device) from the host
 // pool (pinned, device-addressable) into their victim slots.
 hipError_t launch_cache_fill(const int32_t* miss_rec, const uint8_t* host_pool, uint8_t* slot_pool,
-                             size_t expert_bytes, size_t stride, hipStream_t s);
+                             size_t expert_bytes, size_t stride, hipStream_t s, int n_groups = 512);
 // Rebuild a layer's slot cache for to.S slots (state and blobs; plan: 1 + 2 * to.S
 // int32 of workspace).  from_pool == to_pool rebuilds the pool in place.
 hipError_t launch_lru_resize(const moe_lru& from, const uint8_t* from_pool, const moe_lru& to, uint8_t* to_pool,

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     const int32_t* __restrict__ idx_in, int n, int32_t* __restrict__ pair_slot,
     int32_t* __restrict__ pair_order, int32_t* __restrict__ rec, int n_max,
     const float* __restrict__ logits, int k, unsigned flags, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int key_base, int E_route) {
+    float* __restrict__ topk_w, int key_base, int E_route, float* __restrict__ logit_out) {
   __shared__ int s_idx[kMaxFusedPairs];
   const int32_t* idx = idx_in;
   const int tid = threadIdx.x;
@@ -88,6 +88,10 @@ __global__ __launch_bounds__(kThreads) void k_lru_lookup(
     if (wv < T) {
       float v[NV];
       wave_load_logits<NV>(logits + (size_t)wv * E_route, E_route, v);
+      if (logit_out)  // a copy of the logits for a later prefetch step
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (ln + 64 * i < E_route) logit_out[(size_t)wv * E_route + ln + 64 * i] = v[i];
       int e;
       float wt;
       wave_topk_regs<NV>(v, E_route, k, flags, e, wt, s_topk[wv]);
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(64) void k_lru_lookup_wave(
     const int32_t* __restrict__ idx_in, int n, int32_t* __restrict__ pair_slot,
     int32_t* __restrict__ pair_order, int32_t* __restrict__ rec, int n_max,
     const float* __restrict__ logits, int k, unsigned flags, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int key_base) {
+    float* __restrict__ topk_w, int key_base, float* __restrict__ logit_out) {
   const int E = E_route;
   const int lane = threadIdx.x;
   const uint64_t lt = (1ull << lane) - 1ull;
@@ -297,6 +301,10 @@ __global__ __launch_bounds__(64) void k_lru_lookup_wave(
     __shared__ TopkScratch s_topk;
     float v[NE];
     wave_load_logits<NE>(logits, E, v);
+    if (logit_out)  // a copy of the logits for a later prefetch step
+#pragma unroll
+      for (int i = 0; i < NE; ++i)
+        if (lane + 64 * i < E) logit_out[lane + 64 * i] = v[i];
     float wt;
     wave_topk_regs<NE>(v, E, k, flags, e, wt, s_topk);
     if (lane < k) {
@@ -445,7 +453,7 @@ hipError_t launch_lru_lookup(const moe_lru& l, const int32_t* topk_idx, int n_pa
 #define W(NE)                                                                                             \
   hipLaunchKernelGGL((k_lru_lookup_wave<NE, false>), dim3(1), dim3(64), 0, s, E_route, l.S, l.slot_expert, \
                      l.expert_slot, l.slot_stamp, l.clock, topk_idx, n_pairs, pair_slot, pair_order,       \
-                     miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr, l.key_base)
+                     miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr, l.key_base, nullptr)
     if (E_route <= 64) W(1);
     else if (E_route <= 256) W(4);
     else W(16);
@@ -454,19 +462,19 @@ hipError_t launch_lru_lookup(const moe_lru& l, const int32_t* topk_idx, int n_pa
   }
   hipLaunchKernelGGL(k_lru_lookup<0>, dim3(1), dim3(kThreads), 0, s, l.E, l.S, l.slot_expert,
                      l.expert_slot, l.slot_stamp, l.clock, topk_idx, n_pairs, pair_slot, pair_order,
-                     miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr, l.key_base, E_route);
+                     miss_rec, n_max, nullptr, 0, 0u, nullptr, nullptr, l.key_base, E_route, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int E_route, int T, int k, unsigned flags,
                                   int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
-                                  int32_t* miss_rec, int n_max, hipStream_t s) {
+                                  int32_t* miss_rec, int n_max, hipStream_t s, float* logit_out) {
   if (T > kThreads / 64 || k > 16 || E_route > 1024) return hipErrorInvalidValue;
   if (T == 1 && l.S <= 64) {  // one wavefront
 #define W(NE)                                                                                             \
   hipLaunchKernelGGL((k_lru_lookup_wave<NE, true>), dim3(1), dim3(64), 0, s, E_route, l.S, l.slot_expert,  \
                      l.expert_slot, l.slot_stamp, l.clock, nullptr, k, pair_slot, pair_order, miss_rec,    \
-                     n_max, logits, k, flags, topk_idx, topk_w, l.key_base)
+                     n_max, logits, k, flags, topk_idx, topk_w, l.key_base, logit_out)
     if (E_route <= 64) W(1);
     else if (E_route <= 256) W(4);
     else W(16);
@@ -476,7 +484,7 @@ hipError_t launch_lru_lookup_topk(const moe_lru& l, const float* logits, int E_r
 #define L(NV)                                                                                           \
   hipLaunchKernelGGL(k_lru_lookup<NV>, dim3(1), dim3(kThreads), 0, s, l.E, l.S, l.slot_expert,          \
                      l.expert_slot, l.slot_stamp, l.clock, nullptr, T * k, pair_slot, pair_order, miss_rec, \
-                     n_max, logits, k, flags, topk_idx, topk_w, l.key_base, E_route)
+                     n_max, logits, k, flags, topk_idx, topk_w, l.key_base, E_route, logit_out)
   if (E_route <= 64) L(1);
   else if (E_route <= 256) L(4);
   else L(16);
@@ -514,8 +522,8 @@ __global__ __launch_bounds__(256) void k_cache_fill(const int32_t* __restrict__ 
 }  // namespace
 
 hipError_t launch_cache_fill(const int32_t* miss_rec, const uint8_t* host_pool, uint8_t* slot_pool,
-                             size_t expert_bytes, size_t stride, hipStream_t s) {
-  hipLaunchKernelGGL(k_cache_fill, dim3(512), dim3(256), 0, s, miss_rec, host_pool, slot_pool, expert_bytes,
+                             size_t expert_bytes, size_t stride, hipStream_t s, int n_groups) {
+  hipLaunchKernelGGL(k_cache_fill, dim3(n_groups), dim3(256), 0, s, miss_rec, host_pool, slot_pool, expert_bytes,
                      stride);
   return hipGetLastError();
 }

@@ -685,11 +685,18 @@ int moe_cache_fill_device(const int32_t* miss_rec, const void* host_pool, void* 
   return MOE_OK;
 }
 
-int moe_cached_layer_enqueue(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
-                             const moe_cached_layer* L, const uint16_t* x, int T, int32_t* topk_idx,
-                             float* topk_w, int32_t* pair_slot, int32_t* pair_order, uint16_t* out, void* ws,
-                             size_t ws_bytes, moe_stream_t stream) {
-  g_err[0] = 0;
+namespace {
+// Optional predictive prefetch of one cached decode layer (T = 1).
+struct PrefetchArgs {
+  int m;
+  uint8_t* buf;
+  hipStream_t stream;
+};
+
+int cached_enqueue(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                   const moe_cached_layer* L, const uint16_t* x, int T, int32_t* topk_idx, float* topk_w,
+                   int32_t* pair_slot, int32_t* pair_order, uint16_t* out, void* ws, size_t ws_bytes,
+                   moe_stream_t stream, const PrefetchArgs* pf) {
   if (!L || !L->router || !L->host_pool || !L->slot_pool || !L->miss_rec)
     return fail(MOE_E_ARG, "incomplete moe_cached_layer");
   int st = check_shape(fmt, H, F);
@@ -719,11 +726,31 @@ int moe_cached_layer_enqueue(int fmt, size_t stride, int H, int F, int E, int k,
     r.T = T; r.H = H; r.E = E; r.k = k;
     route_ws_carve(r, route_ws);
     if (!aligned(x, 16) || !aligned(L->router, 16)) return fail(MOE_E_ARG, "x and router must be 16-byte aligned");
+    float* keep = pf ? reinterpret_cast<float*>(pf->buf) : nullptr;  // the logits, for the prefetch step
     hipError_t e = launch_router_logits(x, L->router, T, H, E, r.logits, s);
     if (e == hipSuccess)
       e = launch_lru_lookup_topk(L->lru, r.logits, E, T, k, route_flags, topk_idx, topk_w, pair_slot, pair_order,
-                                 L->miss_rec, T * k < L->lru.S ? T * k : L->lru.S, s);
+                                 L->miss_rec, T * k < L->lru.S ? T * k : L->lru.S, s, keep);
     if (e != hipSuccess) return hip_fail(e, "cached layer (route + lookup)");
+    if (pf) {
+      // on the prefetch stream, after this lookup: one more LRU step over the
+      // token's top-(k+m) experts in rank order (the routed k are hits and keep
+      // their slots; runner-ups that miss take victims), then the copy of those
+      // blobs from the host pool, overlapping this stream's work
+      const int kp = k + pf->m, n_max = kp < L->lru.S ? kp : L->lru.S;
+      int32_t* rec = reinterpret_cast<int32_t*>(pf->buf + align256((size_t)E * 4));
+      int32_t* dummy = reinterpret_cast<int32_t*>(pf->buf + align256((size_t)E * 4) +
+                                                  align256((size_t)(5 + 2 * n_max) * 4));
+      e = hipEventRecord(static_cast<hipEvent_t>(L->lookup_done), s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(pf->stream, static_cast<hipEvent_t>(L->lookup_done), 0);
+      if (e == hipSuccess)
+        e = launch_lru_lookup_topk(L->lru, keep, E, 1, kp, route_flags, dummy, reinterpret_cast<float*>(dummy + 16),
+                                   dummy + 32, dummy + 48, rec, n_max, pf->stream);
+      if (e == hipSuccess)
+        e = launch_cache_fill(rec, static_cast<const uint8_t*>(L->host_pool), static_cast<uint8_t*>(L->slot_pool),
+                              moe_expert_bytes(fmt, H, F), stride, pf->stream, 32);
+      if (e != hipSuccess) return hip_fail(e, "cached layer (prefetch)");
+    }
   } else {
     st = moe_route(x, L->router, T, H, E, k, route_flags, topk_idx, topk_w, nullptr, nullptr, route_ws,
                    route_bytes, stream);
@@ -745,4 +772,40 @@ int moe_cached_layer_enqueue(int fmt, size_t stride, int H, int F, int E, int k,
   hipError_t e = launch_ffn_gemv_split(a, 3, 4, s);
   // (the combine is fused into the down kernel, or follows it guarded by the record)
   return e == hipSuccess ? MOE_OK : hip_fail(e, "cached layer (experts)");
+}
+}  // namespace
+
+int moe_cached_layer_enqueue(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                             const moe_cached_layer* L, const uint16_t* x, int T, int32_t* topk_idx,
+                             float* topk_w, int32_t* pair_slot, int32_t* pair_order, uint16_t* out, void* ws,
+                             size_t ws_bytes, moe_stream_t stream) {
+  g_err[0] = 0;
+  return cached_enqueue(fmt, stride, H, F, E, k, route_flags, L, x, T, topk_idx, topk_w, pair_slot, pair_order, out,
+                        ws, ws_bytes, stream, nullptr);
+}
+
+size_t moe_prefetch_buffer_bytes(int E, int k, int m, int S) {
+  if (E < 1 || E > 1024 || k < 1 || m < 1 || k + m > 16 || S < 1) return 0;
+  const int n_max = k + m < S ? k + m : S;
+  return align256((size_t)E * 4) + align256((size_t)(5 + 2 * n_max) * 4) + 256;
+}
+
+size_t moe_prefetch_record_offset(int E) { return E < 1 ? 0 : align256((size_t)E * 4); }
+
+int moe_cached_layer_enqueue_prefetch(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                                      const moe_cached_layer* L, const uint16_t* x, int T, int32_t* topk_idx,
+                                      float* topk_w, int32_t* pair_slot, int32_t* pair_order, uint16_t* out,
+                                      void* ws, size_t ws_bytes, int m, void* pf_buf, size_t pf_bytes,
+                                      moe_stream_t stream, moe_stream_t pf_stream) {
+  g_err[0] = 0;
+  if (T != 1) return fail(MOE_E_ARG, "prefetch runs one token per step (T=%d)", T);
+  if (m < 1 || k + m > 16) return fail(MOE_E_ARG, "m=%d: need 1 <= m and k + m <= 16", m);
+  if (!L || !L->lookup_done) return fail(MOE_E_ARG, "the layer needs its lookup_done event");
+  if (!pf_stream || pf_stream == stream) return fail(MOE_E_ARG, "pf_stream must be a second stream");
+  const size_t need = moe_prefetch_buffer_bytes(E, k, m, L->lru.S);
+  if (!need || !pf_buf || !aligned(pf_buf, 256) || pf_bytes < need)
+    return fail(MOE_E_WORKSPACE, "prefetch buffer needs %zu bytes, 256-aligned", need);
+  PrefetchArgs pf{m, static_cast<uint8_t*>(pf_buf), static_cast<hipStream_t>(pf_stream)};
+  return cached_enqueue(fmt, stride, H, F, E, k, route_flags, L, x, T, topk_idx, topk_w, pair_slot, pair_order, out,
+                        ws, ws_bytes, stream, &pf);
 }

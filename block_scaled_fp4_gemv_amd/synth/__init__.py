@@ -171,6 +171,15 @@ def router(seed, cfg, layer, E, H, std=0.05) -> np.ndarray:
     return normal(st, E * H, 0.0, std).reshape(E, H)
 
 
+def router_skewed(seed, cfg, layer, E, H, sigma, std=0.05) -> np.ndarray:
+    """router() with row e scaled by exp(sigma * g_e), g_e ~ N(0, 1) from its own
+    stream: larger sigma concentrates a layer's routing on fewer experts (a
+    smaller working set), sigma = 0 is router() itself."""
+    g = normal(stream(seed, cfg, KIND_ROUTER, layer, 0, 1), E)
+    r = router(seed, cfg, layer, E, H, std)
+    return (r * np.exp(sigma * g)[:, None]).astype(np.float32)
+
+
 def token_row(seed, cfg, t, H, attempt=0, std=1.0) -> np.ndarray:
     """bf16 row t of an i.i.d. N(0, std^2) token batch (redrawn with attempt+1)."""
     return normal_bf16(stream(seed, cfg, KIND_X, 0, t, 0, attempt), H, 0.0, std)

@@ -426,6 +426,42 @@ int moe_cached_layer_enqueue(int fmt, size_t stride, int H, int F, int E, int k,
                              int32_t* topk_idx, float* topk_w, int32_t* pair_slot, int32_t* pair_order,
                              uint16_t* out, void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* moe_cached_layer_enqueue with predictive prefetch (T = 1): the gate's
+ * output names the experts that come next, and they are copied in ahead of use
+ * while the current step computes (page "FreeToken：753B大模型塞进单卡的本地部署
+ * 硬件账该怎么算", section "按带宽动态分配参数存储": routing-aware asynchronous
+ * copies on streams; prefetch accuracy is one of the validation dimensions the
+ * same page lists).  The pages give no predictor; this one takes the token's
+ * runner-up experts, ranks k .. k+m-1 of the same logits.  After the layer's
+ * lookup on `stream`, the call records layer->lookup_done there, makes
+ * pf_stream wait on it and enqueues on pf_stream:
+ *   - one more LRU step of the layer's cache over the token's top-(k+m)
+ *     experts in rank order: the routed k are hits (restamped in that order),
+ *     a runner-up that misses takes a victim by the usual rule (never a slot
+ *     this step requested) and is stamped after them;
+ *   - a device copy of those runner-ups' blobs from the host pool into their
+ *     victim slots (a few workgroups, so that it overlaps `stream`'s work).
+ * The routed work on `stream` is moe_cached_layer_enqueue's, so topk_idx,
+ * topk_w and `out` are those of moe_layer_forward bit for bit.  The caller
+ * must make `stream` wait for pf_stream before this layer's next call (e.g.
+ * once per decode step) and must not run another call on this layer's cache
+ * meanwhile.
+ *   m       runner-ups per token, 1 <= m, k + m <= 16
+ *   pf_buf  device, moe_prefetch_buffer_bytes(E, k, m, S) bytes, 256-aligned,
+ *           one per layer: a copy of the step's logits, then at byte
+ *           moe_prefetch_record_offset(E) the prefetch step's miss record
+ *           (moe_miss_record_words(1, k+m, S) words; its misses are the
+ *           prefetched experts), then scratch.
+ * Errors as moe_cached_layer_enqueue, plus MOE_E_ARG for T != 1, a bad m, a
+ * missing lookup_done event or pf_stream == stream, and MOE_E_WORKSPACE. */
+size_t moe_prefetch_buffer_bytes(int E, int k, int m, int S);
+size_t moe_prefetch_record_offset(int E);
+int moe_cached_layer_enqueue_prefetch(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                                      const moe_cached_layer* layer, const uint16_t* x, int T, int32_t* topk_idx,
+                                      float* topk_w, int32_t* pair_slot, int32_t* pair_order, uint16_t* out,
+                                      void* ws, size_t ws_bytes, int m, void* pf_buf, size_t pf_bytes,
+                                      moe_stream_t stream, moe_stream_t pf_stream);
+
 /* ------------------------------------------- prefill with streamed experts */
 
 /* Workspace bytes for moe_prefill_streamed (device, 256-byte aligned): one
