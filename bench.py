@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--cache-elastic-steps", type=int, default=64,
                    help="after the timed cache steps: resize every layer's slot cache (half in place, then "
                         "1.5x into new pools) and run this many steps after each resize (0 = skip)")
+    p.add_argument("--cache-prefetch-steps", type=int, default=96,
+                   help="steps of each runner-up prefetch run on the cache workload (m = 2, 4; 0 = skip)")
     p.add_argument("--cache-shared-steps", type=int, default=96,
                    help="steps of the cross-layer cache comparison (per-layer vs shared pools on a trace with "
                         "unequal demand; 0 = skip)")
@@ -316,6 +318,94 @@ def cache_shared_leg(fmt, hosts, stride, warmup, steps, group=4):
             "warmup_steps": warmup, "timed_steps": steps, **res,
             "miss_reduction": round(1 - res["shared"]["misses_per_token"] /
                                     max(res["per_layer"]["misses_per_token"], 1e-9), 4)}
+
+
+def cache_prefetch_leg(fmt, hosts, routers, stride, warmup, steps, ms=(2, 4)):
+    """Predictive prefetch on the cache35b decode (moe_cached_layer_enqueue_prefetch):
+    for each m, the 40-layer step with every layer's runner-up experts (ranks
+    k..k+m-1) prefetched on a second stream (one HIP graph per step, the
+    prefetch stream joined at its end).  Reports tok/s, the routed hit rate,
+    blobs moved over PCIe per token (routed misses + prefetches) and prefetch
+    accuracy: the share of prefetched experts that the same layer routes to at
+    the next step."""
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_gemv_amd import binding as B
+    from block_scaled_fp4_gemv_amd import synth as sy
+
+    wl = sy.WORKLOADS["cache35b"]
+    H, E, F, k, S = wl.H, wl.E, wl.F, wl.k, wl.slots
+    n_layers = len(hosts)
+    xs = torch.from_numpy(sy.ar1_sequence(0, wl.cfg_id, warmup + steps, H)).cuda()
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((n_layers, 1, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    pair_slot = torch.empty(k, dtype=torch.int32, device="cuda")
+    pair_order = torch.empty(k, dtype=torch.int32, device="cuda")
+    out = torch.empty((1, H), dtype=torch.uint16, device="cuda")
+    xbuf = torch.empty((1, H), dtype=torch.uint16, device="cuda")
+    eb = B.moe_expert_bytes(fmt, H, F)
+    pf = torch.cuda.Stream()
+    runs = []
+    for m in ms:
+        layers = [B.CachedLayer(routers[l], hosts[l], torch.zeros(S * stride, dtype=torch.uint8, device="cuda"),
+                                E, S, 1, k, rec_on_device=True) for l in range(n_layers)]
+        bufs = [B.new_prefetch_buffer(E, k, m, S) for _ in range(n_layers)]
+        precs = [B.prefetch_record(b, E, k, m, S) for b in bufs]
+        nw = B.moe_miss_record_words(1, k + m, S)
+
+        def enqueue():
+            main = torch.cuda.current_stream()
+            pf.wait_stream(main)
+            for l, L in enumerate(layers):
+                B.moe_cached_layer_enqueue_prefetch(fmt, stride, H, F, E, k, L, xbuf, idx[l], w, pair_slot,
+                                                    pair_order, out, ws, m, bufs[l], pf)
+            main.wait_stream(pf)
+
+        for t in range(warmup):
+            xbuf.copy_(xs[t:t + 1])
+            enqueue()
+        torch.cuda.synchronize()
+        g_ = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_):
+            enqueue()
+        torch.cuda.synchronize()
+        recs, pfr, routed = [], [], []
+        t0 = time.perf_counter()
+        for t in range(warmup, warmup + steps):
+            xbuf.copy_(xs[t:t + 1])
+            g_.replay()
+            recs.append(torch.stack([L.miss_rec[:4] for L in layers]))
+            pfr.append(torch.stack([pr[:nw] for pr in precs]))
+            routed.append(idx[:, 0, :].clone())
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        r = torch.stack(recs).cpu().numpy()
+        q = torch.stack(pfr).cpu().numpy()
+        ro = torch.stack(routed).cpu().numpy()
+        assert (r[:, :, 0] == 0).all() and (q[:, :, 0] == 0).all(), "cache capacity error"
+        fetched = used = 0
+        for t in range(steps - 1):
+            for l in range(n_layers):
+                n = int(q[t, l, 1])
+                got = set(int(e) for e in q[t, l, 5:5 + n])
+                fetched += n
+                used += len(got & set(int(e) for e in ro[t + 1, l]))
+        misses, pref = float(r[:, :, 1].sum()), float(q[:, :, 1].sum())
+        runs.append({"m": m, "tokens_per_s": round(steps / dt, 2),
+                     "hit_rate": round(float(r[:, :, 3].sum()) / (steps * n_layers * k), 4),
+                     "routed_misses_per_token": round(misses / steps, 2),
+                     "prefetched_per_token": round(pref / steps, 2),
+                     "blobs_over_pcie_per_token": round((misses + pref) / steps, 2),
+                     "prefetch_accuracy": round(used / max(fetched, 1), 4),
+                     "h2d_GBps": round((misses + pref) * eb / dt / 1e9, 2)})
+        del layers, bufs
+        torch.cuda.empty_cache()
+    return {"workload": f"cache35b: {n_layers} layers, {S} VRAM slots per layer, batch 1; runner-up prefetch",
+            "executor": "moe_cached_layer_enqueue_prefetch x 40 layers in one HIP graph (prefetch stream joined "
+                        "at the end of the step)",
+            "warmup_steps": warmup, "timed_steps": steps, "runs": runs}
 
 
 def algorithmic_bytes(wl, fmt):
@@ -673,6 +763,11 @@ def main():
                                  host_sync=args.cache_host_sync, elastic_steps=args.cache_elastic_steps)
         log(f"cache: {res['cache']['tokens_per_s']} tok/s, hit rate {res['cache']['hit_rate']}, "
             f"{res['cache']['h2d_GBps']} GB/s H2D")
+        if args.cache_prefetch_steps > 0:
+            log("cache prefetch leg ...")
+            res["cache_prefetch"] = cache_prefetch_leg(fmt, hosts, routers, stride, args.cache_warmup,
+                                                       args.cache_prefetch_steps)
+            log(f"cache prefetch: {res['cache_prefetch']['runs']}")
         if args.cache_shared_steps > 0:
             log("shared-cache leg ...")
             res["cache_shared"] = cache_shared_leg(fmt, hosts, stride, args.cache_warmup, args.cache_shared_steps)
