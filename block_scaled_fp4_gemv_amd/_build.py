@@ -36,8 +36,15 @@ def build_synth():
     os.replace(tmp, SYNTH_LIB)
 
 
+def host_sources():
+    """Plain host C++ (no HIP), built by the host compiler with OpenMP."""
+    return sorted(glob.glob(os.path.join(CSRC, "*_host.cpp")))
+
+
 def hip_sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    host = set(host_sources())
+    return sorted(s for s in glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp"))
+                  if s not in host)
 
 
 def build_moe(jobs=8):
@@ -60,8 +67,13 @@ def build_moe(jobs=8):
     for p in procs:
         if p.wait() != 0:
             raise RuntimeError("hipcc failed")
+    for s in host_sources():
+        o = os.path.join(objdir, os.path.basename(s) + ".o")
+        objs.append(o)
+        _run(["g++", "-c", s, "-o", o, "-O3", "-mavx2", "-mfma", "-fopenmp", "-fPIC", "-std=c++17", "-I", INCLUDE,
+              "-Wall"])
     tmp = MOE_LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs + ["-lgomp"])
     os.replace(tmp, MOE_LIB)
 
 

@@ -71,6 +71,14 @@ SIGNATURES = {
                                         ctypes.POINTER(moe_cached_layer), _vp, _i32, _vp, _vp, _vp, _vp,
                                         _vp, _vp, _sz, _vp, _vp, ctypes.POINTER(ctypes.c_int32),
                                         ctypes.POINTER(ctypes.c_int32)]),
+    "moe_host_expert_ffn": (_i32, [_i32, _i32, _i32, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                   ctypes.POINTER(_vp), _vp, _i32]),
+    "moe_cached_layer_split_host_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "moe_cached_layer_forward_split": (_i32, [_i32, _sz, _i32, _i32, _i32, _i32, _u32,
+                                              ctypes.POINTER(moe_cached_layer), _vp, _i32, _vp, _vp, _vp, _vp,
+                                              _vp, _vp, _sz, _vp, _vp, ctypes.c_float, _vp, _sz, _i32, _vp,
+                                              ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                              ctypes.POINTER(ctypes.c_int32)]),
     "moe_prefetch_buffer_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "moe_prefetch_record_offset": (_sz, [_i32]),
     "moe_cached_layer_enqueue_prefetch": (_i32, [_i32, _sz, _i32, _i32, _i32, _i32, _u32,
@@ -457,6 +465,29 @@ def moe_cached_layer_forward(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w
     return hits.value, miss.value
 
 
+def new_split_host_workspace(T, H, F, k):
+    import torch
+    return torch.zeros(int(lib().moe_cached_layer_split_host_bytes(T, H, F, k)), dtype=torch.uint8).pin_memory()
+
+
+def moe_cached_layer_forward_split(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w, pair_slot, pair_order, out,
+                                   ws, q, host_ws, defer_done, threads=8, flags=0, stream=None, copy_stream=None):
+    """The host-waiting cached layer with a share q of the misses computed on the
+    CPU; returns (n_hits, n_miss, n_cpu)."""
+    T = x.shape[0]
+    if not defer_done.cuda_event:  # torch creates the HIP event at its first record
+        defer_done.record()
+    hits, miss, cpu = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    st = lib().moe_cached_layer_forward_split(fmt, stride, H, F, E, k, flags, ctypes.byref(layer.c), _ptr(x), T,
+                                              _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
+                                              _ptr(out), _ptr(ws), ws.numel(), _stream(stream), _stream(copy_stream),
+                                              float(q), _ptr(host_ws), host_ws.numel(), threads,
+                                              defer_done.cuda_event, ctypes.byref(hits), ctypes.byref(miss),
+                                              ctypes.byref(cpu))
+    _check(st, "moe_cached_layer_forward_split")
+    return hits.value, miss.value, cpu.value
+
+
 def moe_cache_fill_device(miss_rec, host_pool, slot_pool, expert_bytes, stride, record_ready=None,
                           slots_free=None, copy_stream=None, fill_done=None):
     ev = lambda e: None if e is None else e.cuda_event  # noqa: E731
@@ -474,6 +505,20 @@ def moe_cached_layer_enqueue(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w
                                         _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
                                         _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_cached_layer_enqueue")
+
+
+def moe_host_expert_ffn(fmt, H, F, blobs, xs, threads=8):
+    """Host expert FFNs: blobs (uint8 numpy/pinned arrays, one per pair), xs (bf16
+    uint16 [H] rows) -> ys float32 [n, H]."""
+    n = len(blobs)
+    ys = np.zeros((n, H), np.float32)
+    scratch = np.zeros(max(1, n * (H + F)), np.float32)
+    xs = [np.ascontiguousarray(x, dtype=np.uint16) for x in xs]
+    arr = lambda items: (_vp * max(1, n))(*[_ptr(a) for a in items])  # noqa: E731
+    st = lib().moe_host_expert_ffn(fmt, H, F, n, arr(blobs), arr(xs), arr([ys[i] for i in range(n)]),
+                                   _ptr(scratch), threads)
+    _check(st, "moe_host_expert_ffn")
+    return ys
 
 
 def moe_prefetch_buffer_bytes(E, k, m, S):

@@ -660,6 +660,168 @@ int moe_cached_layer_forward(int fmt, size_t stride, int H, int F, int E, int k,
   return moe_combine(y, topk_w, T, H, k, out, stream);
 }
 
+size_t moe_cached_layer_split_host_bytes(int T, int H, int F, int k) {
+  if (T < 0 || k < 1 || H < 1 || F < 1) return 0;
+  const size_t n = (size_t)T * k;
+  return align256((size_t)T * H * 2) + align256(n * 4) * 2 + align256(n * H * 4) + align256(n * (H + F) * 4);
+}
+
+int moe_cached_layer_forward_split(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                                   const moe_cached_layer* L, const uint16_t* x, int T, int32_t* topk_idx,
+                                   float* topk_w, int32_t* pair_slot, int32_t* pair_order, uint16_t* out,
+                                   void* ws, size_t ws_bytes, moe_stream_t stream, moe_stream_t copy_stream,
+                                   float q, void* host_ws, size_t host_ws_bytes, int n_threads,
+                                   moe_event_t defer_done, int32_t* n_hits, int32_t* n_miss, int32_t* n_cpu) {
+  g_err[0] = 0;
+  if (!L || !L->router || !L->host_pool || !L->slot_pool || !L->miss_rec || !L->lookup_done || !L->fill_done)
+    return fail(MOE_E_ARG, "incomplete moe_cached_layer (needs its lookup_done and fill_done events)");
+  if (!(q >= 0.0f && q <= 1.0f)) return fail(MOE_E_ARG, "q=%g outside [0, 1]", q);
+  if (!defer_done || !copy_stream || copy_stream == stream)
+    return fail(MOE_E_ARG, "needs a defer_done event and a copy stream other than stream");
+  {
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, L->miss_rec) == hipSuccess && at.type == hipMemoryTypeDevice)
+      return fail(MOE_E_ARG, "miss_rec is device memory; the split executor reads it on the host");
+    (void)hipGetLastError();
+  }
+  const size_t need = moe_cached_layer_workspace(fmt, T, H, F, k, E);
+  if (!need) return fail(MOE_E_ARG, "bad shape or format");
+  if (!ws || !aligned(ws, 256) || ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "cached layer workspace needs %zu bytes, 256-aligned", need);
+  const size_t hneed = moe_cached_layer_split_host_bytes(T, H, F, k);
+  if (!host_ws || !aligned(host_ws, 256) || host_ws_bytes < hneed)
+    return fail(MOE_E_WORKSPACE, "host workspace needs %zu bytes of pinned memory, 256-aligned", hneed);
+  if (T == 0) return MOE_OK;
+  if (T * k > 64) return fail(MOE_E_ARG, "the split executor takes at most 64 pairs per step (T=%d k=%d)", T, k);
+  hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(copy_stream);
+  const int n_pairs = T * k;
+  // host workspace: x, topk_idx, the GPU-served missed pairs, y of the CPU pairs, scratch
+  uint8_t* hp = static_cast<uint8_t*>(host_ws);
+  uint16_t* hx = reinterpret_cast<uint16_t*>(hp);
+  hp += align256((size_t)T * H * 2);
+  int32_t* hidx = reinterpret_cast<int32_t*>(hp);
+  hp += align256((size_t)n_pairs * 4);
+  int32_t* hsub = reinterpret_cast<int32_t*>(hp);
+  hp += align256((size_t)n_pairs * 4);
+  float* hy = reinterpret_cast<float*>(hp);
+  hp += align256((size_t)n_pairs * H * 4);
+  float* hscr = reinterpret_cast<float*>(hp);
+  // device workspace: y, routing, then the expert FFN's
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  float* y = reinterpret_cast<float*>(p);
+  p += align256((size_t)n_pairs * H * 4);
+  const size_t route_bytes = moe_route_workspace(T, H, E, k);
+  void* route_ws = p;
+  p += align256(route_bytes);
+  void* ffn_ws = p;
+  const size_t ffn_bytes = moe_ffn_workspace(fmt, T, H, F, k, E);
+  // the previous call's deferred fills land before anything reads the slots
+  hipError_t e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(defer_done), 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(defer_done)");
+  int st = moe_route(x, L->router, T, H, E, k, route_flags, topk_idx, topk_w, nullptr, nullptr, route_ws,
+                     route_bytes, stream);
+  if (st) return st;
+  e = hipMemcpyAsync(hidx, topk_idx, (size_t)n_pairs * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(hx, x, (size_t)T * H * 2, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "split: copies to the host");
+  st = moe_cache_lookup(&L->lru, topk_idx, T, k, pair_slot, pair_order, L->miss_rec, stream);
+  if (st) return st;
+  hipEvent_t lk = static_cast<hipEvent_t>(L->lookup_done);
+  e = hipEventRecord(lk, s);
+  if (e == hipSuccess) e = hipEventSynchronize(lk);
+  if (e != hipSuccess) return hip_fail(e, "lookup event");
+  const int32_t* rec = L->miss_rec;
+  if (rec[0] != MOE_OK) return fail(MOE_E_CAPACITY, "layer cache: %d misses exceed the evictable slots", rec[1]);
+  const int nm = rec[1], n_max = rec[4], n_hit = rec[2];
+  const int nc = (int)(q * (float)nm);  // the last nc distinct misses go to the CPU
+  if (n_hits) *n_hits = rec[3];
+  if (n_miss) *n_miss = nm;
+  if (n_cpu) *n_cpu = nc;
+  const size_t eb = moe_expert_bytes(fmt, H, F);
+  const uint8_t* hpool = static_cast<const uint8_t*>(L->host_pool);
+  uint8_t* spool = static_cast<uint8_t*>(L->slot_pool);
+  // the copy stream: the GPU-served fills, fill_done, then the CPU-served
+  // experts' fills (they still enter the cache), defer_done
+  if (L->slots_free) {
+    e = hipStreamWaitEvent(cs, static_cast<hipEvent_t>(L->slots_free), 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(slots_free)");
+  }
+  for (int r = 0; r < nm; ++r) {
+    if (r == nm - nc) {
+      e = hipEventRecord(static_cast<hipEvent_t>(L->fill_done), cs);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord(fill_done)");
+    }
+    e = hipMemcpyAsync(spool + (size_t)rec[5 + n_max + r] * stride, hpool + (size_t)rec[5 + r] * stride, eb,
+                       hipMemcpyHostToDevice, cs);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(fill)");
+  }
+  if (nc == 0) {
+    e = hipEventRecord(static_cast<hipEvent_t>(L->fill_done), cs);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(fill_done)");
+  }
+  e = hipEventRecord(static_cast<hipEvent_t>(defer_done), cs);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(defer_done)");
+  // the hit pairs on the GPU meanwhile
+  if (n_hit > 0) {
+    st = moe_expert_ffn(fmt, L->slot_pool, stride, H, F, E, x, T, k, topk_idx, pair_slot, nullptr, nullptr,
+                        pair_order, n_hit, nullptr, y, nullptr, MOE_FFN_GEMV, ffn_ws, ffn_bytes, stream);
+    if (st) return st;
+  }
+  // which missed pairs the GPU computes (expert among the first nm - nc misses)
+  auto cpu_served = [&](int ex) {
+    for (int r = nm - nc; r < nm; ++r)
+      if (rec[5 + r] == ex) return true;
+    return false;
+  };
+  auto resident = [&](int ex) {
+    for (int r = 0; r < nm; ++r)
+      if (rec[5 + r] == ex) return false;
+    return true;
+  };
+  int n_gpu_miss = 0, n_cpu_pairs = 0;
+  for (int qp = 0; qp < n_pairs; ++qp) {
+    const int ex = hidx[qp];
+    if (resident(ex)) continue;
+    if (cpu_served(ex)) ++n_cpu_pairs;
+    else hsub[n_gpu_miss++] = qp;
+  }
+  e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(L->fill_done), 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(fill_done)");
+  if (n_gpu_miss > 0) {
+    // the list sits in pinned host memory, which the kernel reads directly; the
+    // next call rewrites it only after its own lookup, i.e. after this kernel
+    st = moe_expert_ffn(fmt, L->slot_pool, stride, H, F, E, x, T, k, topk_idx, pair_slot, nullptr, nullptr,
+                        hsub, n_gpu_miss, nullptr, y, nullptr, MOE_FFN_GEMV, ffn_ws, ffn_bytes, stream);
+    if (st) return st;
+  }
+  if (L->slots_free) {
+    e = hipEventRecord(static_cast<hipEvent_t>(L->slots_free), s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(slots_free)");
+  }
+  // the CPU-served pairs on this thread, from the pinned blobs, while the GPU works
+  if (n_cpu_pairs > 0) {
+    const void* blobs[64];
+    const uint16_t* xs[64];
+    float* ys[64];
+    int qs[64], n = 0;
+    for (int qp = 0; qp < n_pairs && n < 64; ++qp) {
+      const int ex = hidx[qp];
+      if (resident(ex) || !cpu_served(ex)) continue;
+      blobs[n] = hpool + (size_t)ex * stride;
+      xs[n] = hx + (size_t)(qp / k) * H;
+      ys[n] = hy + (size_t)n * H;
+      qs[n++] = qp;
+    }
+    st = moe_host_expert_ffn(fmt, H, F, n, blobs, xs, ys, hscr, n_threads);
+    if (st) return fail(st, "host expert FFN");
+    for (int i = 0; i < n; ++i) {
+      e = hipMemcpyAsync(y + (size_t)qs[i] * H, ys[i], (size_t)H * 4, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(y)");
+    }
+  }
+  return moe_combine(y, topk_w, T, H, k, out, stream);
+}
+
 int moe_cache_fill_device(const int32_t* miss_rec, const void* host_pool, void* slot_pool,
                           size_t expert_bytes, size_t stride, moe_event_t record_ready,
                           moe_event_t slots_free, moe_stream_t copy_stream, moe_event_t fill_done) {

@@ -462,6 +462,62 @@ int moe_cached_layer_enqueue_prefetch(int fmt, size_t stride, int H, int F, int 
                                       void* ws, size_t ws_bytes, int m, void* pf_buf, size_t pf_bytes,
                                       moe_stream_t stream, moe_stream_t pf_stream);
 
+/* ------------------------------------------- host (CPU) experts: the q split */
+
+/* Expert FFNs computed on the host CPU from blobs in host memory, for the
+ * decode scheduler's split of a step's cache misses between GPU cache fills and
+ * CPU compute (page "8GB 笔记本 39.3 tok/s、单卡跑 753B：FreeToken 把 frontier
+ * MoE 拉回本地", section "设计核心", bandwidth-adaptive execution: the split
+ * follows the measured PCIe and host-memory bandwidths).  For pair i:
+ *   h = bf16( silu(G x_i) * (U x_i) ),   ys[i] = D h     (fp32 accumulation)
+ * with the weights of blobs[i] (one packed blob, the layout moe_expert_bytes
+ * describes) decoded on the host.  Pure host code with OpenMP (n_threads
+ * threads); no HIP call.
+ *   blobs [host] n pointers to blobs; xs [host] n pointers to bf16 [H] rows;
+ *   ys [host] n pointers to float [H] outputs;
+ *   scratch [host] n * (H + F) floats.
+ * MOE_E_FORMAT, MOE_E_ARG (a NULL pointer, a bad shape or n < 0). */
+int moe_host_expert_ffn(int fmt, int H, int F, int n, const void* const* blobs, const uint16_t* const* xs,
+                        float* const* ys, float* scratch, int n_threads);
+
+/* moe_cached_layer_forward with a share q of each step's distinct misses
+ * computed on the host CPU instead of waiting for their fill (the decode
+ * scheduler's split, page "8GB 笔记本 39.3 tok/s、单卡跑 753B：FreeToken 把
+ * frontier MoE 拉回本地", section "设计核心": bandwidth-adaptive execution; the
+ * pages give no formula for the share, so the caller picks q, e.g. from the
+ * two measured bandwidths as B_host / (B_host + B_pcie)).
+ * Order: `stream` waits defer_done (the previous call's deferred fills) ->
+ * moe_route -> topk_idx and x copied to host_ws -> moe_cache_lookup -> record
+ * lookup_done and wait for it on the host.  Of the record's nm distinct
+ * misses, the last floor(q * nm) are CPU-served.  copy_stream: wait
+ * slots_free, one hipMemcpyAsync per GPU-served miss, record fill_done, then
+ * one per CPU-served miss (those experts still enter the cache), record
+ * defer_done.  `stream`: the hit pairs (GEMV), wait fill_done, the GPU-served
+ * missed pairs, record slots_free.  Meanwhile this thread computes the
+ * CPU-served pairs with moe_host_expert_ffn (n_threads threads) from the
+ * pinned host pool and copies their y rows to the device; then moe_combine.
+ * The LRU state follows moe_cache_lookup exactly (q never changes it).  The
+ * CPU-served pairs' y are the host kernel's (fp32 on the CPU), so `out` agrees
+ * with the resident layer within the output tolerance, bit for bit when no
+ * pair is CPU-served.
+ *   layer: needs lookup_done and fill_done events and a [pinned] miss record;
+ *   host_ws: [pinned] moe_cached_layer_split_host_bytes(T, H, F, k) bytes,
+ *            256-aligned; a later call may reuse it (each call waits for its own
+ *            lookup, which follows this call's work on `stream`);
+ *   defer_done: an event owned by the layer (recorded by each call).
+ *   n_hits, n_miss, n_cpu: [host] optional, the step's hits, distinct misses
+ *   and CPU-served misses.
+ * Errors as moe_cached_layer_forward, MOE_E_ARG for q outside [0, 1], more
+ * than 64 pairs (T * k), a missing event or stream == copy_stream,
+ * MOE_E_WORKSPACE. */
+size_t moe_cached_layer_split_host_bytes(int T, int H, int F, int k);
+int moe_cached_layer_forward_split(int fmt, size_t stride, int H, int F, int E, int k, unsigned route_flags,
+                                   const moe_cached_layer* layer, const uint16_t* x, int T, int32_t* topk_idx,
+                                   float* topk_w, int32_t* pair_slot, int32_t* pair_order, uint16_t* out,
+                                   void* ws, size_t ws_bytes, moe_stream_t stream, moe_stream_t copy_stream,
+                                   float q, void* host_ws, size_t host_ws_bytes, int n_threads,
+                                   moe_event_t defer_done, int32_t* n_hits, int32_t* n_miss, int32_t* n_cpu);
+
 /* ------------------------------------------- prefill with streamed experts */
 
 /* Workspace bytes for moe_prefill_streamed (device, 256-byte aligned): one
