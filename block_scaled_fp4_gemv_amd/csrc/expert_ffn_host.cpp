@@ -10,6 +10,7 @@
 // holding row l%16 and elements 32(l/16) .. +31 of the fragment's 128), fp32
 // accumulation.  Plain C++ compiled by the host compiler with OpenMP: rows of a
 // batch of pairs are shared among the threads.
+#include <immintrin.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -61,16 +62,79 @@ uint16_t f2bf16_rne(float f) {
 }
 
 // E4M3 (OCP "FN") and E2M1 values
-float e4m3f(uint32_t b) {
+float e4m3_value(uint32_t b) {
   const int e = (b >> 3) & 15, m = b & 7;
   const float v = e ? ldexpf(1.0f + m / 8.0f, e - 7) : ldexpf(m / 8.0f, -6);
   return (b & 0x80) ? -v : v;
 }
+// byte -> value tables: E4M3, and half of each E8M0 power of two (the FP4
+// table of fp4x32_dot2 decodes twice the E2M1 values)
+struct Tables {
+  float e4m3[256], e4m3_half[256], e8m0_half[256];
+  Tables() {
+    for (int b = 0; b < 256; ++b) {
+      e4m3[b] = e4m3_value(b);
+      e4m3_half[b] = 0.5f * e4m3[b];
+      e8m0_half[b] = 0.5f * ldexpf(1.0f, b - 127);  // b = 0: 2^-127, a subnormal, as the format defines
+    }
+  }
+};
+const Tables kTab;
+float e4m3f(uint32_t b) { return kTab.e4m3[b & 0xff]; }
 const float kE2M1[16] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f,
                          -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
 
+// 32 FP4 codes (16 bytes, element 2i in the low nibble of byte i) against 32
+// floats with AVX2: the two 16-element halves' dot products as 8-wide partial
+// sums, each carrying a factor 2 (the codes decode through a table of twice the
+// E2M1 values, which are small integers).
+inline void fp4x32_dot2(const uint8_t* c16, const float* x, __m256& half0, __m256& half1) {
+  const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(c16));
+  const __m128i m4 = _mm_set1_epi8(0x0F);
+  const __m128i lo = _mm_and_si128(raw, m4), hi = _mm_and_si128(_mm_srli_epi16(raw, 4), m4);
+  const __m128i lut = _mm_setr_epi8(0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12);
+  const __m128i v0 = _mm_shuffle_epi8(lut, _mm_unpacklo_epi8(lo, hi));  // elements 0..15
+  const __m128i v1 = _mm_shuffle_epi8(lut, _mm_unpackhi_epi8(lo, hi));  // elements 16..31
+  const __m256 f0 = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(v0));
+  const __m256 f1 = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(v0, 8)));
+  const __m256 f2 = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(v1));
+  const __m256 f3 = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(v1, 8)));
+  half0 = _mm256_fmadd_ps(f1, _mm256_loadu_ps(x + 8), _mm256_mul_ps(f0, _mm256_loadu_ps(x)));
+  half1 = _mm256_fmadd_ps(f3, _mm256_loadu_ps(x + 24), _mm256_mul_ps(f2, _mm256_loadu_ps(x + 16)));
+}
+
+inline float hsum8(__m256 v) {
+  __m128 s = _mm_add_ps(_mm256_castps256_ps128(v), _mm256_extractf128_ps(v, 1));
+  s = _mm_add_ps(s, _mm_movehl_ps(s, s));
+  s = _mm_add_ss(s, _mm_shuffle_ps(s, s, 1));
+  return _mm_cvtss_f32(s);
+}
+
+// Row n of an FP4 matrix [N][K] against xf[K], vectorized.
+float row_dot_fp4(int fmt, const uint8_t* codes, const uint8_t* scales, int K, int n, const float* xf) {
+  const int S = K / 128, g = n / 16, r = n % 16;
+  __m256 acc = _mm256_setzero_ps();
+  for (int s = 0; s < S; ++s) {
+    const size_t f = (size_t)g * S + s;
+    for (int q = 0; q < 4; ++q) {
+      const int l = 16 * q + r;
+      __m256 h0, h1;
+      fp4x32_dot2(codes + f * 1024 + (size_t)l * 16, xf + 128 * s + 32 * q, h0, h1);
+      if (fmt == MOE_FMT_NVFP4) {
+        const uint8_t* sc = scales + f * 128 + (size_t)l * 2;
+        acc = _mm256_fmadd_ps(h0, _mm256_set1_ps(kTab.e4m3_half[sc[0]]), acc);
+        acc = _mm256_fmadd_ps(h1, _mm256_set1_ps(kTab.e4m3_half[sc[1]]), acc);
+      } else {
+        acc = _mm256_fmadd_ps(_mm256_add_ps(h0, h1), _mm256_set1_ps(kTab.e8m0_half[scales[f * 64 + l]]), acc);
+      }
+    }
+  }
+  return hsum8(acc);
+}
+
 // Row n of matrix [N][K] (codes at `codes`, scales at `scales`) against xf[K].
 float row_dot(int fmt, const uint8_t* codes, const uint8_t* scales, int K, int n, const float* xf) {
+  if (fmt != MOE_FMT_FP8_E4M3) return row_dot_fp4(fmt, codes, scales, K, n, xf);
   const int S = K / 128, g = n / 16, r = n % 16;
   float acc = 0.0f;
   for (int s = 0; s < S; ++s) {
@@ -124,7 +188,8 @@ extern "C" int moe_host_expert_ffn(int fmt, int H, int F, int n, const void* con
 #pragma omp parallel num_threads(nt)
   {
 #pragma omp for schedule(static)
-    for (long i = 0; i < (long)n * H; ++i) xf[i] = bf16f(xs[i / H][i % H]);
+    for (int p = 0; p < n; ++p)
+      for (int i = 0; i < H; ++i) xf[(size_t)p * H + i] = bf16f(xs[p][i]);
     // gate/up rows of every pair, then the SwiGLU with h rounded to bf16
 #pragma omp for schedule(static)
     for (long i = 0; i < (long)n * F; ++i) {
