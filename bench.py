@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--cache-elastic-steps", type=int, default=64,
                    help="after the timed cache steps: resize every layer's slot cache (half in place, then "
                         "1.5x into new pools) and run this many steps after each resize (0 = skip)")
+    p.add_argument("--cache-split-steps", type=int, default=48,
+                   help="timed steps of each q run of the GPU-fill / CPU-expert miss split (0 = skip)")
+    p.add_argument("--cache-split-warmup", type=int, default=24)
     p.add_argument("--cache-prefetch-steps", type=int, default=96,
                    help="steps of each runner-up prefetch run on the cache workload (m = 2, 4; 0 = skip)")
     p.add_argument("--cache-shared-steps", type=int, default=96,
@@ -405,6 +408,81 @@ def cache_prefetch_leg(fmt, hosts, routers, stride, warmup, steps, ms=(2, 4)):
     return {"workload": f"cache35b: {n_layers} layers, {S} VRAM slots per layer, batch 1; runner-up prefetch",
             "executor": "moe_cached_layer_enqueue_prefetch x 40 layers in one HIP graph (prefetch stream joined "
                         "at the end of the step)",
+            "warmup_steps": warmup, "timed_steps": steps, "runs": runs}
+
+
+def cache_split_leg(fmt, hosts, routers, stride, warmup, steps, threads):
+    """The decode scheduler's split of each step's misses between GPU cache fills
+    and host CPU experts (moe_cached_layer_forward_split, host-waiting executor):
+    PCIe H2D bandwidth (one layer's pinned host pool copied to the device) and the
+    host expert kernel's blob bandwidth (moe_host_expert_ffn on 32 blobs of the
+    pinned pool) are measured first; q* = B_host / (B_host + B_pcie) is the share
+    that keeps both sides equally busy.  Then the 40-layer cache workload runs at
+    q = 0, q* and 0.5."""
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_gemv_amd import binding as B
+    from block_scaled_fp4_gemv_amd import synth as sy
+
+    wl = sy.WORKLOADS["cache35b"]
+    H, E, F, k, S = wl.H, wl.E, wl.F, wl.k, wl.slots
+    n_layers = len(hosts)
+    eb = B.moe_expert_bytes(fmt, H, F)
+    # PCIe H2D: one layer's pool
+    dev = torch.empty_like(hosts[0], device="cuda")
+    dev.copy_(hosts[0], non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        dev.copy_(hosts[0], non_blocking=True)
+    torch.cuda.synchronize()
+    b_pcie = 3 * hosts[0].numel() / (time.perf_counter() - t0)
+    del dev
+    # host expert kernel on blobs of the pinned pool
+    hp = hosts[0].numpy()
+    blobs = [hp[e * stride:e * stride + eb] for e in range(32)]
+    xh = sy.ar1_sequence(0, wl.cfg_id, 1, H)[0]
+    B.moe_host_expert_ffn(fmt, H, F, blobs, [xh] * 32, threads=threads)
+    t0 = time.perf_counter()
+    for _ in range(5):
+        B.moe_host_expert_ffn(fmt, H, F, blobs, [xh] * 32, threads=threads)
+    b_host = 5 * 32 * eb / (time.perf_counter() - t0)
+    q_star = b_host / (b_host + b_pcie)
+    xs = torch.from_numpy(sy.ar1_sequence(0, wl.cfg_id, warmup + steps, H)).cuda()
+    ws = torch.empty(B.moe_cached_layer_workspace(fmt, 1, H, F, k, E) + 256, dtype=torch.uint8, device="cuda")
+    hws = B.new_split_host_workspace(1, H, F, k)
+    bufs = [torch.empty(s_, dtype=d, device="cuda") for s_, d in
+            (((1, k), torch.int32), ((1, k), torch.float32), (k, torch.int32), (k, torch.int32), ((1, H), torch.uint16))]
+    copy = torch.cuda.Stream()
+    runs = []
+    for q in (0.0, round(q_star, 3), 0.5):
+        layers = [B.CachedLayer(routers[l], hosts[l], torch.zeros(S * stride, dtype=torch.uint8, device="cuda"),
+                                E, S, 1, k) for l in range(n_layers)]
+        defers = [torch.cuda.Event() for _ in range(n_layers)]
+        tot = np.zeros(3, np.int64)
+        for t in range(warmup + steps):
+            if t == warmup:
+                torch.cuda.synchronize()
+                tot[:] = 0
+                t0 = time.perf_counter()
+            x = xs[t:t + 1]
+            for l, L in enumerate(layers):
+                tot += B.moe_cached_layer_forward_split(fmt, stride, H, F, E, k, L, x, *bufs, ws, q, hws, defers[l],
+                                                        threads=threads, copy_stream=copy)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        runs.append({"q": q, "tokens_per_s": round(steps / dt, 2),
+                     "hit_rate": round(float(tot[0]) / (steps * n_layers * k), 4),
+                     "misses_per_token": round(float(tot[1]) / steps, 2),
+                     "cpu_served_per_token": round(float(tot[2]) / steps, 2)})
+        del layers
+        torch.cuda.empty_cache()
+    return {"workload": f"cache35b: {n_layers} layers, {S} VRAM slots per layer, batch 1; misses split between "
+                        f"GPU fills and host CPU experts",
+            "executor": "moe_cached_layer_forward_split per layer (host waits on each layer's miss record)",
+            "pcie_h2d_GBps": round(b_pcie / 1e9, 2), "host_expert_GBps": round(b_host / 1e9, 2),
+            "host_threads": threads, "q_star": round(q_star, 3),
             "warmup_steps": warmup, "timed_steps": steps, "runs": runs}
 
 
@@ -763,6 +841,11 @@ def main():
                                  host_sync=args.cache_host_sync, elastic_steps=args.cache_elastic_steps)
         log(f"cache: {res['cache']['tokens_per_s']} tok/s, hit rate {res['cache']['hit_rate']}, "
             f"{res['cache']['h2d_GBps']} GB/s H2D")
+        if args.cache_split_steps > 0:
+            log("cache split leg ...")
+            res["cache_split"] = cache_split_leg(fmt, hosts, routers, stride, args.cache_split_warmup,
+                                                 args.cache_split_steps, args.threads)
+            log(f"cache split: {res['cache_split']}")
         if args.cache_prefetch_steps > 0:
             log("cache prefetch leg ...")
             res["cache_prefetch"] = cache_prefetch_leg(fmt, hosts, routers, stride, args.cache_warmup,
