@@ -65,6 +65,9 @@ def parse():
     p.add_argument("--prefill-stream-reps", type=int, default=3,
                    help="streamed-prefill leg passes (0 = skip; runs with the cache leg's host pools)")
     p.add_argument("--fmt", type=int, default=0, help="override weight format (1 NVFP4, 2 MXFP4, 3 FP8)")
+    p.add_argument("--plain-router", action="store_true",
+                   help="prefill legs: pass the fp32 router (split into bf16 planes on every call) instead of a "
+                        "router prepared once per weight set")
     p.add_argument("--mx-native", action="store_true",
                    help="MXFP4 prefill on the native scaled MFMA (FP4 weights x two FP8 activation terms) instead "
                         "of bf16 MFMA with the weights dequantized in registers")
@@ -503,7 +506,7 @@ MX_NATIVE_INSTR = ("v_mfma_scale_f32_16x16x128_f8f6f4, FP4 weights x FP8 activat
                    "so the expert flops count twice in the instruction's own rate)")
 
 
-def prefill_leg(name, fmt_override, reps, threads, mx_native=False):
+def prefill_leg(name, fmt_override, reps, threads, mx_native=False, prepared_router=True):
     """Time moe_layer_forward over a T-token prefill of one layer (grouped MFMA path)."""
     import numpy as np
     import torch
@@ -524,8 +527,10 @@ def prefill_leg(name, fmt_override, reps, threads, mx_native=False):
         B.pack_layer(fmt, H, F, sy.experts(fmt, 0, wl.wcfg, l, 0, E, H, F, wl.w_std), host, stride,
                      threads=threads)
         pools.append(torch.from_numpy(host).cuda())
-        Rs.append(torch.from_numpy(sy.router(0, wl.wcfg, l, E, H)).cuda())
-        del host
+        R = torch.from_numpy(sy.router(0, wl.wcfg, l, E, H)).cuda()
+        # the router's bf16 split is made once per weight set, not per call
+        Rs.append(B.PreparedRouter(R) if prepared_router else R)
+        del host, R
     x = torch.from_numpy(sy.token_rows(0, wl.cfg_id, T, H)).cuda()
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
@@ -586,6 +591,8 @@ def prefill_leg(name, fmt_override, reps, threads, mx_native=False):
             "router_fp32_gflop": round(flops_router / 1e9, 2),
             "timing": f"moe_layer_forward captured in one HIP graph per weight set (two sets, replayed "
                       f"alternately); HIP events around each replay, median of {reps}",
+            "router": ("prepared once per weight set (moe_router_prepare: fp32 router + its bf16 split)"
+                       if prepared_router else "plain fp32 router (split into bf16 planes on every call)"),
             **({"role": f"compute-bound point: {T * k // E} rows per expert on average, "
                         f"{flops_mfma / bytes_alg:.0f} flop per algorithmic byte"} if name == "prefill35b_16k" else {})}
 
@@ -866,13 +873,15 @@ def main():
         log(f"prefill leg {args.prefill} ...")
         del pools
         torch.cuda.empty_cache()
-        res["prefill"] = prefill_leg(args.prefill, args.fmt, args.prefill_reps, args.threads, args.mx_native)
+        res["prefill"] = prefill_leg(args.prefill, args.fmt, args.prefill_reps, args.threads, args.mx_native,
+                                     prepared_router=not args.plain_router)
         log(f"prefill: {res['prefill']['layer_us']} us/layer, {res['prefill']['tokens_per_s']} tok/s")
         if args.prefill == "prefill35b" and args.compute_bound_reps > 0:
             log("compute-bound prefill point prefill35b_16k ...")
             torch.cuda.empty_cache()
             res["prefill_compute_bound"] = prefill_leg("prefill35b_16k", args.fmt, args.compute_bound_reps,
-                                                       args.threads, args.mx_native)
+                                                       args.threads, args.mx_native,
+                                                       prepared_router=not args.plain_router)
             log(f"prefill35b_16k: {res['prefill_compute_bound']['layer_us']} us/layer, bf16 MFMA "
                 f"{res['prefill_compute_bound']['mfma_util_vs_bf16_peak']}")
     if not args.no_cpu_baseline:

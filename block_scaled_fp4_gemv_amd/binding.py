@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_fp4.so")
 MOE_OK, MOE_E_ARG, MOE_E_FORMAT, MOE_E_CAPACITY, MOE_E_WORKSPACE, MOE_E_HIP = 0, -1, -2, -3, -4, -5
 MOE_FMT_NVFP4, MOE_FMT_MXFP4, MOE_FMT_FP8_E4M3 = 1, 2, 3
 MOE_ROUTE_RENORM = 1
+MOE_ROUTE_PREPARED = 0x200      # router is a prepared router (moe_router_prepare)
 MOE_FFN_AUTO, MOE_FFN_GEMV, MOE_FFN_GROUPED = 0, 1, 2
 MOE_FFN_MX_NATIVE = 4           # MXFP4 grouped path on the scaled MFMA (FP8 activation terms)
 MOE_LAYER_MX_NATIVE = 0x100     # the same for moe_layer_forward (in its route flags)
@@ -43,6 +44,8 @@ SIGNATURES = {
     "moe_pack_expert": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_vp), _vp]),
     "moe_unpack_expert": (_i32, [_i32, _i32, _i32, _vp, ctypes.POINTER(_vp)]),
     "moe_route_workspace": (_sz, [_i32, _i32, _i32, _i32]),
+    "moe_router_prepared_bytes": (_sz, [_i32, _i32]),
+    "moe_router_prepare": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "moe_route": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _u32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_lru_reset": (_i32, [ctypes.POINTER(moe_lru), _vp]),
     "moe_lru_resize_workspace": (_sz, [_i32]),
@@ -222,11 +225,47 @@ def new_route_workspace(T, H, E, k, device="cuda"):
     return torch.empty(moe_route_workspace(T, H, E, k) + 256, dtype=torch.uint8, device=device)
 
 
+class PreparedRouter:
+    """A prepared router (moe_router_prepare): the fp32 router [E][H] then its
+    three bf16 planes, in one uint8 device tensor `buf`.  Accepted wherever a
+    router tensor is; the wrappers add MOE_ROUTE_PREPARED to the route flags.
+    As a read-ahead buffer it stands for its fp32 part."""
+
+    def __init__(self, router, stream=None):
+        import torch
+        self.E, self.H = (int(d) for d in router.shape)
+        n = int(lib().moe_router_prepared_bytes(self.E, self.H))
+        if n == 0:
+            raise ValueError(f"moe_router_prepared_bytes({self.E}, {self.H}) = 0")
+        self.buf = torch.empty(n + 256, dtype=torch.uint8, device=router.device)
+        off = (-self.buf.data_ptr()) % 256
+        self.buf = self.buf[off:off + n]
+        r = router.contiguous()
+        _check(lib().moe_router_prepare(_ptr(r), self.E, self.H, _ptr(self.buf), _stream(stream)),
+               "moe_router_prepare")
+        self.shape = (self.E, self.H)
+        self.device = router.device
+
+    def data_ptr(self):
+        return self.buf.data_ptr()
+
+    def numel(self):
+        return self.E * self.H
+
+    def element_size(self):
+        return 4
+
+
+def _route_flags(router, flags):
+    return flags | MOE_ROUTE_PREPARED if isinstance(router, PreparedRouter) else flags
+
+
 def moe_route(x, router, k, flags=0, topk_idx=None, topk_w=None, pair_perm=None, expert_off=None,
               ws=None, want_perm=True, stream=None):
     import torch
     T, H = x.shape
     E = router.shape[0]
+    flags = _route_flags(router, flags)
     dev = x.device
     if topk_idx is None:
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -365,6 +404,7 @@ def moe_layer_forward(fmt, pool, stride, H, F, E, k, x, router, flags=0, topk_id
     import torch
     T = x.shape[0]
     dev = x.device
+    flags = _route_flags(router, flags)
     if topk_idx is None:
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     if topk_w is None:
@@ -457,7 +497,7 @@ def moe_cached_layer_forward(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w
                                   "the layer needs a pinned record (rec_on_device=False)")
     T = x.shape[0]
     hits, miss = ctypes.c_int32(0), ctypes.c_int32(0)
-    st = lib().moe_cached_layer_forward(fmt, stride, H, F, E, k, flags, ctypes.byref(layer.c), _ptr(x), T,
+    st = lib().moe_cached_layer_forward(fmt, stride, H, F, E, k, _route_flags(layer.router, flags), ctypes.byref(layer.c), _ptr(x), T,
                                         _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
                                         _ptr(out), _ptr(ws), ws.numel(), _stream(stream),
                                         _stream(copy_stream), ctypes.byref(hits), ctypes.byref(miss))
@@ -478,7 +518,7 @@ def moe_cached_layer_forward_split(fmt, stride, H, F, E, k, layer, x, topk_idx, 
     if not defer_done.cuda_event:  # torch creates the HIP event at its first record
         defer_done.record()
     hits, miss, cpu = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
-    st = lib().moe_cached_layer_forward_split(fmt, stride, H, F, E, k, flags, ctypes.byref(layer.c), _ptr(x), T,
+    st = lib().moe_cached_layer_forward_split(fmt, stride, H, F, E, k, _route_flags(layer.router, flags), ctypes.byref(layer.c), _ptr(x), T,
                                               _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
                                               _ptr(out), _ptr(ws), ws.numel(), _stream(stream), _stream(copy_stream),
                                               float(q), _ptr(host_ws), host_ws.numel(), threads,
@@ -501,7 +541,7 @@ def moe_cached_layer_enqueue(fmt, stride, H, F, E, k, layer, x, topk_idx, topk_w
     """Enqueue one cached layer on one stream (no host wait; misses streamed from the
     host pool); hits/misses are in layer.miss_rec once the stream has passed it."""
     T = x.shape[0]
-    st = lib().moe_cached_layer_enqueue(fmt, stride, H, F, E, k, flags, ctypes.byref(layer.c), _ptr(x), T,
+    st = lib().moe_cached_layer_enqueue(fmt, stride, H, F, E, k, _route_flags(layer.router, flags), ctypes.byref(layer.c), _ptr(x), T,
                                         _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
                                         _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_cached_layer_enqueue")
@@ -540,7 +580,7 @@ def moe_cached_layer_enqueue_prefetch(fmt, stride, H, F, E, k, layer, x, topk_id
                                       out, ws, m, pf_buf, pf_stream, flags=0, stream=None):
     """moe_cached_layer_enqueue with the runner-up prefetch on pf_stream (T = 1)."""
     T = x.shape[0]
-    st = lib().moe_cached_layer_enqueue_prefetch(fmt, stride, H, F, E, k, flags, ctypes.byref(layer.c), _ptr(x), T,
+    st = lib().moe_cached_layer_enqueue_prefetch(fmt, stride, H, F, E, k, _route_flags(layer.router, flags), ctypes.byref(layer.c), _ptr(x), T,
                                                  _ptr(topk_idx), _ptr(topk_w), _ptr(pair_slot), _ptr(pair_order),
                                                  _ptr(out), _ptr(ws), ws.numel(), m, _ptr(pf_buf), pf_buf.numel(),
                                                  _stream(stream), _stream(pf_stream))
@@ -574,7 +614,7 @@ def moe_prefill_streamed(fmt, stride, H, F, E, k, host_pools, routers, x, outs, 
     L, T = len(host_pools), x.shape[0]
     arr = lambda xs: (_vp * max(1, len(xs)))(*[_ptr(t) for t in xs])  # noqa: E731
     evs = (_vp * 4)(*[e.cuda_event for e in ps.events])
-    st = lib().moe_prefill_streamed(fmt, stride, H, F, E, k, flags, L, arr(host_pools), arr(routers), _ptr(x), T,
+    st = lib().moe_prefill_streamed(fmt, stride, H, F, E, k, _route_flags(routers[0], flags), L, arr(host_pools), arr(routers), _ptr(x), T,
                                     arr(outs), _ptr(topk_idx), _ptr(topk_w), arr(ps.pools), _ptr(ws), ws.numel(),
                                     _stream(stream), _stream(ps.copy_stream), evs)
     _check(st, "moe_prefill_streamed")

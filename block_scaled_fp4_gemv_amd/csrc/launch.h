@@ -77,8 +77,11 @@ struct RouteArgs {
   // tiles = [tile_e (max_tiles) | tile_m0 (max_tiles) | n_tiles]
   int32_t* tiles;
   int tile_rows, max_tiles;
+  // prepared bf16 split of the router ([3][E][H], moe_router_prepare) or NULL
+  const uint16_t* planes_ready;
   // workspace carve-up
   float* logits;       // [T][E]
+  int32_t* counts;     // [64][E] pairs per expert in copies (permutation)
   uint16_t* planes;    // [3][E][H] bf16 split of the router (T > 4)
 };
 size_t route_ws_bytes(int T, int H, int E, int k);
@@ -86,12 +89,17 @@ void route_ws_carve(RouteArgs& a, void* ws);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // Router logits ([T][E] fp32): GEMV kernel for T <= 4 (launch_router_logits),
 // bf16x3 MFMA GEMM otherwise (launch_router_gemm, planes = [3][E][H] bf16 scratch).
+// counts (optional): [64][E] copies of the pairs per expert, zeroed by the router
+// kernel, then one atomic increment per selected pair by the top-k kernel.
 hipError_t launch_router_logits(const uint16_t* x, const float* R, int T, int H, int E, float* logits,
-                                hipStream_t s);
+                                hipStream_t s, int32_t* counts = nullptr);
+// The planes are split from R into `planes` first unless planes_ready is given.
 hipError_t launch_router_gemm(const uint16_t* x, const float* R, int T, int H, int E, float* logits,
-                              uint16_t* planes, hipStream_t s);
+                              uint16_t* planes, hipStream_t s, const uint16_t* planes_ready = nullptr,
+                              int32_t* counts = nullptr);
+hipError_t launch_router_split(const float* R, int E, int H, uint16_t* planes, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, unsigned flags, int32_t* idx,
-                       float* w, hipStream_t s, int nsplit = 1);
+                       float* w, hipStream_t s, int nsplit = 1, int32_t* counts = nullptr);
 
 hipError_t launch_combine(const float* y, const float* w, int T, int H, int k, uint16_t* out,
                           hipStream_t s);

@@ -100,7 +100,7 @@ const char* moe_status_str(int s) {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_abi_version(void) { return (1 << 16) | 1; }
+int moe_abi_version(void) { return (1 << 16) | 2; }
 
 // ------------------------------------------------------------------ blobs
 
@@ -184,6 +184,37 @@ int moe_unpack_expert(int fmt, int H, int F, const void* blob, void* const canon
 
 // ---------------------------------------------------------------- routing
 
+namespace {
+// The bf16 planes of a prepared router (MOE_ROUTE_PREPARED), else NULL.
+const uint16_t* prepared_planes(const float* router, int E, int H, unsigned flags) {
+  if (!(flags & MOE_ROUTE_PREPARED) || !router) return nullptr;
+  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(router) +
+                                           align256((size_t)E * H * 4));
+}
+}  // namespace
+
+size_t moe_router_prepared_bytes(int E, int H) {
+  if (E < 1 || E > 1024 || !valid_dim(H)) return 0;
+  return align256((size_t)E * H * 4) + align256((size_t)3 * E * H * 2);
+}
+
+int moe_router_prepare(const float* router, int E, int H, void* prepared, moe_stream_t stream) {
+  g_err[0] = 0;
+  if (!moe_router_prepared_bytes(E, H)) return fail(MOE_E_ARG, "E=%d H=%d", E, H);
+  if (!router || !prepared) return fail(MOE_E_ARG, "NULL router or prepared buffer");
+  if (!aligned(router, 16) || !aligned(prepared, 256))
+    return fail(MOE_E_ARG, "router must be 16-byte and prepared 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t n = (size_t)E * H;
+  hipError_t e = hipSuccess;
+  if (prepared != static_cast<const void*>(router))
+    e = hipMemcpyAsync(prepared, router, n * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_router_split(router, E, H,
+                            reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(prepared) + align256(n * 4)), s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_router_prepare");
+}
+
 size_t moe_route_workspace(int T, int H, int E, int k) {
   if (T < 0 || E < 1 || k < 1 || !valid_dim(H)) return 0;
   return route_ws_bytes(T, H, E, k);
@@ -195,7 +226,7 @@ int moe_route(const uint16_t* x, const float* router, int T, int H, int E, int k
   g_err[0] = 0;
   int st = check_route_dims(T, H, E, k);
   if (st) return st;
-  if (flags & ~MOE_ROUTE_RENORM) return fail(MOE_E_ARG, "unknown route flags 0x%x", flags);
+  if (flags & ~(MOE_ROUTE_RENORM | MOE_ROUTE_PREPARED)) return fail(MOE_E_ARG, "unknown route flags 0x%x", flags);
   if (T > 0 && (pair_perm == nullptr) != (expert_off == nullptr))
     return fail(MOE_E_ARG, "pair_perm and expert_off must both be given or both be NULL");
   if (T > 0 && (!x || !router || !topk_idx || !topk_w))
@@ -204,7 +235,8 @@ int moe_route(const uint16_t* x, const float* router, int T, int H, int E, int k
   if (!ws || !aligned(ws, 256) || ws_bytes < route_ws_bytes(T, H, E, k))
     return fail(MOE_E_WORKSPACE, "route workspace needs %zu bytes, 256-aligned", route_ws_bytes(T, H, E, k));
   RouteArgs a{};
-  a.x = x; a.router = router; a.T = T; a.H = H; a.E = E; a.k = k; a.flags = flags;
+  a.x = x; a.router = router; a.T = T; a.H = H; a.E = E; a.k = k; a.flags = flags & MOE_ROUTE_RENORM;
+  a.planes_ready = prepared_planes(router, E, H, flags);
   a.topk_idx = topk_idx; a.topk_w = topk_w; a.pair_perm = pair_perm; a.expert_off = expert_off;
   route_ws_carve(a, ws);
   hipError_t e = launch_route(a, static_cast<hipStream_t>(stream));
@@ -397,7 +429,7 @@ int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, 
   if (st) return st;
   st = check_route_dims(T, H, E, k);
   if (st) return st;
-  if (route_flags & ~(MOE_ROUTE_RENORM | MOE_LAYER_MX_NATIVE))
+  if (route_flags & ~(MOE_ROUTE_RENORM | MOE_ROUTE_PREPARED | MOE_LAYER_MX_NATIVE))
     return fail(MOE_E_ARG, "unknown route flags 0x%x", route_flags);
   if (k > 16) return fail(MOE_E_ARG, "moe_layer_forward needs k <= 16");
   const size_t eb = blob_layout(fmt, H, F).total;
@@ -414,6 +446,7 @@ int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, 
   uint8_t* p = static_cast<uint8_t*>(ws);
   RouteArgs r{};
   r.x = x; r.router = router; r.T = T; r.H = H; r.E = E; r.k = k; r.flags = route_flags & MOE_ROUTE_RENORM;
+  r.planes_ready = prepared_planes(router, E, H, route_flags);
   r.topk_idx = topk_idx; r.topk_w = topk_w;
   route_ws_carve(r, p);
   p += align256(route_ws_bytes(T, H, E, k));
@@ -432,7 +465,7 @@ int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, 
   hipError_t e;
   if (T <= 4) {
     e = launch_router_logits(x, router, T, H, E, r.logits, s);
-    if (e == hipSuccess) e = launch_decode_layer(a, r.logits, route_flags, topk_idx, topk_w, s);
+    if (e == hipSuccess) e = launch_decode_layer(a, r.logits, route_flags & MOE_ROUTE_RENORM, topk_idx, topk_w, s);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_layer_forward(decode)");
   }
   r.pair_perm = perm;
@@ -498,7 +531,8 @@ int moe_layer_forward_static(int fmt, const void* pool, size_t stride, int H, in
   if (need > (size_t)MOE_STATIC_SCRATCH_BYTES)
     return fail(MOE_E_WORKSPACE, "this call needs %zu bytes of workspace, more than the %u of the static scratch array "
                 "(use moe_layer_forward with a caller workspace)", need, (unsigned)MOE_STATIC_SCRATCH_BYTES);
-  if (route_flags & ~MOE_ROUTE_RENORM) return fail(MOE_E_ARG, "unknown route flags 0x%x", route_flags);
+  if (route_flags & ~(MOE_ROUTE_RENORM | MOE_ROUTE_PREPARED))
+    return fail(MOE_E_ARG, "unknown route flags 0x%x", route_flags);
   const size_t eb = blob_layout(fmt, H, F).total;
   if (stride < eb || stride % 256) return fail(MOE_E_ARG, "stride %zu < blob %zu or not 256-multiple", stride, eb);
   if (!pool || !aligned(pool, 256)) return fail(MOE_E_ARG, "pool NULL or not 256-aligned");
@@ -870,6 +904,8 @@ int cached_enqueue(int fmt, size_t stride, int H, int F, int E, int k, unsigned 
   if (!pair_slot || !pair_order || !out || !topk_idx || !topk_w) return fail(MOE_E_ARG, "NULL output");
   if (stride < moe_expert_bytes(fmt, H, F) || stride % 256) return fail(MOE_E_ARG, "bad stride %zu", stride);
   if (!aligned(L->host_pool, 256) || !aligned(L->slot_pool, 256)) return fail(MOE_E_ARG, "pools must be 256-byte aligned");
+  if (route_flags & ~(MOE_ROUTE_RENORM | MOE_ROUTE_PREPARED))
+    return fail(MOE_E_ARG, "unknown route flags 0x%x", route_flags);
   if (T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* p = static_cast<uint8_t*>(ws);
@@ -891,7 +927,8 @@ int cached_enqueue(int fmt, size_t stride, int H, int F, int E, int k, unsigned 
     float* keep = pf ? reinterpret_cast<float*>(pf->buf) : nullptr;  // the logits, for the prefetch step
     hipError_t e = launch_router_logits(x, L->router, T, H, E, r.logits, s);
     if (e == hipSuccess)
-      e = launch_lru_lookup_topk(L->lru, r.logits, E, T, k, route_flags, topk_idx, topk_w, pair_slot, pair_order,
+      e = launch_lru_lookup_topk(L->lru, r.logits, E, T, k, route_flags & MOE_ROUTE_RENORM, topk_idx, topk_w,
+                                 pair_slot, pair_order,
                                  L->miss_rec, T * k < L->lru.S ? T * k : L->lru.S, s, keep);
     if (e != hipSuccess) return hip_fail(e, "cached layer (route + lookup)");
     if (pf) {
@@ -906,7 +943,8 @@ int cached_enqueue(int fmt, size_t stride, int H, int F, int E, int k, unsigned 
       e = hipEventRecord(static_cast<hipEvent_t>(L->lookup_done), s);
       if (e == hipSuccess) e = hipStreamWaitEvent(pf->stream, static_cast<hipEvent_t>(L->lookup_done), 0);
       if (e == hipSuccess)
-        e = launch_lru_lookup_topk(L->lru, keep, E, 1, kp, route_flags, dummy, reinterpret_cast<float*>(dummy + 16),
+        e = launch_lru_lookup_topk(L->lru, keep, E, 1, kp, route_flags & MOE_ROUTE_RENORM, dummy,
+                                   reinterpret_cast<float*>(dummy + 16),
                                    dummy + 32, dummy + 48, rec, n_max, pf->stream);
       if (e == hipSuccess)
         e = launch_cache_fill(rec, static_cast<const uint8_t*>(L->host_pool), static_cast<uint8_t*>(L->slot_pool),

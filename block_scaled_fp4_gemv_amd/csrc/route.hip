@@ -23,12 +23,18 @@ constexpr int kMaxE = 1024;
 // identical router rows produce identical logits.
 constexpr int kGemvMaxT = 4;
 constexpr int kRouterSplitK = 4;  // large-T router GEMM: K split 4 ways, partials summed by k_topk
+// Pairs per expert for the permutation are counted by the top-k kernel in
+// kCountCopies copies ([copy][E], copy = top-k workgroup mod kCountCopies), so
+// that few increments meet at one address; the permutation adds the copies.
+constexpr int kCountCopies = 64;
+static_assert(kCountCopies == 64, "the router GEMV zeroes one copy per lane of its 64-lane workgroup");
 
 template <int NT, int NC>
 __global__ __launch_bounds__(64) void k_router_logits(const uint16_t* __restrict__ x,
                                                       const float* __restrict__ R, int H, int E,
-                                                      float* __restrict__ logits) {
+                                                      float* __restrict__ logits, int32_t* __restrict__ counts) {
   const int lane = threadIdx.x, e = blockIdx.x;
+  if (counts) counts[lane * E + e] = 0;  // this expert's count copies (one per lane), for the top-k kernel
   const float4* r4 = reinterpret_cast<const float4*>(R + (size_t)e * H);
   float4 r[NC];
   uint2 xv[NT][NC];
@@ -54,9 +60,11 @@ __global__ __launch_bounds__(64) void k_router_logits(const uint16_t* __restrict
 }
 
 template <int NT>
-hipError_t router_logits_nt(const uint16_t* x, const float* R, int H, int E, float* logits, hipStream_t s) {
+hipError_t router_logits_nt(const uint16_t* x, const float* R, int H, int E, float* logits, int32_t* counts,
+                            hipStream_t s) {
 #define L(NC) \
-  case NC * 256: hipLaunchKernelGGL((k_router_logits<NT, NC>), dim3(E), dim3(64), 0, s, x, R, H, E, logits); break;
+  case NC * 256: \
+    hipLaunchKernelGGL((k_router_logits<NT, NC>), dim3(E), dim3(64), 0, s, x, R, H, E, logits, counts); break;
   switch (H) {
     L(1) L(2) L(4) L(8) L(16) L(24) L(32)
     default: return hipErrorInvalidValue;
@@ -66,16 +74,17 @@ hipError_t router_logits_nt(const uint16_t* x, const float* R, int H, int E, flo
 }
 
 // ---------------------------------------------------------- large-T router GEMM
-// logits[T][E] = x[T][H] . R[E][H]^T on bf16 MFMA with fp32 accuracy: every fp32
+// logits[T][E] = x[T][H] . R[E][H]^T on bf16 MFMA with fp32 accuracy: an fp32
 // router weight splits exactly into three bf16 terms (hi + mid + lo covers the
-// 24-bit significand; a small kernel writes the three planes once per call), x
-// is already bf16, so each product is exact in fp32 and the three MFMA chains
-// accumulate in fp32.  64x64 tile per workgroup (4 waves of 32x32), K staged
-// through LDS 64 at a time with the next step's global loads issued before the
-// current step's MFMAs.
+// 24-bit significand for every |w| in [2^-100, 3.3e38] and zero), x is already
+// bf16, so each product is exact in fp32 and the three MFMA chains accumulate
+// in fp32.  64x64 tile per workgroup (4 waves of 32x32), K staged through LDS
+// 64 at a time with the next step's global loads issued before the current
+// step's MFMAs.  The planes are written by a small kernel on every call, or
+// once per weight set by moe_router_prepare.
 typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float rfloatx16_t __attribute__((ext_vector_type(16)));
-constexpr int RBM = 64, RBN = 64, RBK = 64, RLD = RBK + 8;
+constexpr int RBM = 64, RBN = 64, RBK = 64, RLD = RBK + 8, RTHREADS = 256;
 
 __global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ R, size_t n,
                                                       uint16_t* __restrict__ planes) {
@@ -96,11 +105,18 @@ __global__ __launch_bounds__(256) void k_router_split(const float* __restrict__ 
   *reinterpret_cast<uint2*>(planes + 2 * n + i) = make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
 }
 
-__global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict__ x,
-                                                     const uint16_t* __restrict__ planes, int T, int H,
-                                                     int E, float* __restrict__ logits) {
+__global__ __launch_bounds__(RTHREADS) void k_router_gemm(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ planes, int T, int H,
+                                                           int E, float* __restrict__ logits,
+                                                           int32_t* __restrict__ counts) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[RBM * RLD];
   __shared__ __attribute__((aligned(16))) uint16_t rs[3][RBN * RLD];
+  if (counts) {  // zero the permutation's count copies for the top-k kernel, a slice per workgroup
+    const int nb = gridDim.x * gridDim.y * gridDim.z;
+    const int b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int n = kCountCopies * E, per = (n + nb - 1) / nb;
+    for (int j = b * per + (int)threadIdx.x; j < min(n, (b + 1) * per); j += RTHREADS) counts[j] = 0;
+  }
   // split K: workgroup z sums k in [z*H/Z, (z+1)*H/Z) into partial z of logits
   const int kz = H / gridDim.z, k0 = blockIdx.z * kz;
   logits += (size_t)blockIdx.z * T * E;
@@ -158,10 +174,13 @@ __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict_
 }
 
 // logits holds nsplit partial sums [nsplit][T][E]; they are added in order.
+// With counts != NULL (kCountCopies copies of [E], zeroed by the router
+// kernel) every selected pair adds 1 to its expert's count in copy
+// blockIdx.x % kCountCopies (integer atomics: the sums do not depend on order).
 template <int NV>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               unsigned flags, int32_t* __restrict__ topk_idx,
-                                              float* __restrict__ topk_w, int nsplit) {
+                                              float* __restrict__ topk_w, int nsplit, int32_t* __restrict__ counts) {
   __shared__ TopkScratch scr[4];
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (t >= T) return;
@@ -179,31 +198,35 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = idx;
     topk_w[(size_t)t * k + lane] = w;
+    if (counts) atomicAdd(&counts[(blockIdx.x % kCountCopies) * E + idx], 1);
   }
 }
 
 hipError_t topk_impl(const float* logits, int T, int E, int k, unsigned flags, int32_t* idx,
-                     float* w, int nsplit, hipStream_t s) {
+                     float* w, int nsplit, int32_t* counts, hipStream_t s) {
   dim3 grid((T + 3) / 4);
-  if (E <= 64) hipLaunchKernelGGL(k_topk<1>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w, nsplit);
-  else if (E <= 256) hipLaunchKernelGGL(k_topk<4>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w, nsplit);
-  else hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w, nsplit);
+  if (E <= 64)
+    hipLaunchKernelGGL(k_topk<1>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w, nsplit, counts);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_topk<4>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w, nsplit, counts);
+  else
+    hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, flags, idx, w, nsplit, counts);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ permutation
 // Stable counting sort of the pairs by expert in one kernel: workgroup e
-// histograms all pair experts in LDS (every workgroup the same histogram),
-// takes its expert's offset from the exclusive scan, then writes the pairs of
-// expert e in ascending pair order.  Wave w owns the w-th quarter of the pairs
+// reads the pairs per expert (counted by the top-k kernel), takes its
+// expert's offset from their exclusive scan, then writes the pairs of expert e
+// in ascending pair order.  Wave w owns the w-th sixteenth of the pairs
 // and walks it 64 pairs at a time (one coalesced load per lane); a ballot
 // ranks the matches inside a 64-pair chunk and the waves' match counts, scanned
-// once, order the quarters.  With tile_rows > 0 it also writes the grouped
+// once, order the sixteenths.  With tile_rows > 0 it also writes the grouped
 // path's tile list (one entry per tile_rows pairs of each expert, in expert
 // order).
-constexpr int kPermThreads = 256, kPermWaves = kPermThreads / 64, kPermUnroll = 64;
+constexpr int kPermThreads = 1024, kPermWaves = kPermThreads / 64, kPermUnroll = 16;
 
-// Exclusive scan over the 256 threads' values; *total = the sum.
+// Exclusive scan over the workgroup's threads' values; *total = the sum.
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
@@ -225,10 +248,12 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
   return base + incl - v;
 }
 
-// ONE: every wave's quarter fits one batch of kPermUnroll chunks (n <=
-// 4 * 64 * kPermUnroll); its pair experts stay in registers between the passes.
+// ONE: every wave's share fits one batch of kPermUnroll chunks (n <=
+// kPermWaves * 64 * kPermUnroll); its pair experts stay in registers between
+// the passes.
 template <bool ONE>
-__global__ __launch_bounds__(kPermThreads) void k_perm_experts(const int32_t* __restrict__ idx, int n, int E,
+__global__ __launch_bounds__(kPermThreads) void k_perm_experts(const int32_t* __restrict__ idx,
+                                                              const int32_t* __restrict__ counts, int n, int E,
                                                               int32_t* __restrict__ pair_perm,
                                                               int32_t* __restrict__ expert_off, int tile_rows,
                                                               int32_t* __restrict__ tile_e,
@@ -240,10 +265,12 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_experts(const int32_t* __
   __shared__ int s_off, s_tbase;
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t lt = (1ull << lane) - 1ull;
-  for (int j = tid; j < E; j += kPermThreads) hist[j] = 0;
-  __syncthreads();
-  // this wave's quarter [b0, b1), in chunks of 64 pairs: the histogram of all
-  // pairs' experts and this wave's matches of e
+  for (int j = tid; j < E; j += kPermThreads) {
+    int c = 0;
+    for (int r = 0; r < kCountCopies; ++r) c += counts[r * E + j];
+    hist[j] = c;
+  }
+  // this wave's share [b0, b1), in chunks of 64 pairs: this wave's matches of e
   const int qn = (n + kPermWaves - 1) / kPermWaves, b0 = min(n, wave * qn), b1 = min(n, b0 + qn);
   int wcnt = 0;
   int v[kPermUnroll];
@@ -254,16 +281,13 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_experts(const int32_t* __
       v[u] = q < b1 ? idx[q] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < kPermUnroll; ++u) {
-      if (v[u] >= 0) atomicAdd(&hist[v[u]], 1);
-      wcnt += __popcll(__ballot(v[u] == e));
-    }
+    for (int u = 0; u < kPermUnroll; ++u) wcnt += __popcll(__ballot(v[u] == e));
     if (ONE) break;
   }
   if (lane == 0) s_wcnt[wave] = wcnt;
   __syncthreads();
   // offsets of expert e (pairs and tiles): sums over the experts before it, the
-  // experts split into contiguous runs of ceil(E / 256) per thread
+  // experts split into contiguous runs of ceil(E / kPermThreads) per thread
   const int epr = (E + kPermThreads - 1) / kPermThreads, j0 = tid * epr, j1 = min(E, j0 + epr);
   int cnt = 0, tl = 0;
   for (int j = j0; j < j1; ++j) {
@@ -324,30 +348,39 @@ __global__ void k_fill_zero(int32_t* p, int n) {
 }  // namespace
 
 hipError_t launch_router_logits(const uint16_t* x, const float* R, int T, int H, int E, float* logits,
-                                hipStream_t s) {
+                                hipStream_t s, int32_t* counts) {
   if (T <= kGemvMaxT) {
     switch (T) {
-      case 1: return router_logits_nt<1>(x, R, H, E, logits, s);
-      case 2: return router_logits_nt<2>(x, R, H, E, logits, s);
-      case 3: return router_logits_nt<3>(x, R, H, E, logits, s);
-      default: return router_logits_nt<4>(x, R, H, E, logits, s);
+      case 1: return router_logits_nt<1>(x, R, H, E, logits, counts, s);
+      case 2: return router_logits_nt<2>(x, R, H, E, logits, counts, s);
+      case 3: return router_logits_nt<3>(x, R, H, E, logits, counts, s);
+      default: return router_logits_nt<4>(x, R, H, E, logits, counts, s);
     }
   }
   return hipErrorInvalidValue;  // large T needs the split planes (launch_router_gemm)
 }
 
-hipError_t launch_router_gemm(const uint16_t* x, const float* R, int T, int H, int E, float* logits,
-                              uint16_t* planes, hipStream_t s) {
+hipError_t launch_router_split(const float* R, int E, int H, uint16_t* planes, hipStream_t s) {
   const size_t n = (size_t)E * H;
   hipLaunchKernelGGL(k_router_split, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, R, n, planes);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_gemm(const uint16_t* x, const float* R, int T, int H, int E, float* logits,
+                              uint16_t* planes, hipStream_t s, const uint16_t* planes_ready, int32_t* counts) {
+  if (!planes_ready) {
+    hipError_t e = launch_router_split(R, E, H, planes, s);
+    if (e != hipSuccess) return e;
+  }
   dim3 grid((E + RBN - 1) / RBN, (T + RBM - 1) / RBM, kRouterSplitK);
-  hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, x, planes, T, H, E, logits);
+  hipLaunchKernelGGL(k_router_gemm, grid, dim3(RTHREADS), 0, s, x, planes_ready ? planes_ready : planes, T, H, E,
+                     logits, counts);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, unsigned flags, int32_t* idx,
-                       float* w, hipStream_t s, int nsplit) {
-  return topk_impl(logits, T, E, k, flags, idx, w, nsplit, s);
+                       float* w, hipStream_t s, int nsplit, int32_t* counts) {
+  return topk_impl(logits, T, E, k, flags, idx, w, nsplit, counts, s);
 }
 
 static size_t logits_bytes(int T, int E) {
@@ -357,13 +390,15 @@ static size_t logits_bytes(int T, int E) {
 size_t route_ws_bytes(int T, int H, int E, int k) {
   (void)k;
   const size_t planes = T > kGemvMaxT ? align256((size_t)3 * E * H * 2) : 0;
-  return logits_bytes(T, E) + planes;
+  return logits_bytes(T, E) + align256((size_t)kCountCopies * E * 4) + planes;
 }
 
 void route_ws_carve(RouteArgs& a, void* ws) {
   uint8_t* p = static_cast<uint8_t*>(ws);
   a.logits = reinterpret_cast<float*>(p);
   p += logits_bytes(a.T, a.E);
+  a.counts = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)kCountCopies * a.E * 4);
   a.planes = a.T > kGemvMaxT ? reinterpret_cast<uint16_t*>(p) : nullptr;
 }
 
@@ -373,20 +408,24 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(k_fill_zero, dim3((a.E + 1 + 255) / 256), dim3(256), 0, s, a.expert_off, a.E + 1);
     return hipGetLastError();
   }
-  hipError_t e = a.T <= kGemvMaxT ? launch_router_logits(a.x, a.router, a.T, a.H, a.E, a.logits, s)
-                                  : launch_router_gemm(a.x, a.router, a.T, a.H, a.E, a.logits, a.planes, s);
+  // the per-expert pair counts of the permutation: zeroed by the router
+  // kernel, counted by the top-k kernel
+  int32_t* counts = a.pair_perm ? a.counts : nullptr;
+  hipError_t e = a.T <= kGemvMaxT
+                     ? launch_router_logits(a.x, a.router, a.T, a.H, a.E, a.logits, s, counts)
+                     : launch_router_gemm(a.x, a.router, a.T, a.H, a.E, a.logits, a.planes, s, a.planes_ready, counts);
   if (e != hipSuccess) return e;
   e = launch_topk(a.logits, a.T, a.E, a.k, a.flags, a.topk_idx, a.topk_w, s,
-                  a.T <= kGemvMaxT ? 1 : kRouterSplitK);
+                  a.T <= kGemvMaxT ? 1 : kRouterSplitK, counts);
   if (e != hipSuccess || !a.pair_perm) return e;
   const int n = a.T * a.k;
   int32_t* te = a.tile_rows > 0 ? a.tiles : nullptr;
   if (n <= kPermWaves * 64 * kPermUnroll)
-    hipLaunchKernelGGL(k_perm_experts<true>, dim3(a.E), dim3(kPermThreads), 0, s, a.topk_idx, n, a.E, a.pair_perm,
+    hipLaunchKernelGGL(k_perm_experts<true>, dim3(a.E), dim3(kPermThreads), 0, s, a.topk_idx, counts, n, a.E, a.pair_perm,
                        a.expert_off, a.tile_rows, te, te ? te + a.max_tiles : nullptr,
                        te ? te + 2 * a.max_tiles : nullptr);
   else
-    hipLaunchKernelGGL(k_perm_experts<false>, dim3(a.E), dim3(kPermThreads), 0, s, a.topk_idx, n, a.E, a.pair_perm,
+    hipLaunchKernelGGL(k_perm_experts<false>, dim3(a.E), dim3(kPermThreads), 0, s, a.topk_idx, counts, n, a.E, a.pair_perm,
                        a.expert_off, a.tile_rows, te, te ? te + a.max_tiles : nullptr,
                        te ? te + 2 * a.max_tiles : nullptr);
   return hipGetLastError();

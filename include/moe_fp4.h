@@ -72,6 +72,10 @@ enum moe_fmt { MOE_FMT_NVFP4 = 1, MOE_FMT_MXFP4 = 2, MOE_FMT_FP8_E4M3 = 3 };
 
 /* moe_route flags */
 #define MOE_ROUTE_RENORM 1u /* w /= sum of the selected probabilities (off by default) */
+/* `router` points to a prepared router (moe_router_prepare): the fp32 [E][H]
+ * router followed by its bf16 split, so that calls with many tokens do not
+ * split the router again.  Accepted wherever route flags are. */
+#define MOE_ROUTE_PREPARED 0x200u
 
 /* moe_expert_ffn flags */
 #define MOE_FFN_AUTO 0u
@@ -154,6 +158,23 @@ size_t moe_route_workspace(int T, int H, int E, int k);
 int moe_route(const uint16_t* x, const float* router, int T, int H, int E, int k, unsigned flags,
               int32_t* topk_idx, float* topk_w, int32_t* pair_perm, int32_t* expert_off,
               void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Bytes of a prepared router (device memory, 256-byte aligned): the fp32
+ * router [E][H] as given, then at byte align256(E*H*4) three bf16 planes
+ * [3][E][H] with hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid)
+ * (round to nearest even).  bf16 carries 8 of fp32's 24 significand bits, so
+ * hi + mid + lo = w exactly for every zero and every |w| in [2^-100, 3.3e38];
+ * smaller weights lose the bits below bf16's smallest subnormal (2^-133) and
+ * larger ones round to infinity.  The planes are the operand of the many-token
+ * router GEMM (the same split that calls without a prepared router make on
+ * every call); the fp32 copy serves the few-token GEMV. */
+size_t moe_router_prepared_bytes(int E, int H);
+
+/* Write a prepared router from an fp32 router [E][H] (16-byte aligned) into
+ * `prepared` (device, 256-byte aligned, moe_router_prepared_bytes); once per
+ * weight set.  Pass it as `router` with MOE_ROUTE_PREPARED in the route flags.
+ * The logits are the same as from the plain router, bit for bit. */
+int moe_router_prepare(const float* router, int E, int H, void* prepared, moe_stream_t stream);
 
 /* --------------------------------------------------------------- cache */
 
@@ -240,8 +261,10 @@ int moe_cache_lookup(const moe_lru* lru, const int32_t* topk_idx, int T, int k,
                      int32_t* pair_slot, int32_t* pair_order, int32_t* miss_rec,
                      moe_stream_t stream);
 
-/* Enqueue the GPU cache fill for a completed miss record (read on the host):
- * copy_stream first waits on slots_free (if not NULL; record it after the last
+/* Enqueue the GPU cache fill for a completed miss record (read on the host)
+ * (page "753B...", section "按带宽动态分配参数存储": asynchronous host->device
+ * copies on their own stream; page "8GB 笔记本 39.3 tok/s...", section
+ * "设计核心": the GPU fills the VRAM expert cache):  copy_stream first waits on slots_free (if not NULL; record it after the last
  * kernel that reads the victim slots), then one hipMemcpyAsync host->device of
  * expert_bytes per miss, from host_pool + expert*stride to slot_pool +
  * slot*stride, then fill_done is recorded (if not NULL).
@@ -270,7 +293,10 @@ int moe_cache_fill_device(const int32_t* miss_rec, const void* host_pool, void* 
 /* Workspace bytes for moe_expert_ffn. */
 size_t moe_ffn_workspace(int fmt, int T, int H, int F, int k, int E);
 
-/* Expert FFNs of the routed pairs:  for pair q = t*k+j with e = topk_idx[q]
+/* Expert FFNs of the routed pairs (page "753B...", section "混合专家架构（MoE）的
+ * 天然稀疏性": each expert an independent FFN; page "8GB显存跑35B MoE模型...",
+ * §2.1: weights dequantized at compute time):
+ * for pair q = t*k+j with e = topk_idx[q]
  * and slot s = pair_slot ? pair_slot[q] : e,
  *     h = bf16( silu(G_s x_t) * (U_s x_t) ),   y_q = D_s h        (fp32 out)
  * with the weights of blob s dequantized in registers (never materialised).

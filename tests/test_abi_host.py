@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     assert B.lib().moe_status_str(0) == b"ok"
     assert B.lib().moe_status_str(B.MOE_E_CAPACITY) == b"cache capacity exceeded"
-    assert B.lib().moe_abi_version() == (1 << 16) | 1   # 1.1: keyed LRU state (key_base)
+    assert B.lib().moe_abi_version() == (1 << 16) | 2   # 1.2: prepared routers (MOE_ROUTE_PREPARED)
 
 
 @pytest.mark.parametrize("fmt,H,F,exp", [
