@@ -76,6 +76,13 @@ def parse():
                    help="generate layer 0's experts once and give every other layer its own device copy "
                         "(distinct addresses, same bytes; routers stay per layer) - for the large stacks")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--c4-steps", type=int, default=100,
+                   help="timed decode steps of the 753B-class stack leg (0 = skip the leg)")
+    p.add_argument("--c4-prefill-reps", type=int, default=5,
+                   help="passes of the 753B-class 4096-token prefill in that leg (0 = skip)")
+    p.add_argument("--persistence-steps", type=int, default=32,
+                   help="decode steps after the timed ones over which the previous step's routing is compared "
+                        "with each step's (0 = skip)")
     p.add_argument("--cpu-sample-steps", type=int, default=6)
     p.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     p.add_argument("--calib-copy-mib", type=int, default=256,
@@ -489,6 +496,118 @@ def cache_split_leg(fmt, hosts, routers, stride, warmup, steps, threads):
             "warmup_steps": warmup, "timed_steps": steps, "runs": runs}
 
 
+class DecodeStack:
+    """Batch-1 decode through a stack of resident layers, one moe_layer_forward
+    per layer (each layer's down kernel reading the next layer's router ahead),
+    the whole step captured in one HIP graph."""
+
+    def __init__(self, fmt, wl, pools, routers, stride, n_layers, xs, read_ahead=True):
+        import torch
+
+        from block_scaled_fp4_gemv_amd import binding as B
+
+        H, E, F, k = wl.H, wl.E, wl.F, wl.k
+        self.n_layers, self.n_states = n_layers, xs.shape[0]
+        self.xs_dev = torch.from_numpy(xs).cuda()
+        self.x = torch.empty((1, H), dtype=torch.uint16, device="cuda")
+        self.idx = [torch.empty((1, k), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+        w = [torch.empty((1, k), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+        out = [torch.empty((1, H), dtype=torch.uint16, device="cuda") for _ in range(n_layers)]
+        lws = [B.new_layer_workspace(fmt, 1, H, F, k, E) for _ in range(n_layers)]
+
+        def step():
+            for l in range(n_layers):
+                B.moe_layer_forward(fmt, pools[l], stride, H, F, E, k, self.x, routers[l], topk_idx=self.idx[l],
+                                    topk_w=w[l], out=out[l], ws=lws[l],
+                                    warm=routers[(l + 1) % n_layers] if read_ahead else None)
+
+        # eager warm-up, then capture one step in a HIP graph
+        self.x.copy_(self.xs_dev[0:1])
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            step()
+        torch.cuda.synchronize()
+        self._keep = (w, out, lws)
+
+    def replay(self, i):
+        j = i % self.n_states
+        self.x.copy_(self.xs_dev[j:j + 1])
+        self.g.replay()
+
+    def time(self, warmup, steps):
+        """ms per step over `steps` timed replays (HIP events) after `warmup`."""
+        import torch
+        for i in range(warmup):
+            self.replay(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(steps):
+            self.replay(warmup + i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps
+
+    def routing_persistence(self, start, n):
+        """How well the previous step's routing of the same layer predicts this
+        step's (the predictor of a speculative weight stream): over n more
+        steps, the share of each layer's k routed experts that the layer also
+        routed at the previous step, and the share routed at the same rank."""
+        import numpy as np
+        import torch
+        if n < 2:
+            return None
+        prev, in_set, same_rank, tot = None, 0, 0, 0
+        for i in range(n):
+            self.replay(start + i)
+            cur = torch.stack(self.idx).cpu().numpy().reshape(self.n_layers, -1)
+            if prev is not None:
+                for l in range(self.n_layers):
+                    in_set += len(set(cur[l].tolist()) & set(prev[l].tolist()))
+                    same_rank += int(np.sum(cur[l] == prev[l]))
+                    tot += cur.shape[1]
+            prev = cur
+        return {"prev_step_set_overlap": round(in_set / tot, 4), "prev_step_same_rank": round(same_rank / tot, 4),
+                "steps": n, "layers": self.n_layers}
+
+
+def c4_leg(args):
+    """The 753B-class stack (hidden 6144, 256 experts, top-8, width 2048, NVFP4):
+    batch-1 decode through its 8 layers (layer 0's experts generated once, every
+    other layer its own device copy) and the 4096-token prefill of one layer."""
+    import torch
+
+    from block_scaled_fp4_gemv_amd import synth as sy
+
+    wl = sy.WORKLOADS["decode753b"]
+    fmt = 1
+    pools, routers, stride, _ = build_stack(wl, fmt, wl.layers, args.threads, replicate=True)
+    xs = sy.ar1_sequence(0, wl.cfg_id, wl.steps, wl.H)
+    dec = DecodeStack(fmt, wl, pools, routers, stride, wl.layers, xs)
+    ms = dec.time(args.warmup, args.c4_steps)
+    layer_us = ms * 1000.0 / wl.layers
+    nb = algorithmic_bytes(wl, fmt)
+    gbps = nb["layer_total"] / (layer_us * 1e-6) / 1e9
+    res = {"decode": {"workload": f"decode753b: {wl.layers} stacked MoE layers, hidden {wl.H}, {wl.E} experts, "
+                                  f"top-{wl.k}, expert width {wl.F}, nvfp4, batch 1 (layer 0's experts replicated "
+                                  f"to every layer's own device pool)",
+                      "tokens_per_s": round(1000.0 / ms, 2), "layer_us": round(layer_us, 3),
+                      "bytes_per_layer": nb["layer_total"], "hbm_GBps": round(gbps, 1),
+                      "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "steps": args.c4_steps,
+                      "timing": "one HIP graph per token, HIP events over the timed replays"}}
+    log(f"C4 decode: {res['decode']}")
+    del dec, pools, routers
+    torch.cuda.empty_cache()
+    if args.c4_prefill_reps > 0:
+        res["prefill"] = prefill_leg("prefill753b", fmt, args.c4_prefill_reps, args.threads)
+        log(f"C4 prefill: {res['prefill']['layer_us']} us/layer")
+        torch.cuda.empty_cache()
+    return res
+
+
 def algorithmic_bytes(wl, fmt):
     """Bytes one decode token must move, per layer: weights of the k routed experts
     (codes + block scales + tensor scales), the fp32 router, and the activations."""
@@ -688,9 +807,18 @@ def cpu_baseline(wl, fmt, xs, n_steps, n_layers):
 
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        pools = threadpool_info()
+        blas_threads = max([d.get("num_threads", 1) for d in pools] + [1])
+        blas = ", ".join(f"{d.get('internal_api')} {d.get('version')} ({d.get('num_threads')} threads)"
+                         for d in pools if d.get("user_api") == "blas") or "none found"
     except Exception:  # pragma: no cover
-        blas_threads = 1
+        blas_threads, blas = 1, "unknown"
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
+    except OSError:  # pragma: no cover
+        pass
 
     class Lazy:
         def __init__(self, l):
@@ -717,7 +845,7 @@ def cpu_baseline(wl, fmt, xs, n_steps, n_layers):
     return dict(value=n_steps / dt, unit="tok/s", cores=int(blas_threads), kind="oracle",
                 sample=f"first {n_steps} decode tokens through all {n_layers} layers "
                        f"(NumPy fp64 oracle incl. dequant; {dt:.1f} s)",
-                host_cpus=os.cpu_count())
+                host_cpus=os.cpu_count(), cpu_model=cpu_model, blas=blas)
 
 
 def main():
@@ -745,23 +873,7 @@ def main():
 
     n_states = wl.steps
     xs = sy.ar1_sequence(0, wl.cfg_id, n_states, H)
-    xs_dev = torch.from_numpy(xs).cuda()
-    x = torch.empty((1, H), dtype=torch.uint16, device="cuda")
-    idx = [torch.empty((1, k), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
-    w = [torch.empty((1, k), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
-    out = [torch.empty((1, H), dtype=torch.uint16, device="cuda") for _ in range(n_layers)]
-    lws = [B.new_layer_workspace(fmt, 1, H, F, k, E) for _ in range(n_layers)]
-
-    def layer(l):
-        # the next layer's router (a static weight) is read ahead during this layer's down kernel
-        B.moe_layer_forward(fmt, pools[l], stride, H, F, E, k, x, routers[l], topk_idx=idx[l],
-                            topk_w=w[l], out=out[l], ws=lws[l],
-                            warm=None if args.no_read_ahead else routers[(l + 1) % n_layers])
-
-    def step():
-        for l in range(n_layers):
-            layer(l)
-
+    dec = DecodeStack(fmt, wl, pools, routers, stride, n_layers, xs, read_ahead=not args.no_read_ahead)
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -770,33 +882,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    # eager warm-up, then capture one step in a HIP graph
-    x.copy_(xs_dev[0:1])
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    torch.cuda.synchronize()
-
-    for i in range(args.warmup):
-        x.copy_(xs_dev[i % n_states:i % n_states + 1])
-        g.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(args.steps):
-        j = (args.warmup + i) % n_states
-        x.copy_(xs_dev[j:j + 1])
-        g.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    ms_step = dec.time(args.warmup, args.steps)
     tok_s = 1000.0 / ms_step
     log(f"timed {args.steps} steps: {ms_step * 1000:.1f} us/step, {tok_s:.1f} tok/s")
+    persistence = dec.routing_persistence(args.warmup + args.steps, args.persistence_steps)
+    log(f"routing persistence: {persistence}")
 
     # one layer launch = the layer's kernels inside the timed graph replays: its
     # mean duration is the timed region (HIP events) divided by steps x layers
@@ -832,6 +922,7 @@ def main():
                    "read_ahead": None if args.no_read_ahead else
                    "each layer's down kernel warms the next layer's router (moe_layer_forward_prefetch)"},
         "weight_stream_GBps": round(stream_gbps, 1),
+        "routing_persistence": persistence,
         "weight_stream_frac_of_hbm": round(stream_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"kernel": "moe_layer_forward decode layer (router GEMV, gate/up+SwiGLU with "
                                "in-block top-k, down+combine: 3 kernels)",
@@ -871,7 +962,7 @@ def main():
         del hosts
     if args.prefill != "none":
         log(f"prefill leg {args.prefill} ...")
-        del pools
+        del pools, dec
         torch.cuda.empty_cache()
         res["prefill"] = prefill_leg(args.prefill, args.fmt, args.prefill_reps, args.threads, args.mx_native,
                                      prepared_router=not args.plain_router)
@@ -884,6 +975,10 @@ def main():
                                                        prepared_router=not args.plain_router)
             log(f"prefill35b_16k: {res['prefill_compute_bound']['layer_us']} us/layer, bf16 MFMA "
                 f"{res['prefill_compute_bound']['mfma_util_vs_bf16_peak']}")
+    if args.c4_steps > 0 and wl.name == "decode35b":
+        log("753B-class leg ...")
+        torch.cuda.empty_cache()
+        res["c4"] = c4_leg(args)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(wl, fmt, xs, args.cpu_sample_steps, n_layers)
