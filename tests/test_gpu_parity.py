@@ -965,3 +965,28 @@ def test_layer_forward_prefill_2048_sampled(fmt):
     yg = y.cpu().numpy().reshape(T, k, H)[rows].reshape(-1, H)
     assert_rows_close(yg, ref["y"].reshape(-1, H), what="y")
     assert_rows_close(bf16_dev_to_f64(out)[rows], fm.bf16_to_f64(ref["out"]), what="out")
+
+
+@pytest.mark.parametrize("k", [1, 3, 8, 16, 17, 24])
+def test_combine_every_k(k):
+    """moe_combine for k = 1 .. 24 (the kernels unrolled over k up to 16, the
+    generic one above), 37 tokens: every bf16 output lies between the roundings
+    of the oracle's fp64 sum minus and plus the fp32 FMA chain's error bound
+    ((k+1) * 2^-24 * sum |w y|; rounding is monotone), and almost all equal the
+    oracle's."""
+    T, H = 37, 2048
+    rng = np.random.default_rng(100 + k)
+    y = (rng.normal(0.0, 1.0, (T, k, H)) * 10.0 ** rng.integers(-2, 3, (T, k, 1))).astype(np.float32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    out = torch.empty((T, H), dtype=torch.uint16, device="cuda")
+    B.moe_combine(torch.from_numpy(y.reshape(T * k, H)).cuda(), torch.from_numpy(w).cuda(), out)
+    torch.cuda.synchronize()
+    got = fm.bf16_to_f64(out.cpu().numpy())
+    ref64 = moe.combine_f64(y, w)
+    ref = fm.bf16_to_f64(moe.combine(y, w))
+    bound = (k + 1) * 2.0 ** -24 * np.einsum("tj,tjh->th", np.abs(w.astype(np.float64)), np.abs(y.astype(np.float64)))
+    lo = fm.bf16_to_f64(fm.to_bf16_rne(ref64 - bound))
+    hi = fm.bf16_to_f64(fm.to_bf16_rne(ref64 + bound))
+    ok = (lo <= got) & (got <= hi)
+    assert ok.all(), f"{np.count_nonzero(~ok)} outputs outside the rounding of the error bound"
+    assert np.mean(got == ref) > 0.99
