@@ -782,7 +782,7 @@ def prefill_stream_leg(fmt, hosts, pools, routers, stride, reps):
 
 
 def measured_traffic(n_layers_run, n_layers_default):
-    """HBM bytes per decode layer from the committed FETCH_SIZE/WRITE_SIZE runs, if the
+    """HBM bytes per decode layer from the committed request-size counter runs, if the
     kernel sources are unchanged since they were taken (else None)."""
     import glob
     import hashlib
