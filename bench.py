@@ -80,6 +80,11 @@ def parse():
                    help="timed decode steps of the 753B-class stack leg (0 = skip the leg)")
     p.add_argument("--c4-prefill-reps", type=int, default=5,
                    help="passes of the 753B-class 4096-token prefill in that leg (0 = skip)")
+    p.add_argument("--c4-cpu", type=int, default=8,
+                   help="753B-class leg: time the oracle on one decode token and on this many prefill tokens "
+                        "(0 = skip)")
+    p.add_argument("--cpu-prefill-tokens", type=int, default=512,
+                   help="time the oracle on this many tokens of the prefill leg's input (0 = skip)")
     p.add_argument("--persistence-steps", type=int, default=32,
                    help="decode steps after the timed ones over which the previous step's routing is compared "
                         "with each step's (0 = skip)")
@@ -91,10 +96,11 @@ def parse():
     return p.parse_args()
 
 
-def build_stack(wl, fmt, n_layers, threads, keep_host=False, replicate=False):
+def build_stack(wl, fmt, n_layers, threads, keep_host=False, replicate=False, batch0=None):
     """Generate, quantize, pack and upload every layer; returns device pools, routers,
     the blob stride and (keep_host) the pinned host copy of every layer.  With
-    replicate, layers after the first get a device copy of layer 0's experts."""
+    replicate, layers after the first get a device copy of layer 0's experts.  A
+    list passed as batch0 receives layer 0's canonical experts (for the oracle)."""
     import torch
 
     from block_scaled_fp4_gemv_amd import binding as B
@@ -111,6 +117,8 @@ def build_stack(wl, fmt, n_layers, threads, keep_host=False, replicate=False):
             routers.append(torch.from_numpy(sy.router(0, wl.wcfg, l, wl.E, wl.H)).cuda())
             continue
         batch = sy.experts(fmt, 0, wl.wcfg, l, 0, wl.E, wl.H, wl.F, wl.w_std)
+        if batch0 is not None and l == 0:
+            batch0.append(batch)
         if keep_host and l > 0:
             host = torch.empty(wl.E * stride, dtype=torch.uint8).pin_memory()
         B.pack_layer(fmt, wl.H, wl.F, batch, host.numpy(), stride, threads=threads)
@@ -574,6 +582,29 @@ class DecodeStack:
                 "steps": n, "layers": self.n_layers}
 
 
+def oracle_sample(fmt, wl, x, routers, batch, what):
+    """The oracle as it stands (NumPy fp64, dequant included) on a bounded sample:
+    x's rows through one layer per router, every layer with the experts of
+    `batch` (generated outside the timed region).  Returns tokens/s and the sample."""
+    import numpy as np
+
+    from block_scaled_fp4_gemv_amd import synth as sy
+    from oracle import moe
+
+    class View:
+        def __getitem__(self, e):
+            return sy.expert_view(batch, int(e))
+
+    ex = View()
+    t0 = time.perf_counter()
+    for R in routers:
+        moe.moe_layer(fmt, x, np.asarray(R), ex, wl.k)
+    dt = time.perf_counter() - t0
+    return {"tokens_per_s": round(x.shape[0] / dt, 4), "kind": "oracle", "cores": os.cpu_count(),
+            "sample": f"{what}: {x.shape[0]} token(s) through {len(routers)} layer(s) "
+                      f"(NumPy fp64 oracle incl. dequant; {dt:.1f} s)"}
+
+
 def c4_leg(args):
     """The 753B-class stack (hidden 6144, 256 experts, top-8, width 2048, NVFP4):
     batch-1 decode through its 8 layers (layer 0's experts generated once, every
@@ -584,7 +615,8 @@ def c4_leg(args):
 
     wl = sy.WORKLOADS["decode753b"]
     fmt = 1
-    pools, routers, stride, _ = build_stack(wl, fmt, wl.layers, args.threads, replicate=True)
+    batch0 = [] if args.c4_cpu and not args.no_cpu_baseline else None
+    pools, routers, stride, _ = build_stack(wl, fmt, wl.layers, args.threads, replicate=True, batch0=batch0)
     xs = sy.ar1_sequence(0, wl.cfg_id, wl.steps, wl.H)
     dec = DecodeStack(fmt, wl, pools, routers, stride, wl.layers, xs)
     ms = dec.time(args.warmup, args.c4_steps)
@@ -599,12 +631,24 @@ def c4_leg(args):
                       "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "steps": args.c4_steps,
                       "timing": "one HIP graph per token, HIP events over the timed replays"}}
     log(f"C4 decode: {res['decode']}")
+    routers_host = [r.cpu().numpy() for r in routers]
     del dec, pools, routers
     torch.cuda.empty_cache()
     if args.c4_prefill_reps > 0:
         res["prefill"] = prefill_leg("prefill753b", fmt, args.c4_prefill_reps, args.threads)
         log(f"C4 prefill: {res['prefill']['layer_us']} us/layer")
         torch.cuda.empty_cache()
+    if batch0:
+        # the replicated stack's layers all carry layer 0's experts, which are also
+        # the first weight set of the 4096-token prefill
+        res["decode"]["cpu_oracle"] = oracle_sample(fmt, wl, xs[:1], routers_host, batch0[0],
+                                                    "decode753b, first decode token")
+        pw = sy.WORKLOADS["prefill753b"]
+        xp = sy.token_rows(0, pw.cfg_id, args.c4_cpu, pw.H)
+        if "prefill" in res:
+            res["prefill"]["cpu_oracle"] = oracle_sample(fmt, pw, xp, [sy.router(0, pw.wcfg, 0, pw.E, pw.H)],
+                                                         batch0[0], "prefill753b, first tokens of the input")
+        log(f"C4 oracle: decode {res['decode']['cpu_oracle']}")
     return res
 
 
@@ -625,7 +669,7 @@ MX_NATIVE_INSTR = ("v_mfma_scale_f32_16x16x128_f8f6f4, FP4 weights x FP8 activat
                    "so the expert flops count twice in the instruction's own rate)")
 
 
-def prefill_leg(name, fmt_override, reps, threads, mx_native=False, prepared_router=True):
+def prefill_leg(name, fmt_override, reps, threads, mx_native=False, prepared_router=True, cpu_tokens=0):
     """Time moe_layer_forward over a T-token prefill of one layer (grouped MFMA path)."""
     import numpy as np
     import torch
@@ -641,10 +685,14 @@ def prefill_leg(name, fmt_override, reps, threads, mx_native=False, prepared_rou
     # two layers used alternately, so that more than twice the 256 MB MALL is
     # touched between reuses of a weight set
     pools, Rs = [], []
+    batch0 = None
     for l in range(2):
         host = np.empty(E * stride, np.uint8)
-        B.pack_layer(fmt, H, F, sy.experts(fmt, 0, wl.wcfg, l, 0, E, H, F, wl.w_std), host, stride,
-                     threads=threads)
+        batch = sy.experts(fmt, 0, wl.wcfg, l, 0, E, H, F, wl.w_std)
+        B.pack_layer(fmt, H, F, batch, host, stride, threads=threads)
+        if l == 0 and cpu_tokens > 0:
+            batch0 = batch
+        del batch
         pools.append(torch.from_numpy(host).cuda())
         R = torch.from_numpy(sy.router(0, wl.wcfg, l, E, H)).cuda()
         # the router's bf16 split is made once per weight set, not per call
@@ -696,7 +744,13 @@ def prefill_leg(name, fmt_override, reps, threads, mx_native=False, prepared_rou
     hbm_frac = bytes_alg / t / (HBM_PEAK_GBPS * 1e9)
     mf = flops_mfma / t / 1e12
     fmt_name = {1: "nvfp4", 2: "mxfp4", 3: "fp8"}[fmt]
-    return {"workload": f"{name}: {T} tokens through one layer, hidden {H}, {E} experts, top-{k}, "
+    cpu = None
+    if batch0 is not None:
+        del pools, graphs
+        cpu = oracle_sample(fmt, wl, x[:cpu_tokens].cpu().numpy(), [sy.router(0, wl.wcfg, 0, E, H)], batch0,
+                            f"{name}, first tokens of the input")
+    return {**({"cpu_oracle": cpu} if cpu else {}),
+            "workload": f"{name}: {T} tokens through one layer, hidden {H}, {E} experts, top-{k}, "
                         f"width {F}, {fmt_name}",
             "tokens_per_s": round(T / t, 1), "layer_us": round(us, 2), "experts_used": used,
             "algorithmic_bytes": bytes_alg, "hbm_GBps": round(bytes_alg / t / 1e9, 1),
@@ -965,7 +1019,8 @@ def main():
         del pools, dec
         torch.cuda.empty_cache()
         res["prefill"] = prefill_leg(args.prefill, args.fmt, args.prefill_reps, args.threads, args.mx_native,
-                                     prepared_router=not args.plain_router)
+                                     prepared_router=not args.plain_router,
+                                     cpu_tokens=0 if args.no_cpu_baseline else args.cpu_prefill_tokens)
         log(f"prefill: {res['prefill']['layer_us']} us/layer, {res['prefill']['tokens_per_s']} tok/s")
         if args.prefill == "prefill35b" and args.compute_bound_reps > 0:
             log("compute-bound prefill point prefill35b_16k ...")
