@@ -275,3 +275,26 @@ def test_layer_forward_static_checks_before_any_hip_call():
                                       None) == B.MOE_E_FORMAT
     assert L.moe_layer_forward_static(fmt, fake, stride, H, F, E, k, 0, fake, 0, fake, fake, fake, fake,
                                       None) == B.MOE_OK
+
+
+def test_router_prepare_sizes_and_argument_errors():
+    """moe_router_prepared_bytes = 256-aligned fp32 router + 256-aligned three
+    bf16 planes; moe_router_prepare and the route calls refuse bad arguments
+    before any HIP call."""
+    L = B.lib()
+    for E, H in ((8, 256), (256, 2048), (256, 6144), (1024, 8192)):
+        a = (E * H * 4 + 255) // 256 * 256
+        assert B.lib().moe_router_prepared_bytes(E, H) == a + (3 * E * H * 2 + 255) // 256 * 256
+    assert L.moe_router_prepared_bytes(0, 2048) == 0
+    assert L.moe_router_prepared_bytes(1025, 2048) == 0
+    assert L.moe_router_prepared_bytes(256, 300) == 0
+    assert L.moe_router_prepare(0x1000, 0, 2048, 0x1000, None) == B.MOE_E_ARG     # E
+    assert L.moe_router_prepare(None, 256, 2048, 0x1000, None) == B.MOE_E_ARG     # NULL router
+    assert L.moe_router_prepare(0x1000, 256, 2048, None, None) == B.MOE_E_ARG     # NULL buffer
+    assert L.moe_router_prepare(0x1004, 256, 2048, 0x1000, None) == B.MOE_E_ARG   # router not 16-aligned
+    assert L.moe_router_prepare(0x1000, 256, 2048, 0x1010, None) == B.MOE_E_ARG   # buffer not 256-aligned
+    # an unknown route flag next to MOE_ROUTE_PREPARED is refused by the route call
+    ws = np.zeros(B.moe_route_workspace(8, 2048, 256, 8) + 256, np.uint8)
+    wsp = (ws.ctypes.data + 255) // 256 * 256
+    assert L.moe_route(0x1000, 0x1000, 8, 2048, 256, 8, B.MOE_ROUTE_PREPARED | 0x400, 0x1000, 0x1000,
+                       None, None, wsp, ws.size - 256, None) == B.MOE_E_ARG
