@@ -538,7 +538,8 @@ class DecodeStack:
         with torch.cuda.graph(self.g):
             step()
         torch.cuda.synchronize()
-        self._keep = (w, out, lws)
+        # the graph's buffers: each layer's routing and output of the last replay
+        self.topk_w, self.out, self.ws = w, out, lws
 
     def replay(self, i):
         j = i % self.n_states
