@@ -8,14 +8,15 @@
 //
 // Pairs arrive sorted by expert (pair_perm / expert_off).  A device-built tile
 // list holds one (expert, first row) entry per 128 rows of each expert (64 for
-// FP8, whose per-step partial sums need more registers).  A workgroup of NW
+// FP8, whose per-step partial sums need more registers, and for native MXFP4,
+// whose FP8 operand sets do).  A workgroup of NW
 // waves (8 when the output width allows, else 4) owns one tile x NW*32 output columns
 // per matrix for gate/up (NW*64 for down): wave w takes the weight fragments
 // of its 32 (64) columns and all rows of the tile (up to eight 16-row
 // subtiles for gate/up, six for down, v_mfma_f32_16x16x32_bf16), so each
 // dequantized weight operand feeds one MFMA per subtile and an expert's gate
 // and up weights are fetched and dequantized once per column tile whenever it
-// has at most 128 rows (FP8: 64).  The subtile count is a template parameter
+// has at most 128 rows (FP8, native MXFP4: 64).  The subtile count is a template parameter
 // chosen per tile, so the inner loop has no branches.
 //
 // K runs in steps of 128 (one weight fragment).  The pre-shuffled blob gives
@@ -80,7 +81,7 @@ constexpr int ROWB = BK * 2;                 // LDS bytes per activation row per
 // tiles of more than 6 subtiles as two halves, its accumulators being twice
 // as wide)
 template <int FMT>
-constexpr int kSubMax = FMT == MOE_FMT_FP8_E4M3 ? 4 : 8;
+constexpr int kSubMax = FMT == MOE_FMT_FP8_E4M3 || FMT == kMxNat ? 4 : 8;
 template <int FMT>
 constexpr int kTileRows = kFragRows * kSubMax<FMT>;
 
@@ -765,23 +766,24 @@ void launch_grouped_k(const FfnArgs& a, int max_tiles, const int32_t* tile_e, co
                        a_q, a_plane, a_s, hq, a.hs, n_pairs * a.F);                                           \
   }
   // gate/up widths are multiples of 256 (8-wave tiles); down takes 4 waves for hidden 256.
-  // Native MXFP4 runs 4-wave workgroups, one per compute unit: its scaled MFMAs
-  // need more registers than two waves per SIMD leave.
-  if constexpr (kNat<FMT>) GK(4) else if constexpr (NMAT == 2) GK(8) else if (N % kBN<NMAT, 8> == 0) GK(8) else GK(4)
+  // Native MXFP4 runs 8-wave workgroups on 64-row tiles: with 128-row tiles its
+  // scaled-MFMA operands and accumulators spill at two waves per SIMD.
+  if constexpr (NMAT == 2) GK(8) else if (N % kBN<NMAT, 8> == 0) GK(8) else GK(4)
 #undef GK
 }
 
 template <int FMT>
 hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
   const int n_pairs = a.T * a.k;
-  const int max_tiles = max_tiles_for<FMT>(n_pairs, a.E);
+  const bool nat = FMT == MOE_FMT_MXFP4 && a.mx_native;
+  const int max_tiles = nat ? max_tiles_for<kMxNat>(n_pairs, a.E) : max_tiles_for<FMT>(n_pairs, a.E);
   int32_t *tile_e = tiles, *tile_m0 = tiles + max_tiles, *n_tiles = tiles + 2 * max_tiles;
   if (a.F % kBN<2, 8> || a.H % kBN<1, 4> || a.H % BK || a.F % BK) return hipErrorInvalidValue;
   if (!a.tiles_ready)  // else the permutation kernel wrote the list (grouped_tile_rows / grouped_max_tiles)
-    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E, kTileRows<FMT>, tile_e,
-                       tile_m0, n_tiles);
+    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E,
+                       nat ? kTileRows<kMxNat> : kTileRows<FMT>, tile_e, tile_m0, n_tiles);
   float* y = a.y ? a.y : a.ybuf;
-  if (FMT == MOE_FMT_MXFP4 && a.mx_native) {
+  if (nat) {
     // x rows into their FP8 terms once, then both grouped kernels on the scaled MFMA
     const size_t n8 = (size_t)a.T * a.H / 8;
     hipLaunchKernelGGL(k_split_rows, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a.x, n8,
@@ -805,11 +807,13 @@ size_t grouped_tiles_bytes(int T, int k, int E) {
   return align256((size_t)(2 * max_tiles + 1) * 4);
 }
 
-int grouped_tile_rows(int fmt) {
+int grouped_tile_rows(int fmt, int mx_native) {
+  if (fmt == MOE_FMT_MXFP4 && mx_native) return kTileRows<kMxNat>;
   return fmt == MOE_FMT_FP8_E4M3 ? kTileRows<MOE_FMT_FP8_E4M3> : kTileRows<MOE_FMT_NVFP4>;
 }
 
-int grouped_max_tiles(int fmt, int n_pairs, int E) {
+int grouped_max_tiles(int fmt, int mx_native, int n_pairs, int E) {
+  if (fmt == MOE_FMT_MXFP4 && mx_native) return max_tiles_for<kMxNat>(n_pairs, E);
   return fmt == MOE_FMT_FP8_E4M3 ? max_tiles_for<MOE_FMT_FP8_E4M3>(n_pairs, E)
                                  : max_tiles_for<MOE_FMT_NVFP4>(n_pairs, E);
 }

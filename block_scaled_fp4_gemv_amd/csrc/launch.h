@@ -50,8 +50,8 @@ void ffn_ws_carve(FfnArgs& a, uint8_t* ws);
 size_t grouped_tiles_bytes(int T, int k, int E);
 // Tile list geometry of the grouped path for a format: rows per tile and the
 // list capacity (for the permutation kernel to write it).
-int grouped_tile_rows(int fmt);
-int grouped_max_tiles(int fmt, int n_pairs, int E);
+int grouped_tile_rows(int fmt, int mx_native);
+int grouped_max_tiles(int fmt, int mx_native, int n_pairs, int E);
 
 // GEMV path: gate/up + SwiGLU into hbuf, then down (+ combine when out != NULL).
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t s);

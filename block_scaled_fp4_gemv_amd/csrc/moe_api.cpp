@@ -473,8 +473,8 @@ int moe_layer_forward_prefetch(int fmt, const void* pool, size_t stride, int H, 
   const bool grouped = (long long)T * k >= 2LL * E;
   if (grouped) {  // the permutation kernel also writes the grouped path's tile list
     r.tiles = a.tiles;
-    r.tile_rows = grouped_tile_rows(fmt);
-    r.max_tiles = grouped_max_tiles(fmt, T * k, E);
+    r.tile_rows = grouped_tile_rows(fmt, a.mx_native);
+    r.max_tiles = grouped_max_tiles(fmt, a.mx_native, T * k, E);
     a.tiles_ready = 1;
   }
   e = launch_route(r, s);
