@@ -336,15 +336,21 @@ __device__ __forceinline__ void tile_step(floatx4_t (&acc)[NMAT][kCG<NMAT>][NS],
       }
     // the hi terms of every subtile, then the lo terms; the operand of subtile
     // r + 1 is read from LDS while subtile r's MFMAs run, and the reads of later
-    // subtiles are not hoisted
+    // subtiles are not hoisted.  The LDS bases pass through an empty asm so that
+    // the per-subtile addresses (base + constant) are formed inside the step
+    // rather than hoisted out of the k loop into registers of their own.
+    int lz = 0;
+    asm volatile("" : "+v"(lz));
+    const uint8_t* bufl = buf + lz;
+    const uint8_t* sbufl = sbuf + lz;
     const auto read_a = [&](int r, int term, i32x8_t& av8, int& sc) {
       const int row = kFragRows * r + am, sw = row & 15;
-      const uint8_t* rp = buf + row * ROWB;
+      const uint8_t* rp = bufl + row * ROWB;
       const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(rp + (((8 * term + aq) ^ sw) << 4));
       const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(rp + (((8 * term + 4 + aq) ^ sw) << 4));
       av8 = i32x8_t{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
       // lane group aq supplies the scale of k-block aq of its row
-      sc = (int)sbuf[row * kNatScaleRow + 2 * aq + term];
+      sc = (int)sbufl[row * kNatScaleRow + 2 * aq + term];
     };
 #pragma unroll
     for (int term = 0; term < 2; ++term) {
@@ -370,6 +376,15 @@ __device__ __forceinline__ void tile_step(floatx4_t (&acc)[NMAT][kCG<NMAT>][NS],
         }
       }
     }
+    // the step's MFMAs stay in the step: without this the compiler sinks them
+    // below the next barrier, beside the next step's LDS reads, and the operands
+    // of both steps spill
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int cg = 0; cg < kCG<NMAT>; ++cg)
+#pragma unroll
+        for (int r = 0; r < NS; ++r) asm volatile("" : "+v"(acc[m][cg][r]));
   } else if constexpr (FMT != MOE_FMT_FP8_E4M3) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
