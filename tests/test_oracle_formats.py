@@ -117,3 +117,34 @@ def test_bf16_rne_single_rounding_from_f64():
 
 def test_bf16_decode():
     assert fm.bf16_to_f64(np.array([0x3F80, 0xC000, 0x0001], np.uint16)).tolist() == [1.0, -2.0, 2.0 ** -133]
+
+
+def test_f32_rne_ties_to_even_and_specials():
+    """to_f32_rne (the oracle's fp32 rounding of logits and routing weights)
+    against IEEE binary32 round-to-nearest-even, worked by hand: halfway cases
+    go to the even significand, just above halfway rounds up, and overflow,
+    signed zeros and subnormals follow IEEE."""
+    one = 1.0
+    ulp = 2.0 ** -23
+    cases = {
+        one + ulp / 2: one,                        # tie, 1.0 has an even significand
+        one + 3 * ulp / 2: one + 2 * ulp,          # tie, rounds up to the even one
+        one + ulp / 2 + 2.0 ** -50: one + ulp,     # just above the tie
+        -(one + ulp / 2): -one,
+        2.0 ** 128: np.inf,                        # beyond the largest finite value
+        (2.0 - 2.0 ** -24) * 2.0 ** 127: np.inf,   # tie at the top rounds to even = overflow
+        2.0 ** -149: 2.0 ** -149,                  # smallest subnormal
+        2.0 ** -150: 0.0,                          # tie between 0 and the smallest subnormal
+        3 * 2.0 ** -151: 2.0 ** -149,              # above that tie
+        -0.0: -0.0,
+    }
+    got = fm.to_f32_rne(np.array(list(cases), dtype=np.float64))
+    assert got.dtype == np.float32
+    for (x, want), g in zip(cases.items(), got):
+        assert g == np.float32(want), (x, g, want)
+        assert np.signbit(g) == np.signbit(want), x
+    # agrees with torch's float64 -> float32 cast on random values of every magnitude
+    rng = np.random.default_rng(0)
+    x = rng.normal(size=4096) * 10.0 ** rng.integers(-40, 39, size=4096)
+    t = torch.from_numpy(x).to(torch.float32).numpy()
+    assert np.array_equal(fm.to_f32_rne(x), t)
