@@ -87,9 +87,9 @@ enum moe_fmt { MOE_FMT_NVFP4 = 1, MOE_FMT_MXFP4 = 2, MOE_FMT_FP8_E4M3 = 3 };
  * two FP8 E4M3 terms with E8M0 scales per 32 elements (hi and the remainder
  * lo; exact for every value within 2^14 of its block's largest), instead of
  * dequantizing the weights in registers into bf16 MFMA operands.  Outputs
- * agree within the tolerance; without the flag the dequant path runs (the
- * faster of the two as the kernels stand: the scaled path needs more registers
- * and runs 4 waves per compute unit). */
+ * agree within the tolerance; without the flag the dequant path runs (as fast
+ * or faster as the kernels stand: the scaled path's operands leave room for
+ * 64-row tiles only, so an expert's weights stream once per 64 rows). */
 #define MOE_FFN_MX_NATIVE 4u
 #define MOE_LAYER_MX_NATIVE 0x100u
 
