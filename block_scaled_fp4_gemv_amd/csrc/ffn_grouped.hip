@@ -661,24 +661,30 @@ __global__ __launch_bounds__(64 * NW, NW == 4 && FMT != MOE_FMT_FP8_E4M3 && !kNa
     const uint8_t* __restrict__ pool, size_t stride, BlobLayout L, int K, int N, int k_top,
     const uint16_t* __restrict__ a_src, int a_by_token, const int32_t* __restrict__ pair_perm,
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ tile_e,
-    const int32_t* __restrict__ tile_m0, const int32_t* __restrict__ n_tiles, int n_sweeps, int npass,
-    uint16_t* __restrict__ hout, float* __restrict__ yout, const uint8_t* __restrict__ a_q, size_t a_plane,
+    const int32_t* __restrict__ tile_m0, const int32_t* __restrict__ n_tiles, int tile_rows, int n_sweeps,
+    int npass, uint16_t* __restrict__ hout, float* __restrict__ yout, const uint8_t* __restrict__ a_q, size_t a_plane,
     const uint8_t* __restrict__ a_s, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, size_t h_plane) {
   __shared__ __attribute__((aligned(16))) uint8_t As[2 * kTileRows<FMT> * ROWB +
                                                    (NMAT == 1 ? NW * kPatchFloats * 4 : NW * kHPatchHalfs * 2) +
                                                    (kNat<FMT> ? 2 * kTileRows<FMT> * kNatScaleRow : 0)];
   __shared__ int s_rows[NMAT == 1 ? kTileRows<FMT> : 1];
   // A workgroup takes one row tile and a sweep of npass consecutive column
-  // tiles.  Workgroups are handed to the 8 XCDs round-robin by index; within
-  // each run of 8 * n_sweeps indices, the sweeps of one row tile share an XCD
-  // (and its L2 copy of the gathered activation rows).
-  const int grp = blockIdx.x / (8 * n_sweeps), r8 = blockIdx.x % (8 * n_sweeps);
-  const int tile = grp * 8 + (r8 & 7);
-  if (tile >= *n_tiles) return;
+  // tiles.  Workgroups are handed to the 8 XCDs round-robin by index (the grid,
+  // max_tiles * n_sweeps, is a multiple of 8); XCD c takes the c-th eighth of
+  // the tile list, in order, every tile with all its sweeps.  The sweeps of a
+  // row tile then share that XCD's L2 copy of the gathered activation rows, and
+  // the row tiles of one expert (consecutive in the list) its copy of the
+  // expert's weights.
+  const int nt = *n_tiles, per = (nt + 7) >> 3;
+  const int j = blockIdx.x >> 3, tl = j / n_sweeps;
+  const int tile = (blockIdx.x & 7) * per + tl;
+  if (tl >= per || tile >= nt) return;
   TileArgs t;
   const int e = tile_e[tile];
   t.row_base = expert_off[e] + tile_m0[tile];
-  t.rows = min(kTileRows<FMT>, expert_off[e + 1] - t.row_base);
+  // (bounded by the format's tile rows, so that the compiler drops the subtile
+  // counts a format never reaches)
+  t.rows = min(min(tile_rows, kTileRows<FMT>), expert_off[e + 1] - t.row_base);
   t.epi = As + 2 * kTileRows<FMT> * ROWB;
   t.rows_perm = s_rows;
   if constexpr (NMAT == 1)  // read before the first epilogue, after the pipeline's first barrier
@@ -689,7 +695,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 && FMT != MOE_FMT_FP8_E4M3 && !kNa
   t.N = N;
   t.k_top = k_top;
   t.a_by_token = a_by_token;
-  t.ct = (r8 >> 3) * npass;
+  t.ct = (j % n_sweeps) * npass;
   t.npass = npass;
   t.a_src = a_src;
   t.pair_perm = pair_perm;
@@ -749,11 +755,22 @@ int sweep_len(int n_col_tiles, int S) {
   return n;
 }
 
+// Entries of a tile list of rb-row tiles: a multiple of 8 (k_grouped maps
+// tiles to XCDs by eighths).
+int max_tiles_rows(int n_pairs, int E, int rb) { return ((n_pairs + rb - 1) / rb + E + 7) / 8 * 8; }
 template <int FMT>
 int max_tiles_for(int n_pairs, int E) {
-  constexpr int RB = kTileRows<FMT>;
-  return ((n_pairs + RB - 1) / RB + E + 7) / 8 * 8;
+  return max_tiles_rows(n_pairs, E, kTileRows<FMT>);
 }
+
+// Row tiles of the FP4 down kernel when experts average more than this many
+// rows: its accumulators hold at most six 16-row subtiles without spilling, so
+// a 128-row tile runs as two passes (64 rows + the rest), each streaming the
+// expert's down weights and dequantizing them for few rows.  A list of 96-row
+// tiles (built after the gate/up kernel, over the same buffer) needs one pass
+// per tile: 16384 tokens of the 35B-class layer take 1501 instead of 2120
+// passes, the 753B-class layer at 4096 tokens 511 instead of 635.
+constexpr int kDownRows = 96;
 
 // One grouped kernel: NMAT = 2 gate/up (A = x rows by token, K = H, N = F,
 // h rows in expert order), NMAT = 1 down (A = h rows in expert order, K = F,
@@ -762,7 +779,7 @@ int max_tiles_for(int n_pairs, int E) {
 // else four.
 template <int FMT, int NMAT>
 void launch_grouped_k(const FfnArgs& a, int max_tiles, const int32_t* tile_e, const int32_t* tile_m0,
-                      const int32_t* n_tiles, float* y, hipStream_t s) {
+                      const int32_t* n_tiles, int tile_rows, float* y, hipStream_t s) {
   const int K = NMAT == 2 ? a.H : a.F, N = NMAT == 2 ? a.F : a.H;
   const uint16_t* a_src = NMAT == 2 ? a.x : a.hbuf;
   // native MXFP4: x's FP8 terms (gate/up) or h's (down; they replace the bf16 h rows in hbuf)
@@ -777,7 +794,8 @@ void launch_grouped_k(const FfnArgs& a, int max_tiles, const int32_t* tile_e, co
     const int np = NMAT == 2 ? 1 : sweep_len(nct, K / BK); /* gate/up keeps its epilogue out of the loop */   \
     hipLaunchKernelGGL((k_grouped<FMT, NMAT, NW>), dim3(max_tiles * (nct / np)), dim3(64 * NW), 0, s, a.pool, \
                        a.stride, a.L, K, N, a.k, a_src, NMAT == 2 ? 1 : 0, a.pair_perm, a.expert_off, tile_e,  \
-                       tile_m0, n_tiles, nct / np, np, NMAT == 2 ? a.hbuf : nullptr, NMAT == 2 ? nullptr : y,  \
+                       tile_m0, n_tiles, tile_rows, nct / np, np, NMAT == 2 ? a.hbuf : nullptr,                \
+                       NMAT == 2 ? nullptr : y,                                                               \
                        a_q, a_plane, a_s, hq, a.hs, n_pairs * a.F);                                           \
   }
   // gate/up widths are multiples of 256 (8-wave tiles); down takes 4 waves for hidden 256.
@@ -803,11 +821,21 @@ hipError_t grouped_fmt(const FfnArgs& a, int32_t* tiles, hipStream_t s) {
     const size_t n8 = (size_t)a.T * a.H / 8;
     hipLaunchKernelGGL(k_split_rows, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a.x, n8,
                        (size_t)a.T * a.H, a.xq, a.xs);
-    launch_grouped_k<kMxNat, 2>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
-    launch_grouped_k<kMxNat, 1>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
+    launch_grouped_k<kMxNat, 2>(a, max_tiles, tile_e, tile_m0, n_tiles, kTileRows<kMxNat>, y, s);
+    launch_grouped_k<kMxNat, 1>(a, max_tiles, tile_e, tile_m0, n_tiles, kTileRows<kMxNat>, y, s);
   } else {
-    launch_grouped_k<FMT, 2>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
-    launch_grouped_k<FMT, 1>(a, max_tiles, tile_e, tile_m0, n_tiles, y, s);
+    launch_grouped_k<FMT, 2>(a, max_tiles, tile_e, tile_m0, n_tiles, kTileRows<FMT>, y, s);
+    if (kTileRows<FMT> > kDownRows && n_pairs > kDownRows * a.E) {
+      // the down kernel's own list of 96-row tiles, written over the gate/up
+      // kernel's list once that kernel is done (same stream); the buffer holds
+      // the longest list (64-row tiles)
+      const int mt = max_tiles_rows(n_pairs, a.E, kDownRows);
+      hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, a.expert_off, a.E, kDownRows, tiles,
+                         tiles + mt, tiles + 2 * mt);
+      launch_grouped_k<FMT, 1>(a, mt, tiles, tiles + mt, tiles + 2 * mt, kDownRows, y, s);
+    } else {
+      launch_grouped_k<FMT, 1>(a, max_tiles, tile_e, tile_m0, n_tiles, kTileRows<FMT>, y, s);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.out) return e;

@@ -117,10 +117,26 @@ __global__ __launch_bounds__(RTHREADS) void k_router_gemm(const uint16_t* __rest
     const int n = kCountCopies * E, per = (n + nb - 1) / nb;
     for (int j = b * per + (int)threadIdx.x; j < min(n, (b + 1) * per); j += RTHREADS) counts[j] = 0;
   }
+  // Workgroups go to the 8 XCDs round-robin by linear index.  Tile (bx, by, bz)
+  // is taken from the XCD-contiguous order instead: XCD c runs the c-th eighth
+  // of the tiles in x-fastest order, so the column tiles of one (row tile, K
+  // slice) run one after another on one XCD and fetch their x rows into its L2
+  // once (in grid order they sat on different XCDs and each read x from HBM).
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  {
+    const int n = gridDim.x * gridDim.y * gridDim.z;
+    if (n % 8 == 0) {
+      const int b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+      const int l = (b & 7) * (n >> 3) + (b >> 3);
+      bx = l % gridDim.x;
+      by = (l / gridDim.x) % gridDim.y;
+      bz = l / (gridDim.x * gridDim.y);
+    }
+  }
   // split K: workgroup z sums k in [z*H/Z, (z+1)*H/Z) into partial z of logits
-  const int kz = H / gridDim.z, k0 = blockIdx.z * kz;
-  logits += (size_t)blockIdx.z * T * E;
-  const int tm = blockIdx.y * RBM, tn = blockIdx.x * RBN;
+  const int kz = H / gridDim.z, k0 = bz * kz;
+  logits += (size_t)bz * T * E;
+  const int tm = by * RBM, tn = bx * RBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
   // staging: thread -> row tid/4, 16 columns at (tid%4)*16 of each of x and the 3 planes
