@@ -907,10 +907,42 @@ def test_grouped_35b_shape(fmt, T):
 @pytest.mark.parametrize("fmt", [NV, MX, F8])
 def test_grouped_many_rows_per_expert(fmt):
     """About 128 rows per expert: several row tiles per expert (128-row FP4
-    tiles, which the down kernel runs as two halves past 96 rows; 64-row FP8
-    tiles), odd subtile counts, and down workgroups that sweep two column tiles
-    (hidden 512 = 4 column tiles, width 1024 = 8 steps)."""
+    tiles for gate/up and, past 96 rows per expert on average, 96-row tiles for
+    down; 64-row FP8 tiles), odd subtile counts, and down workgroups that sweep
+    two column tiles (hidden 512 = 4 column tiles, width 1024 = 8 steps)."""
     _grouped_case(fmt, 512, 16, 1024, 4, 512, cfg=45, sample=96)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX, F8])
+@pytest.mark.parametrize("T", [500, 1200])
+def test_grouped_skewed_experts_both_down_tile_lists(fmt, T):
+    """Router rows scaled by exp(N(0,1)), so a few experts take most pairs.
+    T = 500 (1000 pairs, fewer than 96 per expert on average): the FP4 down
+    kernel runs the gate/up kernel's 128-row tiles, experts of 129..201 rows
+    give a full 128-row tile that it runs as two passes; T = 1200 (2400 pairs):
+    it runs its own list of 96-row tiles, and the largest expert (487 rows)
+    takes five full tiles and a ragged one.  Every token is checked."""
+    H, E, F, k, cfg = 512, 16, 1024, 2, 48
+    L = Layer(fmt, H, E, F, cfg=cfg, layer=0, w_std=0.02)
+    L.router = sy.router_skewed(0, cfg, 0, E, H, 1.0)
+    x = iid_tokens(0, cfg, T, H, [L.router], k)
+    counts = np.bincount(moe.route(x, L.router, k)[0].ravel(), minlength=E)
+    if T == 500:
+        assert T * k <= 96 * E and counts.max() > 128
+    else:
+        assert T * k > 96 * E and counts.max() > 5 * 96 and counts.max() % 96
+    pool, R = L.device()
+    xd = _x_dev(x)
+    idx, w, perm, off = B.moe_route(xd, R, k)
+    y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.uint16, device="cuda")
+    B.moe_expert_ffn(fmt, pool, L.stride, H, F, E, xd, idx, pair_perm=perm, expert_off=off,
+                     topk_w=w, y=y, out=out, flags=B.MOE_FFN_GROUPED)
+    torch.cuda.synchronize()
+    ref = moe.moe_layer(fmt, x, L.router, L.experts, k)
+    _check_route(x, L.router, k, idx.cpu(), w.cpu())
+    assert_rows_close(y.cpu().numpy(), ref["y"].reshape(-1, H), what="y")
+    assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
 
 
 def test_grouped_ragged_tiles():
