@@ -808,6 +808,25 @@ def test_layer_forward(fmt, T):
     assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
 
 
+@pytest.mark.parametrize("fmt,T", [(NV, 1), (MX, 4), (NV, 160), (F8, 160)])
+def test_layer_forward_largest_expert_count_and_top_k(fmt, T):
+    """The largest routing the C ABI accepts: 1024 experts, top-16.  T = 1 and 4
+    take the router GEMV and the GEMV experts (sixteen pairs per token, the
+    top-k over 1024 logits); T = 160 (2560 pairs) the router GEMM over sixteen
+    64-expert column tiles and the grouped path, with about 2.5 rows per expert
+    (tiles of one to a few rows, many experts with one pair)."""
+    H, E, F, k = 256, 1024, 256, 16
+    L = Layer(fmt, H, E, F, cfg=50, layer=0, w_std=0.02, eager=False)
+    x = iid_tokens(0, 50, T, H, [L.router], k)
+    oidx, _, _ = moe.route(x, L.router, k)
+    pool, R = L.device(needed=oidx)
+    idx, w, out = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, _x_dev(x), R)
+    torch.cuda.synchronize()
+    _check_route(x, L.router, k, idx, w)
+    ref = moe.moe_layer(fmt, x, L.router, L.experts, k)
+    assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
+
+
 @pytest.mark.parametrize("fmt", [NV, F8])
 def test_layer_forward_prefetch_equals_layer_forward(fmt):
     """moe_layer_forward_prefetch (the decode down kernel also reads a warm
