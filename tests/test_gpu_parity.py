@@ -827,6 +827,25 @@ def test_layer_forward_largest_expert_count_and_top_k(fmt, T):
     assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
 
 
+@pytest.mark.parametrize("fmt,H,F,T", [(NV, 8192, 256, 1), (MX, 8192, 256, 96), (F8, 256, 8192, 1),
+                                        (NV, 256, 8192, 96)])
+def test_layer_forward_largest_hidden_and_width(fmt, H, F, T):
+    """The largest hidden size and expert width the C ABI accepts (8192): the
+    decode kernels stage a full 8192-wide row in LDS and run 64 k-steps (hidden),
+    or fill the fused down + combine kernel's LDS exactly (four 8192-wide h rows,
+    64 KiB); the grouped kernels run 64 k-steps, or sweep 16 column tiles of
+    down in two passes."""
+    E, k = 16, 4
+    L = Layer(fmt, H, E, F, cfg=51, layer=0, w_std=0.02)
+    x = iid_tokens(0, 51, T, H, [L.router], k)
+    pool, R = L.device()
+    idx, w, out = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, _x_dev(x), R)
+    torch.cuda.synchronize()
+    _check_route(x, L.router, k, idx, w)
+    ref = moe.moe_layer(fmt, x, L.router, L.experts, k)
+    assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
+
+
 @pytest.mark.parametrize("fmt", [NV, F8])
 def test_layer_forward_prefetch_equals_layer_forward(fmt):
     """moe_layer_forward_prefetch (the decode down kernel also reads a warm
