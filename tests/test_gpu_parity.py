@@ -846,6 +846,27 @@ def test_layer_forward_largest_hidden_and_width(fmt, H, F, T):
     assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
 
 
+@pytest.mark.parametrize("fmt,E,T", [(NV, 8, 1), (MX, 8, 64), (NV, 1, 300), (F8, 1, 5)])
+def test_layer_forward_top1_and_single_expert(fmt, E, T):
+    """The smallest routing: top-1 over 8 experts (decode: one pair per token,
+    a one-wave down + combine; 64 tokens: the grouped path), and a single
+    expert that takes every token with weight 1 (300 tokens: one expert with
+    more than 96 rows per expert on average, so the down kernel runs its 96-row
+    tile list, three full tiles and one of 12 rows; 5 tokens: the router GEMM
+    with one expert row)."""
+    H, F, k = 512, 512, 1
+    L = Layer(fmt, H, E, F, cfg=52, layer=0, w_std=0.02)
+    x = iid_tokens(0, 52, T, H, [L.router], k)
+    pool, R = L.device()
+    idx, w, out = B.moe_layer_forward(fmt, pool, L.stride, H, F, E, k, _x_dev(x), R)
+    torch.cuda.synchronize()
+    _check_route(x, L.router, k, idx, w)
+    if E == 1:
+        assert torch.all(idx == 0) and torch.all(w == 1.0)
+    ref = moe.moe_layer(fmt, x, L.router, L.experts, k)
+    assert_rows_close(bf16_dev_to_f64(out), fm.bf16_to_f64(ref["out"]), what="out")
+
+
 @pytest.mark.parametrize("fmt", [NV, F8])
 def test_layer_forward_prefetch_equals_layer_forward(fmt):
     """moe_layer_forward_prefetch (the decode down kernel also reads a warm
